@@ -1,0 +1,383 @@
+#!/usr/bin/env python3
+"""One-GPU benchmark of the block-quantized matmul path on MI355X.
+
+Main line (the JSON `value`): the Qwen3-0.6B-shaped linear set of a
+4096-token prefill in MXFP8 weights and activations.  One step = for each of
+the seven linears, dynamic per-32 MXFP8 quantization of its BF16
+activations (rq_quantize) and the block-scaled GEMM against weights
+quantized once (rq_gemm, BF16 output).  value = GEMM FLOP per step (128.85
+GFLOP) / wall time per step, in TFLOP/s, inputs resident in HBM.
+
+`roofline` covers the dominant kernel (the MXFP8 GEMM): algorithmic FLOP
+(2 M N K per launch) over its average launch time from HIP events recorded
+around every GEMM launch in the timed region.  `rows` measures the other
+steps of the path on their own workloads: single MXFP4 GEMM (128 x 1024 x
+1024), 4096^3 MXFP4 plain / ARC (K' = 4224) / BF16, quantization bandwidth,
+the recurrent prefill (8 steps, RAMP vs all-BF16) and the nibble GEMV
+(LM head, full 28-layer sweep, escalation).  `cpu_baseline` times the CPU
+oracle on a bounded sample of the main workload.
+
+    python bench.py [--steps K] [--warmup W] [--no-rows] [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"mxfp4": 10.1e15, "mxfp8": 5.0e15, "bf16": 2.5e15, "hbm": 8.0e12}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_mxfp8_qwen3_linear_set.json")
+GEMM_SRC = os.path.join(ROOT, "mixed_precision_block_amd", "csrc", "gemm.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the main GEMM from the committed counter
+    summary, or None when the kernel source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("gemm_source_sha256_16") != source_hash(GEMM_SRC):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+class Timer:
+    """HIP events on torch's current stream (where librq launches)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, s):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append((s, e))
+
+    def total_ms(self):
+        self.torch.cuda.synchronize()
+        return sum(s.elapsed_time(e) for s, e in self.pairs)
+
+
+def time_calls(torch, fn, iters, warmup=3, before=None):
+    """Mean per-call milliseconds of fn() from events around each call."""
+    for _ in range(warmup):
+        if before:
+            before()
+        fn()
+    tm = Timer(torch)
+    for _ in range(iters):
+        if before:
+            before()
+        s = tm.start()
+        fn()
+        tm.stop(s)
+    return tm.total_ms() / iters
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-rows", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (no multi-GPU path is built).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mixed_precision_block_amd import api
+    from mixed_precision_block_amd import _lib as L
+    from synthetic import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev)
+
+    # ------------------------------------------------------ main workload --
+    log("generating the Qwen3-0.6B linear set at 4096 tokens (seeded)")
+    M = 4096
+    lin = []
+    for i in range(7):
+        d = W.c2_linear(i, M=M)
+        K, N = d["a"].shape[1], d["w"].shape[0]
+        a = to_dev(d["a"])
+        wq = api.quantize(to_dev(d["w"]), L.RQ_MXFP8)  # weights: quantized once
+        lin.append(dict(name=d["name"], K=K, N=N, a=a, wc=wq[0], ws=wq[1],
+                        ac=torch.empty((M, K), dtype=torch.uint8, device=dev),
+                        as_=torch.empty((M, K // 32), dtype=torch.uint8, device=dev),
+                        y=torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
+    flops_step = sum(2.0 * M * l["K"] * l["N"] for l in lin)
+
+    def step(tm=None):
+        for l in lin:
+            L.rq_quantize(l["a"], M, l["K"], L.RQ_MXFP8, None, 0, L.RQ_APPEND_NONE, l["ac"], l["as_"])
+            s = tm.start() if tm else None
+            L.rq_gemm(L.RQ_MXFP8, l["ac"], l["as_"], l["wc"], l["ws"], M, l["N"], l["K"], L.RQ_OUT_BF16, l["y"])
+            if tm:
+                tm.stop(s)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(tm)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    gemm_ms = tm.total_ms() / (args.steps * len(lin))  # average launch
+    achieved = flops_step / len(lin) / (gemm_ms * 1e-3)
+    log(f"main: {ms_step:.3f} ms/step, GEMM avg launch {gemm_ms * 1e3:.1f} us")
+    value = flops_step / (ms_step * 1e-3) / 1e12
+    traffic = measured_traffic()
+
+    line = {
+        "metric": "MXFP4/MXFP8 GEMM TFLOPS & % MFMA peak; nibble-GEMV GB/s & % HBM peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8",
+        "data": "synthetic (seeded, shapes and distributions of the Qwen3-0.6B linear set)",
+        "config": {"workload": "qwen3-0.6b linear set (q,k,v,o,gate,up,down), 4096-token prefill, "
+                               "MXFP8 W/A, dynamic per-32 activation quantization + block-scaled GEMM",
+                   "tokens": M, "gemm_gflop_per_step": round(flops_step / 1e9, 2)},
+        "roofline": {"bound": "mfma", "kernel": "gemm_kernel<MXFP8, BF16 out>",
+                     "achieved": round(achieved / 1e12, 2), "peak": PEAK["mxfp8"] / 1e12, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK["mxfp8"], 4), "traffic": traffic,
+                     "avg_launch_us": round(gemm_ms * 1e3, 2)},
+    }
+    for l in lin:
+        del l["ac"], l["as_"], l["y"], l["a"]
+    if not args.no_rows:
+        line["rows"] = measure_rows(torch, np, api, L, W, to_dev, dev)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(np, W)
+    print(json.dumps(line), flush=True)
+
+
+def measure_rows(torch, np, api, L, W, to_dev, dev):
+    rows = {}
+
+    def tflops(flop, ms):
+        return flop / (ms * 1e-3) / 1e12
+
+    # ---- single MXFP4 GEMM, 128 x 1024 x 1024 (launch/latency bound)
+    d = W.c1_gemm_mxfp4()
+    ac, as_ = api.quantize(to_dev(d["a"]), L.RQ_MXFP4)
+    wc, ws = api.quantize(to_dev(d["w"]), L.RQ_MXFP4)
+    y = torch.empty((128, 1024), dtype=torch.bfloat16, device=dev)
+    ms = time_calls(torch, lambda: L.rq_gemm(L.RQ_MXFP4, ac, as_, wc, ws, 128, 1024, 1024, 0, y), 200)
+    f = 2.0 * 128 * 1024 * 1024
+    rows["single_mxfp4_gemm_128x1024x1024"] = {"us": round(ms * 1e3, 2), "tflops": round(tflops(f, ms), 2),
+                                               "frac_mxfp4_peak": round(tflops(f, ms) * 1e12 / PEAK["mxfp4"], 5)}
+    log(f"rows: config-1 {ms * 1e3:.1f} us")
+
+    # ---- 4096^3: plain MXFP4, ARC (K' = 4224), BF16; quantization bandwidth
+    d = W.c3_arc()
+    a = to_dev(d["a"])
+    w = to_dev(d["w"])
+    n = 4096
+    f = 2.0 * n ** 3
+    pc, ps = api.quantize(a, L.RQ_MXFP4)
+    qc, qs = api.quantize(w, L.RQ_MXFP4)
+    y = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+    ms_plain = time_calls(torch, lambda: L.rq_gemm(L.RQ_MXFP4, pc, ps, qc, qs, n, n, n, 0, y), 50)
+    ms_q = time_calls(torch, lambda: L.rq_quantize(a, n, n, L.RQ_MXFP4, None, 0, 0, pc, ps), 50)
+    idx = api.select_channels(api.channel_amax(a), 128).to(dev)
+    w_aug = api.quantize(w, L.RQ_MXFP4, idx, L.RQ_APPEND_COPY)
+    ws_bytes = L.rq_gemm_arc_workspace_bytes(n, n, 128)
+    wsp = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ms_arc = time_calls(torch, lambda: L.rq_gemm_arc(a, n, n, idx, 128, w_aug[0], w_aug[1], n, wsp, ws_bytes, 0, y),
+                        50)
+    ms_bf = time_calls(torch, lambda: L.rq_gemm(L.RQ_BF16, a, None, w, None, n, n, n, 0, y), 20)
+    qbytes = n * n * 2 + n * n // 2 + n * n // 32
+    f_arc = 2.0 * n * n * (n + 128)
+    rows["mxfp4_gemm_4096cubed"] = {"us": round(ms_plain * 1e3, 1), "tflops": round(tflops(f, ms_plain), 1),
+                                    "frac_mxfp4_peak": round(tflops(f, ms_plain) * 1e12 / PEAK["mxfp4"], 4)}
+    rows["arc_gemm_4096cubed_kprime4224"] = {
+        "us_quant_plus_gemm": round(ms_arc * 1e3, 1), "tflops_gemm_flop": round(tflops(f_arc, ms_arc), 1),
+        "overhead_vs_plain_quant_plus_gemm": round(ms_arc / (ms_plain + ms_q) - 1, 4)}
+    rows["bf16_gemm_4096cubed"] = {"us": round(ms_bf * 1e3, 1), "tflops": round(tflops(f, ms_bf), 1),
+                                   "frac_bf16_peak": round(tflops(f, ms_bf) * 1e12 / PEAK["bf16"], 4)}
+    rows["quantize_mxfp4_4096x4096"] = {"us": round(ms_q * 1e3, 2), "gb_s": round(qbytes / (ms_q * 1e-3) / 1e9, 1),
+                                        "frac_hbm": round(qbytes / (ms_q * 1e-3) / PEAK["hbm"], 4)}
+    log(f"rows: 4096^3 plain {ms_plain * 1e3:.1f} us, ARC {ms_arc * 1e3:.1f} us, BF16 {ms_bf * 1e3:.1f} us, "
+        f"quant {ms_q * 1e3:.1f} us")
+    del a, w, pc, ps, qc, qs, y, w_aug, wsp
+
+    # ---- recurrent prefill, 4096 x 2048, FFN 5632, 8 steps
+    d = W.c4_ramp()
+    h0 = to_dev(d["h0"])
+    w1, w2 = to_dev(d["w1"]), to_dev(d["w2"])
+    w1q, w2q = api.quantize(w1, L.RQ_MXFP4), api.quantize(w2, L.RQ_MXFP4)
+    S, D, F = 4096, 2048, 5632
+    wsb = L.rq_recurrent_prefill_workspace_bytes(S, D, F, L.RQ_MXFP4)
+    wsp = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    h = torch.empty_like(h0)
+    res = {}
+    outs = {}
+    for name, sched in (("all_bf16", 0x00), ("ramp_steps1_6_mxfp4", 0x3F), ("uniform_mxfp4", 0xFF)):
+        def run(sched=sched):
+            L.rq_recurrent_prefill(h, S, D, F, w1, w2, w1q[0], w1q[1], w2q[0], w2q[1], L.RQ_MXFP4, sched, 8, 1e-6,
+                                   wsp, wsb)
+        ms = time_calls(torch, run, 5, warmup=1, before=lambda: h.copy_(h0))
+        h.copy_(h0)
+        run()
+        outs[name] = h.clone()
+        res[name] = {"ms": round(ms, 3)}
+    ref = outs["all_bf16"].view(torch.bfloat16).float()
+    for name in res:
+        x = outs[name].view(torch.bfloat16).float()
+        res[name]["final_state_rel_err_vs_all_bf16"] = float((x - ref).norm() / ref.norm())
+    res["ramp_speedup_vs_all_bf16"] = round(res["all_bf16"]["ms"] / res["ramp_steps1_6_mxfp4"]["ms"], 4)
+    rows["recurrent_prefill_4096x2048_ffn5632_r8"] = res
+    log(f"rows: RAMP {res}")
+    del h0, w1, w2, w1q, w2q, wsp, h, outs, ref
+
+    # ---- nibble GEMV: weights drawn on the GPU with the same recipe
+    rows.update(measure_gemv(torch, np, api, L, W, dev))
+    return rows
+
+
+def gpu_int8_weights(torch, gen, N, K, dev):
+    w = torch.randn((N, K), generator=gen, device=dev) * 0.02
+    blk = w.view(N, K // 32, 32)
+    s = (blk.abs().amax(-1) / 127.0).to(torch.float16)
+    s = torch.where(s == 0, torch.ones_like(s), s)
+    q = torch.round(blk / s.float()[..., None]).clamp(-127, 127).to(torch.int8).view(N, K)
+    return q, s.view(torch.int16)
+
+
+def measure_gemv(torch, np, api, L, W, dev):
+    out = {}
+    B = 16
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20261208)
+    lins = W.c5_linear_list()
+    xs = {}
+    for K in (1024, 2048, 3072):
+        xs[K] = torch.randn((B, K), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
+    flags = torch.from_numpy(W.c5_flags(B)).to(dev)
+    planes = []
+    for name, K, N in lins:
+        q, s = gpu_int8_weights(torch, gen, N, K, dev)
+        planes.append((N, K, api.pack_nibble_planes(q, s)))
+        del q, s
+    ys = {N: torch.empty((B, N), dtype=torch.int16, device=dev) for _, _, N in lins}
+
+    def low_bytes(N, K):
+        return N * K // 2 + N * K // 32 * 2 + B * K * 2 + B * N * 2
+
+    def esc_bytes(N, K, nf):
+        return N * K + N * K // 32 * 2 + nf * K * 2 + nf * N * 2
+
+    # LM head alone, low pass; four rotating copies so the 256 MB MALL does not serve it
+    N, K, p = planes[-1]
+    copies = [p] + [tuple(t.clone() for t in p) for _ in range(3)]
+    it = [0]
+
+    def lm_low():
+        c = copies[it[0] % 4]
+        it[0] += 1
+        L.rq_gemv_nibble_escalate(xs[K], B, K, N, c[0], c[1], c[2], None, L.RQ_LOW, ys[N])
+
+    ms = time_calls(torch, lm_low, 40)
+    gb = low_bytes(N, K) / (ms * 1e-3) / 1e9
+    out["gemv_lm_head_low_pass_b16"] = {"us": round(ms * 1e3, 2), "gb_s": round(gb, 1),
+                                        "frac_hbm": round(gb * 1e9 / PEAK["hbm"], 4),
+                                        "bytes": low_bytes(N, K)}
+    del copies
+
+    def sweep(phase):
+        for N, K, (hi, lo, st) in planes:
+            L.rq_gemv_nibble_escalate(xs[K], B, K, N, hi, lo, st, flags, phase, ys[N])
+
+    tot_low = sum(low_bytes(N, K) for N, K, _ in planes)
+    nf = int(flags.sum().item())
+    tot_esc = sum(esc_bytes(N, K, nf) for N, K, _ in planes)
+    ms_low = time_calls(torch, lambda: sweep(L.RQ_LOW), 10)
+    ms_esc = time_calls(torch, lambda: sweep(L.RQ_ESCALATE), 10)
+    out["gemv_full_sweep_197_linears_low_pass_b16"] = {
+        "us": round(ms_low * 1e3, 1), "gb_s": round(tot_low / (ms_low * 1e-3) / 1e9, 1),
+        "frac_hbm": round(tot_low / (ms_low * 1e-3) / PEAK["hbm"], 4), "bytes": tot_low,
+        "launches": len(planes)}
+    out["gemv_full_sweep_escalation_2_of_16"] = {
+        "us": round(ms_esc * 1e3, 1), "gb_s": round(tot_esc / (ms_esc * 1e-3) / 1e9, 1),
+        "frac_hbm": round(tot_esc / (ms_esc * 1e-3) / PEAK["hbm"], 4), "bytes": tot_esc}
+    log(f"rows: GEMV {out}")
+    return out
+
+
+def cpu_baseline(np, W):
+    """The CPU oracle (float64 NumPy) on a bounded sample of the main
+    workload: 256 activation rows of each of the seven linears, weights
+    dequantized outside the timed region; repeated for about 10 s."""
+    import threadpoolctl
+    from oracle import formats as F
+    from oracle import quant as Q
+    from oracle import gemm as G
+
+    rows = 256
+    work = []
+    for i in range(7):
+        d = W.c2_linear(i, M=rows)
+        wd = Q.quantize_dequantize(d["w"], F.FMT_MXFP8)
+        work.append((d["a"], wd))
+    flop = sum(2.0 * rows * a.shape[1] * wd.shape[0] for a, wd in work)
+    info = threadpoolctl.threadpool_info()
+    cores = max([i.get("num_threads", 1) for i in info] or [1])
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for a, wd in work:
+            y = G.matmul_f64(Q.quantize_dequantize(a, F.FMT_MXFP8), wd)
+            F.f64_to_bf16(y)
+        n += 1
+        if time.perf_counter() - t0 >= 10.0:
+            break
+    dt = (time.perf_counter() - t0) / n
+    return {"value": round(flop / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{rows} of 4096 rows of each of the 7 linears (quantize + float64 GEMM + BF16 rounding), "
+                      f"{n} repetitions, {dt:.3f} s each"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,115 @@
+"""Allocate-and-call wrappers over the rq_* binding.
+
+Outputs are torch tensors on the input's device; BF16 tensors may be given
+as torch.bfloat16 or any 2-byte integer view of the bit patterns.  All
+arithmetic happens in librq's kernels.
+"""
+
+import torch
+
+from . import _lib as L
+
+
+def _u8(shape, dev):
+    return torch.empty(shape, dtype=torch.uint8, device=dev)
+
+
+def code_bytes(fmt, K):
+    return K // 2 if fmt == L.RQ_MXFP4 else K
+
+
+def quantize(x, fmt, idx=None, append=L.RQ_APPEND_NONE, stream=None):
+    """x [rows, K] BF16 -> (codes uint8 [rows, K'(/2)], scales uint8 [rows, K'/32])."""
+    rows, K = x.shape
+    S = 0 if idx is None else int(idx.numel())
+    Kp = K + S
+    codes = _u8((rows, code_bytes(fmt, Kp)), x.device)
+    scales = _u8((rows, Kp // 32), x.device)
+    L.rq_quantize(x, rows, K, fmt, idx, S, append, codes, scales, stream)
+    return codes, scales
+
+
+def channel_amax(x, stream=None):
+    rows, K = x.shape
+    out = torch.empty(K, dtype=torch.int16, device=x.device)
+    L.rq_channel_amax(x, rows, K, out, stream)
+    return out
+
+
+def select_channels(amax, S):
+    """Top-S channels (host helper); amax on any device, idx returned on CPU."""
+    a = amax.detach().to("cpu").contiguous()
+    idx = torch.empty(S, dtype=torch.int32)
+    L.rq_select_channels(a, a.numel(), S, idx)
+    return idx
+
+
+def gemm(fmt, a, a_scales, w, w_scales, K, out=L.RQ_OUT_BF16, stream=None):
+    M, N = a.shape[0], w.shape[0]
+    dt = torch.float32 if out == L.RQ_OUT_F32 else torch.bfloat16
+    y = torch.empty((M, N), dtype=dt, device=a.device)
+    L.rq_gemm(fmt, a, a_scales, w, w_scales, M, N, K, out, y, stream)
+    return y
+
+
+def gemm_arc(a, idx, w_aug, w_aug_scales, out=L.RQ_OUT_BF16, workspace=None, stream=None):
+    M, K = a.shape
+    S = int(idx.numel())
+    N = w_aug.shape[0]
+    ws_bytes = L.rq_gemm_arc_workspace_bytes(M, K, S)
+    if workspace is None:
+        workspace = _u8((ws_bytes,), a.device)
+    dt = torch.float32 if out == L.RQ_OUT_F32 else torch.bfloat16
+    y = torch.empty((M, N), dtype=dt, device=a.device)
+    L.rq_gemm_arc(a, M, K, idx, S, w_aug, w_aug_scales, N, workspace, workspace.numel(), out, y, stream)
+    return y
+
+
+def recurrent_prefill(h, w1, w2, w1q, w2q, fmt, schedule, steps, eps=1e-6, workspace=None, stream=None):
+    """In place on h [S, D] BF16.  w1q / w2q: (codes, scales) or None."""
+    S, D = h.shape
+    F = w1.shape[0] if w1 is not None else w1q[0].shape[0]
+    ws_bytes = L.rq_recurrent_prefill_workspace_bytes(S, D, F, fmt)
+    if workspace is None:
+        workspace = _u8((ws_bytes,), h.device)
+    w1c, w1s = w1q if w1q is not None else (None, None)
+    w2c, w2s = w2q if w2q is not None else (None, None)
+    L.rq_recurrent_prefill(h, S, D, F, w1, w2, w1c, w1s, w2c, w2s, fmt, schedule, steps, eps, workspace,
+                           workspace.numel(), stream)
+    return h
+
+
+def pack_nibble_planes(w, scales_f16, stream=None):
+    """w int8 [N, K], scales FP16 [N, K/32] -> tiled (hi, lo, scales)."""
+    N, K = w.shape
+    pb = L.rq_nibble_plane_bytes(N, K)
+    hi = _u8((pb,), w.device)
+    lo = _u8((pb,), w.device)
+    st = torch.empty(L.rq_nibble_scale_bytes(N, K) // 2, dtype=torch.int16, device=w.device)
+    L.rq_pack_nibble_planes(w, scales_f16, N, K, hi, lo, st, stream)
+    return hi, lo, st
+
+
+def gemv_nibble_escalate(x, N, planes, flags=None, phase=L.RQ_BOTH, y=None, stream=None):
+    B, K = x.shape
+    hi, lo, st = planes
+    if y is None:
+        y = torch.empty((B, N), dtype=torch.bfloat16, device=x.device)
+    L.rq_gemv_nibble_escalate(x, B, K, N, hi, lo, st, flags, phase, y, stream)
+    return y
+
+
+def escalation_gate(logits, tau, delta, stream=None):
+    B, V = logits.shape
+    flags = _u8((B,), logits.device)
+    stats = torch.empty((B, 2), dtype=torch.float32, device=logits.device)
+    L.rq_escalation_gate(logits, B, V, tau, delta, flags, stats, stream)
+    return flags, stats
+
+
+def kv_quantize(x, stream=None):
+    T, H, D = x.shape
+    codes = _u8((T, H, D), x.device)
+    scales = torch.empty((T, H, D // 128), dtype=torch.float32, device=x.device)
+    L.rq_kv_quantize(x, T, H, D, codes, scales, stream)
+    return codes, scales

@@ -1,0 +1,55 @@
+// Internal launch interface between the C ABI layer (rq_api.hip) and the
+// kernel translation units.  Every launcher enqueues on `stream` and
+// returns hipGetLastError() of its launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rq {
+
+// GEMM epilogues.  Y is [M x N] row-major.
+enum Epilogue {
+  kEpiStoreBf16 = 0,  // y = bf16(acc)
+  kEpiStoreF32 = 1,   // y = acc
+  kEpiSiluBf16 = 2,   // y = bf16(SiLU(bf16(acc)))
+  kEpiResAddBf16 = 3  // y = bf16(y + bf16(acc))   (in place)
+};
+
+// fmt: 1 = MXFP4, 2 = MXFP8, 3 = BF16 (scale pointers ignored)
+hipError_t launch_gemm(int fmt, int epi, const void* a, const uint8_t* a_scales, const void* w,
+                       const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y,
+                       hipStream_t stream);
+
+// Primary block quantization of rows [rows x K] into codes/scales whose
+// row strides are ldc_bytes / lds_bytes (room for appended columns).
+hipError_t launch_quant_rows(int fmt, const uint16_t* x, int64_t rows, int64_t K, uint8_t* codes,
+                             uint8_t* scales, int64_t ldc_bytes, int64_t lds_bytes,
+                             hipStream_t stream);
+// Appended columns K..K+S-1 (mode 1 residual, 2 copy); reads the primary
+// scales of the same rows for the residual.
+hipError_t launch_quant_append(int fmt, int mode, const uint16_t* x, int64_t rows, int64_t K,
+                               const int32_t* idx, int64_t S, uint8_t* codes, uint8_t* scales,
+                               int64_t ldc_bytes, int64_t lds_bytes, hipStream_t stream);
+hipError_t launch_channel_amax(const uint16_t* x, int64_t rows, int64_t K, uint16_t* amax,
+                               hipStream_t stream);
+
+// RMSNorm (eps, no gain) of rows [rows x D]: to BF16 (fmt == 3) or fused
+// with block quantization to MX codes/scales (fmt 1/2).
+hipError_t launch_rmsnorm(int fmt, const uint16_t* h, int64_t rows, int64_t D, float eps,
+                          void* out, uint8_t* out_scales, hipStream_t stream);
+
+// Nibble planes and decode GEMV.
+hipError_t launch_pack_nibble_planes(const int8_t* w, const uint16_t* scales, int64_t N, int64_t K,
+                                     uint8_t* hi, uint8_t* lo, uint16_t* scales_tiled,
+                                     hipStream_t stream);
+hipError_t launch_gemv_low(const uint16_t* x, int64_t B, int64_t K, int64_t N, const uint8_t* hi,
+                           const uint16_t* scales, uint16_t* y, hipStream_t stream);
+hipError_t launch_gemv_escalate(const uint16_t* x, int64_t B, int64_t K, int64_t N,
+                                const uint8_t* hi, const uint8_t* lo, const uint16_t* scales,
+                                const uint8_t* flags, uint16_t* y, hipStream_t stream);
+hipError_t launch_gate(const uint16_t* logits, int64_t B, int64_t V, float tau, float delta,
+                       uint8_t* flags, float* stats, hipStream_t stream);
+hipError_t launch_kv_quant(const uint16_t* x, int64_t T, int64_t H, int64_t D, uint8_t* codes,
+                           float* scales, hipStream_t stream);
+
+}  // namespace rq

@@ -1,0 +1,143 @@
+"""The C ABI without a GPU: librq.so loads, exports every function that
+include/rq.h declares, and rejects bad arguments with the documented status
+before touching the device (no compute call runs here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixed_precision_block_amd as rq
+from mixed_precision_block_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 15
+    handle = ctypes.CDLL(L.LIB_PATH)
+    missing = [n for n in names if not hasattr(handle, n)]
+    assert not missing, missing
+    # the binding declares exactly these
+    assert set(names) == set(L._SIGNATURES), set(names) ^ set(L._SIGNATURES)
+
+
+def test_version_and_status_strings():
+    assert rq.rq_abi_version() == 1
+    lib = L.lib()
+    assert lib.rq_status_str(L.RQ_ESHAPE) == b"RQ_ESHAPE"
+    assert lib.rq_status_str(99) == b"RQ_UNKNOWN"
+
+
+A16 = 1 << 20  # a fake, 16-byte aligned address: never dereferenced here
+
+
+def status_of(fn, *args):
+    try:
+        fn(*args)
+    except L.RQError as e:
+        return e.status
+    return L.RQ_OK
+
+
+def no_gpu():
+    import torch
+    return not torch.cuda.is_available()
+
+
+@pytest.mark.parametrize("args,want", [
+    ((None, 4, 64, L.RQ_MXFP4, None, 0, 0, A16, A16), L.RQ_EINVAL),           # null x
+    ((A16, 4, 64, 7, None, 0, 0, A16, A16), L.RQ_EINVAL),                     # bad fmt
+    ((A16, 4, 64, L.RQ_MXFP4, None, 0, 9, A16, A16), L.RQ_EINVAL),            # bad append
+    ((A16, 4, 64, L.RQ_MXFP4, A16, 32, 0, A16, A16), L.RQ_EINVAL),            # NONE with idx
+    ((A16, 4, 64, L.RQ_MXFP4, None, 0, 1, A16, A16), L.RQ_EINVAL),            # RESIDUAL without idx
+    ((A16, 4, 48, L.RQ_MXFP4, None, 0, 0, A16, A16), L.RQ_ESHAPE),            # K % 32
+    ((A16, 4, 64, L.RQ_MXFP4, A16, 16, 1, A16, A16), L.RQ_ESHAPE),            # S % 32
+    ((A16 + 2, 4, 64, L.RQ_MXFP4, None, 0, 0, A16, A16), L.RQ_EALIGN),        # misaligned x
+])
+def test_quantize_validation(args, want):
+    assert status_of(rq.rq_quantize, *args) == want
+
+
+@pytest.mark.parametrize("args,want", [
+    ((L.RQ_MXFP4, None, A16, A16, A16, 4, 4, 64, 0, A16), L.RQ_EINVAL),
+    ((L.RQ_BF16, A16, A16, A16, None, 4, 4, 64, 0, A16), L.RQ_EINVAL),        # BF16 with scales
+    ((L.RQ_MXFP8, A16, None, A16, A16, 4, 4, 64, 0, A16), L.RQ_EINVAL),       # MX without scales
+    ((L.RQ_MXFP4, A16, A16, A16, A16, 4, 4, 64, 5, A16), L.RQ_EINVAL),        # bad out
+    ((L.RQ_MXFP4, A16, A16, A16, A16, 4, 4, 0, 0, A16), L.RQ_ESHAPE),
+    ((L.RQ_MXFP4, A16, A16, A16, A16, -1, 4, 64, 0, A16), L.RQ_ESHAPE),
+    ((L.RQ_MXFP4, A16, A16, A16, A16, 1 << 31, 4, 64, 0, A16), L.RQ_ESHAPE),
+    ((L.RQ_MXFP4, A16 + 8, A16, A16, A16, 4, 4, 64, 0, A16), L.RQ_EALIGN),
+])
+def test_gemm_validation(args, want):
+    assert status_of(rq.rq_gemm, *args) == want
+
+
+def test_gemm_arc_validation():
+    ws = rq.rq_gemm_arc_workspace_bytes(64, 128, 32)
+    assert ws >= 64 * 160 // 2 + 64 * 5
+    base = [A16, 64, 128, A16, 32, A16, A16, 16, A16, ws, 0, A16]
+    assert status_of(rq.rq_gemm_arc, *base[:9], ws - 1, *base[10:]) == L.RQ_ESHAPE
+    assert status_of(rq.rq_gemm_arc, *base[:4], 0, *base[5:]) == L.RQ_ESHAPE
+    assert status_of(rq.rq_gemm_arc, *base[:3], None, *base[4:]) == L.RQ_EINVAL
+
+
+def test_recurrent_prefill_validation():
+    ws = rq.rq_recurrent_prefill_workspace_bytes(64, 128, 256, L.RQ_MXFP4)
+    args = [A16, 64, 128, 256, A16, A16, A16, A16, A16, A16, L.RQ_MXFP4, 0b0011, 4, 1e-6, A16, ws]
+    bad_steps = list(args)
+    bad_steps[12] = 65
+    assert status_of(rq.rq_recurrent_prefill, *bad_steps) == L.RQ_ESHAPE
+    small = list(args)
+    small[15] = ws - 1
+    assert status_of(rq.rq_recurrent_prefill, *small) == L.RQ_ESHAPE
+    noq = list(args)
+    noq[6] = None  # quantized steps scheduled but no w1_q
+    assert status_of(rq.rq_recurrent_prefill, *noq) == L.RQ_EINVAL
+    nobf = list(args)
+    nobf[4] = None  # BF16 steps scheduled but no w1
+    assert status_of(rq.rq_recurrent_prefill, *nobf) == L.RQ_EINVAL
+    allq = list(args)
+    allq[4] = allq[5] = None
+    allq[11] = 0b1111  # every step quantized: BF16 weights not needed
+    assert status_of(rq.rq_recurrent_prefill, *allq) in (L.RQ_OK, L.RQ_ENODEV)
+
+
+def test_gemv_and_gate_validation():
+    g = [A16, 16, 1024, 64, A16, A16, A16, A16, L.RQ_BOTH, A16]
+    for i, v, want in [(1, 0, L.RQ_ESHAPE), (1, 17, L.RQ_ESHAPE), (2, 1000, L.RQ_ESHAPE), (8, 4, L.RQ_EINVAL),
+                       (5, None, L.RQ_EINVAL), (7, None, L.RQ_EINVAL)]:
+        a = list(g)
+        a[i] = v
+        assert status_of(rq.rq_gemv_nibble_escalate, *a) == want, (i, v)
+    lowonly = list(g)
+    lowonly[5] = lowonly[7] = None
+    lowonly[8] = L.RQ_LOW
+    assert status_of(rq.rq_gemv_nibble_escalate, *lowonly) in (L.RQ_OK, L.RQ_ENODEV)
+    assert status_of(rq.rq_escalation_gate, A16, 0, 100, 1.0, 0.1, A16, None) == L.RQ_ESHAPE
+    assert status_of(rq.rq_kv_quantize, A16, 4, 2, 100, A16, A16) == L.RQ_ESHAPE
+    assert rq.rq_nibble_plane_bytes(100, 64) == 128 * 32
+    assert rq.rq_nibble_scale_bytes(100, 64) == 128 * 2 * 2
+
+
+def test_select_channels_host_helper():
+    import torch
+    amax = torch.tensor([0x3F80, 0x4000, 0x3F80, 0x0000, 0x4100], dtype=torch.int16)
+    idx = torch.empty(3, dtype=torch.int32)
+    rq.rq_select_channels(amax, 5, 3, idx)
+    assert idx.tolist() == [4, 1, 0]  # 8.0, 2.0, then the first of two 1.0s
+
+
+@pytest.mark.skipif(not no_gpu(), reason="a GPU is visible")
+def test_valid_call_without_device_reports_enodev():
+    assert status_of(rq.rq_gemm, L.RQ_MXFP4, A16, A16, A16, A16, 4, 4, 64, 0, A16) == L.RQ_ENODEV
+    assert b"no HIP device" in L.lib().rq_last_error()

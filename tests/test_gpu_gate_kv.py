@@ -1,0 +1,44 @@
+"""GPU parity of the escalation gate and the FP8 KV tile quantizer."""
+
+import numpy as np
+import pytest
+
+from mixed_precision_block_amd import api
+from oracle import formats as F
+from oracle import gate as GT
+from oracle import kvquant as KV
+from synthetic import workloads as W
+from tests.gpu_util import dev_bf16, host, log
+
+pytestmark = pytest.mark.gpu
+
+
+def logits_batch(V=151936):
+    rng = np.random.default_rng(9)
+    z = rng.standard_normal((8, V)) * np.array([0.5, 1, 2, 3, 4, 6, 8, 12])[:, None]
+    z[5, 17] += 40.0  # one confident token
+    z[6, 3] = z[6, 9] = z[6].max() + 5.0  # an exact top-2 tie
+    return F.f64_to_bf16(z)
+
+
+def test_gate_stats_and_flags():
+    z = logits_batch()
+    h_o, gap_o = GT.softmax_stats(z)
+    for tau, delta in ((5.0, 0.05), (11.0, 0.5), (0.0, 0.0)):
+        flags, stats = api.escalation_gate(dev_bf16(z), tau, delta)
+        st = host(stats)
+        assert np.allclose(st[:, 0], h_o, rtol=1e-4, atol=1e-4), (st[:, 0], h_o)
+        assert np.allclose(st[:, 1], gap_o, rtol=1e-4, atol=1e-6), (st[:, 1], gap_o)
+        want = GT.escalation_flags(z, tau, delta)
+        clear = (np.abs(h_o - tau) > 1e-3) & (np.abs(gap_o - delta) > 1e-4)
+        assert np.array_equal(host(flags)[clear], want[clear])
+        log(f"gate tau={tau} delta={delta}: flags {host(flags).tolist()}")
+
+
+@pytest.mark.parametrize("T,H,D", [(256, 8, 128), (37, 3, 256), (1, 1, 128)])
+def test_kv_quant_bit_exact(T, H, D):
+    x = W.kv_tiles(T=T, H=H, D=D)["x"]
+    codes, scales = api.kv_quantize(dev_bf16(x))
+    oc, os_ = KV.quantize_kv(x)
+    assert np.array_equal(host(scales), os_)
+    assert np.array_equal(host(codes), oc)

@@ -1,0 +1,166 @@
+"""GPU parity of rq_gemm: a single-tile probe that pins the scaled-MFMA
+operand/scale/output layouts, multi-tile and ragged shapes, the workload
+shapes at full size (sampled rows where the float64 oracle would be slow),
+BF16 output = RNE(FP32 output), determinism."""
+
+import numpy as np
+import pytest
+import torch
+
+from mixed_precision_block_amd import api
+from mixed_precision_block_amd import _lib as L
+from oracle import formats as F
+from oracle import quant as Q
+from oracle import gemm as G
+from synthetic import workloads as W
+from tests.gpu_util import check_bf16, check_f32, dev, dev_bf16, host, host_bits, log, rel_fro
+
+pytestmark = pytest.mark.gpu
+
+MX = [(L.RQ_MXFP4, F.FMT_MXFP4), (L.RQ_MXFP8, F.FMT_MXFP8)]
+
+
+def random_codes(rng, rows, K, ofmt):
+    if ofmt == F.FMT_MXFP4:
+        return rng.integers(0, 16, (rows, K)).astype(np.uint8)
+    c = rng.integers(0, 256, (rows, K)).astype(np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x7E
+    return c
+
+
+def run_mx(fmt, ofmt, ac, as_, wc, ws, out=L.RQ_OUT_F32):
+    K = ac.shape[1]
+    a = dev(Q.storage_codes(ac, ofmt))
+    w = dev(Q.storage_codes(wc, ofmt))
+    y = api.gemm(fmt, a, dev(as_), w, dev(ws), K, out)
+    return host(y.float()) if out == L.RQ_OUT_F32 else host_bits(y)
+
+
+@pytest.mark.parametrize("fmt,ofmt", MX)
+def test_single_tile_probe(fmt, ofmt):
+    """One 32 x 32 output, K = 64: distinct codes and per-(row, block) scales."""
+    rng = np.random.default_rng(1)
+    ac, wc = random_codes(rng, 32, 64, ofmt), random_codes(rng, 32, 64, ofmt)
+    as_ = rng.integers(118, 136, (32, 2)).astype(np.uint8)
+    ws = rng.integers(118, 136, (32, 2)).astype(np.uint8)
+    log(f"single-tile probe fmt={ofmt}")
+    y = run_mx(fmt, ofmt, ac, as_, wc, ws)
+    ref = G.gemm_mx(ac, as_, wc, ws, ofmt)
+    bound = G.abs_bound(Q.dequantize_mx(ac, as_, ofmt), Q.dequantize_mx(wc, ws, ofmt))
+    check_f32(y, ref, bound, "single tile")
+    # scale association alone: every code 1.0, so y = 32 * sum_b 2^(sa+sw-254)
+    one = np.full((32, 64), 0x2 if ofmt == F.FMT_MXFP4 else 0x38, np.uint8)
+    y1 = run_mx(fmt, ofmt, one, as_, one, ws)
+    want = 32.0 * (np.ldexp(1.0, as_[:, None, 0].astype(int) + ws[None, :, 0].astype(int) - 254)
+                   + np.ldexp(1.0, as_[:, None, 1].astype(int) + ws[None, :, 1].astype(int) - 254))
+    assert np.array_equal(y1, want), f"scale/layout mismatch, first bad {np.argwhere(y1 != want)[:4]}"
+
+
+@pytest.mark.parametrize("fmt,ofmt", MX)
+@pytest.mark.parametrize("M,N,K", [(200, 130, 96), (257, 300, 4224), (1, 1, 32), (128, 128, 128)])
+def test_multi_tile_ragged(fmt, ofmt, M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    a = F.f64_to_bf16(rng.standard_t(3, (M, K)))
+    w = F.f64_to_bf16(rng.normal(0, 0.02, (N, K)))
+    ac, as_ = Q.quantize_mx(a, ofmt)
+    wc, ws = Q.quantize_mx(w, ofmt)
+    log(f"gemm fmt={ofmt} M={M} N={N} K={K}")
+    y = run_mx(fmt, ofmt, ac, as_, wc, ws)
+    ref = G.gemm_mx(ac, as_, wc, ws, ofmt)
+    bound = G.abs_bound(Q.dequantize_mx(ac, as_, ofmt), Q.dequantize_mx(wc, ws, ofmt))
+    check_f32(y, ref, bound, "F32 output")
+    yb = run_mx(fmt, ofmt, ac, as_, wc, ws, L.RQ_OUT_BF16)
+    assert np.array_equal(yb, F.f32_to_bf16(y.astype(np.float32))), "BF16 output != RNE(F32 output)"
+    check_bf16(yb, ref, bound, "BF16 output")
+
+
+@pytest.mark.parametrize("M,N,K", [(200, 130, 96), (129, 257, 512), (64, 64, 32)])
+def test_bf16_gemm(M, N, K):
+    rng = np.random.default_rng(M * N)
+    a = F.f64_to_bf16(rng.standard_normal((M, K)))
+    w = F.f64_to_bf16(rng.standard_normal((N, K)))
+    log(f"bf16 gemm M={M} N={N} K={K}")
+    y = host(api.gemm(L.RQ_BF16, dev_bf16(a), None, dev_bf16(w), None, K, L.RQ_OUT_F32))
+    ref = G.gemm_bf16(a, w)
+    bound = G.abs_bound(F.bf16_to_f64(a), F.bf16_to_f64(w))
+    check_f32(y, ref, bound, "BF16 GEMM")
+    yb = host_bits(api.gemm(L.RQ_BF16, dev_bf16(a), None, dev_bf16(w), None, K, L.RQ_OUT_BF16))
+    assert np.array_equal(yb, F.f32_to_bf16(y.astype(np.float32)))
+
+
+def quantize_on_gpu(bits, fmt):
+    return api.quantize(dev_bf16(bits), fmt)
+
+
+def test_config1_full():
+    d = W.c1_gemm_mxfp4()
+    ac, as_ = quantize_on_gpu(d["a"], L.RQ_MXFP4)
+    wc, ws = quantize_on_gpu(d["w"], L.RQ_MXFP4)
+    y = host(api.gemm(L.RQ_MXFP4, ac, as_, wc, ws, 1024, L.RQ_OUT_F32))
+    oa, osa = Q.quantize_mx(d["a"], F.FMT_MXFP4)
+    ow, osw = Q.quantize_mx(d["w"], F.FMT_MXFP4)
+    ref = G.gemm_mx(oa, osa, ow, osw, F.FMT_MXFP4)
+    bound = G.abs_bound(Q.dequantize_mx(oa, osa, F.FMT_MXFP4), Q.dequantize_mx(ow, osw, F.FMT_MXFP4))
+    log(f"config-1 rel fro {check_f32(y, ref, bound, 'config 1'):.2e}")
+
+
+def sampled_rows_check(fmt, ofmt, a_bits, w_bits, rows, what):
+    """GPU quantize + GEMM at full size; oracle on the sampled rows only."""
+    M, K = a_bits.shape
+    ac, as_ = quantize_on_gpu(a_bits, fmt)
+    wc, ws = quantize_on_gpu(w_bits, fmt)
+    y = api.gemm(fmt, ac, as_, wc, ws, K, L.RQ_OUT_F32)
+    yb = api.gemm(fmt, ac, as_, wc, ws, K, L.RQ_OUT_BF16)
+    y = host(y)[rows]
+    yb = host_bits(yb)[rows]
+    oa, osa = Q.quantize_mx(a_bits[rows], ofmt)
+    ow, osw = Q.quantize_mx(w_bits, ofmt)
+    da, dw = Q.dequantize_mx(oa, osa, ofmt), Q.dequantize_mx(ow, osw, ofmt)
+    ref = G.matmul_f64(da, dw)
+    rf = check_f32(y, ref, G.abs_bound(da, dw), what)
+    check_bf16(yb, ref, G.abs_bound(da, dw), what)
+    log(f"{what}: rel fro {rf:.2e}")
+
+
+def test_config2_linear_set_full_size_sampled():
+    rng = np.random.default_rng(2)
+    for i in range(7):
+        d = W.c2_linear(i)
+        rows = np.sort(rng.choice(4096, 48, replace=False))
+        sampled_rows_check(L.RQ_MXFP8, F.FMT_MXFP8, d["a"], d["w"], rows, f"config-2 {d['name']}")
+
+
+def test_config3_plain_full_size_sampled():
+    d = W.c3_arc()
+    rows = np.sort(np.random.default_rng(3).choice(4096, 32, replace=False))
+    sampled_rows_check(L.RQ_MXFP4, F.FMT_MXFP4, d["a"], d["w"], rows, "config-3 plain MXFP4 4096^3")
+
+
+def test_config3_bf16_reference_sampled():
+    d = W.c3_arc()
+    rows = np.sort(np.random.default_rng(4).choice(4096, 32, replace=False))
+    y = host(api.gemm(L.RQ_BF16, dev_bf16(d["a"]), None, dev_bf16(d["w"]), None, 4096, L.RQ_OUT_F32))[rows]
+    a, w = F.bf16_to_f64(d["a"][rows]), F.bf16_to_f64(d["w"])
+    log(f"config-3 BF16 rel fro {check_f32(y, G.matmul_f64(a, w), G.abs_bound(a, w), 'config-3 BF16'):.2e}")
+
+
+@pytest.mark.parametrize("fmt", [L.RQ_MXFP4, L.RQ_MXFP8, L.RQ_BF16])
+def test_deterministic(fmt):
+    d = W.c2_linear(4, M=1024)
+    if fmt == L.RQ_BF16:
+        a, sa, w, sw = dev_bf16(d["a"]), None, dev_bf16(d["w"]), None
+    else:
+        a, sa = quantize_on_gpu(d["a"], fmt)
+        w, sw = quantize_on_gpu(d["w"], fmt)
+    y1 = host(api.gemm(fmt, a, sa, w, sw, 1024, L.RQ_OUT_F32))
+    y2 = host(api.gemm(fmt, a, sa, w, sw, 1024, L.RQ_OUT_F32))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+def test_zero_operand_gives_zero():
+    a = torch.zeros((70, 64), dtype=torch.uint8, device="cuda")
+    s = torch.full((70, 4), 127, dtype=torch.uint8, device="cuda")
+    w = torch.randint(0, 255, (50, 64), dtype=torch.uint8, device="cuda")
+    ws = torch.full((50, 4), 127, dtype=torch.uint8, device="cuda")
+    y = api.gemm(L.RQ_MXFP4, a, s, w, ws, 128, L.RQ_OUT_F32)
+    assert torch.count_nonzero(y).item() == 0

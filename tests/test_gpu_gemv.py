@@ -1,0 +1,137 @@
+"""GPU parity of the nibble planes and rq_gemv_nibble_escalate."""
+
+import numpy as np
+import pytest
+import torch
+
+from mixed_precision_block_amd import api
+from mixed_precision_block_amd import _lib as L
+from oracle import formats as F
+from oracle import gemv as V
+from synthetic import workloads as W
+from tests import _golden as gold
+from tests.gpu_util import check_bf16, dev, dev_bf16, host, host_bits, log
+
+pytestmark = pytest.mark.gpu
+
+
+def tiled_planes(w, scales):
+    """The row-tiled plane layout documented for rq_pack_nibble_planes,
+    built on the host from the oracle's nibbles."""
+    hi, lo = V.split_nibbles(w)
+    h4 = hi.astype(np.uint8) & 0xF
+    N, K = w.shape
+    Np, nb = (N + 63) // 64 * 64, K // 32
+
+    def plane(nib):
+        p = np.zeros((Np, K), np.uint8)
+        p[:N] = nib
+        blk = p.reshape(Np, nb, 4, 8)  # [row, block, dword q, element 8q + e]
+        out = np.zeros((Np, nb, 4), np.uint32)
+        for j in range(4):
+            out |= blk[..., 2 * j].astype(np.uint32) << (4 * j)
+            out |= blk[..., 2 * j + 1].astype(np.uint32) << (16 + 4 * j)
+        # chunk order: (row tile, block, row within tile)
+        return out.reshape(Np // 64, 64, nb, 4).transpose(0, 2, 1, 3).reshape(-1).view(np.uint8)
+
+    s = np.zeros((Np, nb), np.uint16)
+    s[:N] = np.asarray(scales, np.float16).view(np.uint16)
+    st = s.reshape(Np // 64, 64, nb).transpose(0, 2, 1).reshape(-1)
+    return plane(h4), plane(lo), st
+
+
+def gpu_planes(w, scales):
+    return api.pack_nibble_planes(dev(w), dev(np.asarray(scales, np.float16).view(np.int16)))
+
+
+def test_pack_layout():
+    d = W.c5_linear(0, N=200, K=96)
+    hi, lo, st = gpu_planes(d["w"], d["scales"])
+    th, tl, ts = tiled_planes(d["w"], d["scales"])
+    assert np.array_equal(host(hi), th)
+    assert np.array_equal(host(lo), tl)
+    assert np.array_equal(host(st).view(np.uint16), ts)
+
+
+def run(x, w, scales, flags, phase, N):
+    planes = gpu_planes(w, scales)
+    fl = None if flags is None else dev(np.asarray(flags, np.uint8))
+    return host_bits(api.gemv_nibble_escalate(dev_bf16(x), N, planes, fl, phase))
+
+
+def test_worked_example():
+    g = gold.keyed("gemv_worked.txt")
+    w = np.zeros((2, 32), np.int8)
+    w[0, :6] = [127, -128, -1, 16, 15, -17]
+    w[1, :] = 16
+    s = np.array([[0.5], [0.25]], np.float16)
+    x = np.zeros((2, 32))
+    x[0, :6] = 1.0
+    x[1, 0], x[1, 5] = 2.0, -1.0
+    xb = F.f64_to_bf16(x)
+    assert F.bf16_to_f64(run(xb, w, s, None, L.RQ_LOW, 2)).ravel().tolist() == g["y_low"]
+    assert F.bf16_to_f64(run(xb, w, s, [1, 1], L.RQ_BOTH, 2)).ravel().tolist() == g["y_full"]
+    assert F.bf16_to_f64(run(xb, w, s, [0, 1], L.RQ_BOTH, 2)).ravel().tolist() == g["y_mixed"]
+
+
+@pytest.mark.parametrize("B", [1, 2, 5, 16])
+@pytest.mark.parametrize("N,K", [(200, 96), (64, 32), (1000, 1024)])
+def test_small_against_oracle(B, N, K):
+    d = W.c5_linear(3, B=B, N=N, K=K)
+    flags = np.zeros(B, np.uint8)
+    flags[::3] = 1
+    log(f"gemv B={B} N={N} K={K}")
+    y_low = run(d["x"], d["w"], d["scales"], None, L.RQ_LOW, N)
+    hi, _ = V.split_nibbles(d["w"])
+    check_bf16(y_low, V.low_pass(d["x"], d["w"], d["scales"]),
+               V.abs_bound(d["x"], 16 * hi.astype(np.int64), d["scales"]), "low pass")
+    y = run(d["x"], d["w"], d["scales"], flags, L.RQ_BOTH, N)
+    ref = V.low_pass(d["x"], d["w"], d["scales"])
+    ref[flags == 1] = V.full_pass(d["x"][flags == 1], d["w"], d["scales"])
+    bound = V.abs_bound(d["x"], d["w"], d["scales"]) + V.abs_bound(d["x"], 16 * hi.astype(np.int64), d["scales"])
+    check_bf16(y, ref, bound, "low + escalation")
+    assert np.array_equal(y[flags == 0], y_low[flags == 0])
+
+
+def test_escalate_without_flags_leaves_output():
+    d = W.c5_linear(1, B=4, N=128, K=64)
+    planes = gpu_planes(d["w"], d["scales"])
+    y = torch.full((4, 128), 12345, dtype=torch.int16, device="cuda")
+    api.gemv_nibble_escalate(dev_bf16(d["x"]), 128, planes, dev(np.zeros(4, np.uint8)), L.RQ_ESCALATE, y=y)
+    assert torch.all(y == 12345).item()
+
+
+def test_lm_head_full_size_sampled():
+    i = len(W.c5_linear_list()) - 1
+    d = W.c5_linear(i)
+    N, K = 151936, 1024
+    y = run(d["x"], d["w"], d["scales"], d["flags"], L.RQ_BOTH, N)
+    cols = np.sort(np.random.default_rng(8).choice(N, 2048, replace=False))
+    w_s, s_s = d["w"][cols], d["scales"][cols]
+    ref = V.low_pass(d["x"], w_s, s_s)
+    fl = d["flags"] == 1
+    ref[fl] = V.full_pass(d["x"][fl], w_s, s_s)
+    hi, _ = V.split_nibbles(w_s)
+    bound = V.abs_bound(d["x"], w_s, s_s) + V.abs_bound(d["x"], 16 * hi.astype(np.int64), s_s)
+    n = check_bf16(y[:, cols], ref, bound, "LM head")
+    log(f"LM head: {n} of {ref.size} sampled outputs one BF16 step off")
+
+
+def test_one_layer_full():
+    for i in range(7):
+        d = W.c5_linear(i)
+        N, K = d["w"].shape
+        y = run(d["x"], d["w"], d["scales"], d["flags"], L.RQ_BOTH, N)
+        ref = V.low_pass(d["x"], d["w"], d["scales"])
+        fl = d["flags"] == 1
+        ref[fl] = V.full_pass(d["x"][fl], d["w"], d["scales"])
+        hi, _ = V.split_nibbles(d["w"])
+        bound = V.abs_bound(d["x"], d["w"], d["scales"]) + V.abs_bound(d["x"], 16 * hi.astype(np.int64), d["scales"])
+        check_bf16(y, ref, bound, d["name"])
+
+
+def test_deterministic():
+    d = W.c5_linear(4)
+    a = run(d["x"], d["w"], d["scales"], d["flags"], L.RQ_BOTH, d["w"].shape[0])
+    b = run(d["x"], d["w"], d["scales"], d["flags"], L.RQ_BOTH, d["w"].shape[0])
+    assert np.array_equal(a, b)
