@@ -9,11 +9,13 @@
 // tiling (the reference-precision steps of RAMP, section 4.2).
 //
 // Operand layout per MFMA (pinned by the single-tile GPU parity test):
-//   lane l supplies row (l % 32) and the 32-element K half (l / 32) of a
-//   64-deep MX slice (16 B of FP4 or 32 B of FP8) plus the scale byte of
-//   that (row, block); for BF16 lane l supplies 8 elements at K offset
-//   8 * (l / 32) of a 16-deep slice.  Accumulator element r of lane l is
-//   D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].
+//   lane l supplies row (l % 32) of a 64-deep MX slice plus the E8M0 byte
+//   of (row, block l / 32).  FP4: the lane's 16 bytes are K [32h, 32h+32)
+//   with h = l / 32.  FP8: the matrix core takes the first 16 bytes of both
+//   lane halves as block 0 and the last 16 bytes as block 1, so lane half h
+//   carries K [16h, 16h+16) then K [32+16h, 32+16h+16).  BF16: lane l
+//   supplies 8 elements at K offset 8 h of a 16-deep slice.  Accumulator
+//   element r of lane l is D[8 (r / 4) + 4 h + r % 4][l % 32].
 //
 // Tiling: a 256-thread workgroup computes a 128 x 128 tile; its four waves
 // each own a 64 x 64 quadrant (2 x 2 MFMA tiles).  Each K step stages a
@@ -139,8 +141,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ A
       for (int i = 0; i < 2; ++i) {
         const int ar = wm * 64 + i * 32 + lrow;
         const int br = wn * 64 + i * 32 + lrow;
-        const uint8_t* pa = &sA[buf][ar * LDSR + kk * T::kKKBytes + half * T::kOpBytes];
-        const uint8_t* pb = &sW[buf][br * LDSR + kk * T::kKKBytes + half * T::kOpBytes];
+        // FP8 lane halves interleave at 16 bytes (see the layout note above)
+        constexpr int kHalfStride = FMT == 2 ? 16 : T::kOpBytes;
+        constexpr int kSecond = FMT == 2 ? 32 : 16;
+        const uint8_t* pa = &sA[buf][ar * LDSR + kk * T::kKKBytes + half * kHalfStride];
+        const uint8_t* pb = &sW[buf][br * LDSR + kk * T::kKKBytes + half * kHalfStride];
         if constexpr (FMT == 3) {
           a_bf[i] = *reinterpret_cast<const v8bf*>(pa);
           b_bf[i] = *reinterpret_cast<const v8bf*>(pb);
@@ -149,8 +154,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ A
           const uint4 b0 = *reinterpret_cast<const uint4*>(pb);
           uint4 a1 = make_uint4(0, 0, 0, 0), b1 = make_uint4(0, 0, 0, 0);
           if constexpr (T::kOpBytes == 32) {
-            a1 = *reinterpret_cast<const uint4*>(pa + 16);
-            b1 = *reinterpret_cast<const uint4*>(pb + 16);
+            a1 = *reinterpret_cast<const uint4*>(pa + kSecond);
+            b1 = *reinterpret_cast<const uint4*>(pb + kSecond);
           }
           a_op[i] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
           b_op[i] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};

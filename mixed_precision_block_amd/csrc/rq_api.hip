@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <utility>
 #include <vector>
 
 #include "../../include/rq.h"
@@ -33,9 +34,14 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Device presence, checked after argument validation so that bad arguments
 // are reported the same way with or without a GPU.
 rq_status need_device() {
-  int n = 0;
-  const hipError_t e = hipGetDeviceCount(&n);
-  if (e != hipSuccess || n <= 0) return fail(RQ_ENODEV, "no HIP device visible (%s)", hipGetErrorString(e));
+  // Queried once per process: the set of visible devices does not change.
+  static const std::pair<hipError_t, int> probe = [] {
+    int n = 0;
+    const hipError_t e = hipGetDeviceCount(&n);
+    return std::make_pair(e, n);
+  }();
+  if (probe.first != hipSuccess || probe.second <= 0)
+    return fail(RQ_ENODEV, "no HIP device visible (%s)", hipGetErrorString(probe.first));
   return RQ_OK;
 }
 

@@ -84,12 +84,12 @@ def test_small_against_oracle(B, N, K):
     y_low = run(d["x"], d["w"], d["scales"], None, L.RQ_LOW, N)
     hi, _ = V.split_nibbles(d["w"])
     check_bf16(y_low, V.low_pass(d["x"], d["w"], d["scales"]),
-               V.abs_bound(d["x"], 16 * hi.astype(np.int64), d["scales"]), "low pass")
+               V.abs_bound(d["x"], 16 * hi.astype(np.int64), d["scales"]), "low pass", k=K)
     y = run(d["x"], d["w"], d["scales"], flags, L.RQ_BOTH, N)
     ref = V.low_pass(d["x"], d["w"], d["scales"])
     ref[flags == 1] = V.full_pass(d["x"][flags == 1], d["w"], d["scales"])
     bound = V.abs_bound(d["x"], d["w"], d["scales"]) + V.abs_bound(d["x"], 16 * hi.astype(np.int64), d["scales"])
-    check_bf16(y, ref, bound, "low + escalation")
+    check_bf16(y, ref, bound, "low + escalation", k=K)
     assert np.array_equal(y[flags == 0], y_low[flags == 0])
 
 
@@ -113,7 +113,7 @@ def test_lm_head_full_size_sampled():
     ref[fl] = V.full_pass(d["x"][fl], w_s, s_s)
     hi, _ = V.split_nibbles(w_s)
     bound = V.abs_bound(d["x"], w_s, s_s) + V.abs_bound(d["x"], 16 * hi.astype(np.int64), s_s)
-    n = check_bf16(y[:, cols], ref, bound, "LM head")
+    n = check_bf16(y[:, cols], ref, bound, "LM head", k=K)
     log(f"LM head: {n} of {ref.size} sampled outputs one BF16 step off")
 
 
@@ -127,7 +127,7 @@ def test_one_layer_full():
         ref[fl] = V.full_pass(d["x"][fl], d["w"], d["scales"])
         hi, _ = V.split_nibbles(d["w"])
         bound = V.abs_bound(d["x"], d["w"], d["scales"]) + V.abs_bound(d["x"], 16 * hi.astype(np.int64), d["scales"])
-        check_bf16(y, ref, bound, d["name"])
+        check_bf16(y, ref, bound, d["name"], k=K)
 
 
 def test_deterministic():
