@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "librq.so")
-SOURCES = ["rq_api.hip", "quant_mx.hip", "gemm.hip", "gemv_nibble.hip", "norm_gate_kv.hip"]
+SOURCES = ["rq_api.hip", "quant_mx.hip", "gemm.hip", "gemm_pipe.hip", "gemv_nibble.hip", "norm_gate_kv.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

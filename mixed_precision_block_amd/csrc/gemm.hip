@@ -234,6 +234,15 @@ hipError_t launch_gemm(int fmt, int epi, const void* a, const uint8_t* a_scales,
                        const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y,
                        hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
+  if (gemm_pipe_supported(fmt, M, N, K))
+    return launch_gemm_pipe(fmt, epi, a, a_scales, w, w_scales, M, N, K, y, stream);
+  return launch_gemm_basic(fmt, epi, a, a_scales, w, w_scales, M, N, K, y, stream);
+}
+
+hipError_t launch_gemm_basic(int fmt, int epi, const void* a, const uint8_t* a_scales, const void* w,
+                             const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y,
+                             hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
   if (fmt == 1) return launch_fmt<1>(epi, a, a_scales, w, w_scales, M, N, K, y, stream);
   if (fmt == 2) return launch_fmt<2>(epi, a, a_scales, w, w_scales, M, N, K, y, stream);
   return launch_fmt<3>(epi, a, a_scales, w, w_scales, M, N, K, y, stream);

@@ -1,0 +1,459 @@
+// Pipelined block-scaled GEMM for gfx950: Y[M x N] = A . W^T, K-major.
+//
+// Same contraction as gemm.hip (ARCQuant unified GEMM; Day-0 page section V
+// item 3: block scales applied inside the matrix core), organized for
+// throughput on large problems:
+//
+// * Every pipeline stage holds one 64-byte chunk of each row of the A and W
+//   tiles: 128 K of MXFP4, 64 K of MXFP8 or 32 K of BF16, so each stage
+//   carries the same matrix-core work (1024 cycles per wave at 256 x 256).
+// * Global loads are buffer loads (the resource spans the tile's rows, so
+//   rows past M or N read as zeros) into a ring of P register slots, issued
+//   P stages ahead; each stage is then written to one of two LDS buffers
+//   while the other feeds the MFMAs.  The loop is unrolled over the ring so
+//   every register slot is static, and the compiler's load counters wait
+//   exactly for the slot being written out.
+// * LDS rows are 64 bytes; the 16-byte chunk c of row r sits at chunk
+//   c ^ ((r >> 1 ^ r >> 3) & 3), which keeps the 16-byte fragment reads of
+//   8 or 16 consecutive rows on distinct banks.
+// * Four waves in a 2 x 2 arrangement, each owning a (BM/2) x (BN/2)
+//   quadrant of (BM/64) x (BN/64) MFMA tiles of 32 x 32; accumulators live
+//   in AGPRs.
+// * Workgroups are ordered so that consecutive tiles land on the same XCD
+//   (the dispatcher deals workgroups round-robin over the 8 XCDs) and each
+//   XCD's tiles form a compact block of 4 M-tiles, sharing A and W panels in
+//   that XCD's L2.
+//
+// Operand layout per MFMA is the one pinned for gemm.hip: FP4 lane half h
+// holds K [32h, 32h+32) of a 64-deep slice; FP8 lane half h holds
+// K [16h, 16h+16) and [32+16h, 32+16h+16); BF16 lane half h holds 8
+// elements at 8h of a 16-deep slice.
+#include <type_traits>
+
+#include "rq_device.h"
+#include "rq_internal.h"
+
+namespace rq {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+template <int FMT>
+struct PipeTraits;
+// One scale dword per row per stage: the four blocks of an MXFP4 stage, or
+// for MXFP8 the dword at (s / 2) * 4 holding this stage's two blocks and
+// its neighbour's.
+template <>
+struct PipeTraits<1> {  // MXFP4: 128 K per stage, two 64-deep MFMA slices
+  static constexpr int kStepElems = 128, kKK = 2, kCbsz = 4;
+  static constexpr bool kScaled = true;
+};
+template <>
+struct PipeTraits<2> {  // MXFP8: 64 K per stage, one slice
+  static constexpr int kStepElems = 64, kKK = 1, kCbsz = 0;
+  static constexpr bool kScaled = true;
+};
+template <>
+struct PipeTraits<3> {  // BF16: 32 K per stage, two 16-deep slices
+  static constexpr int kStepElems = 32, kKK = 2, kCbsz = 0;
+  static constexpr bool kScaled = false;
+};
+
+constexpr int kRowBytes = 64;
+
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// Publish LDS writes and wait for every wave (no wait on global loads).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int FMT, int BM, int BN>
+struct PipeCfg {
+  using T = PipeTraits<FMT>;
+  static constexpr int TM = BM / 64, TN = BN / 64;                // MFMA tiles per wave
+  static constexpr int CA = BM / 64, CW = BN / 64;                // 16-byte chunks per thread per stage
+  static constexpr int SA = BM * kRowBytes, SW = BN * kRowBytes;  // LDS bytes of the A / W tile
+  static constexpr int SS = T::kScaled ? (BM + BN) * 4 : 0;       // scale dwords
+  static constexpr int STAGE = SA + SW + SS;
+  static constexpr int NS = T::kScaled ? (BM + BN) / 256 : 0;     // scale loads per thread
+  static constexpr int P = BM == 256 ? 2 : 4;                     // register ring depth
+};
+
+template <int FMT, int BM, int BN>
+struct StageRegs {
+  using C = PipeCfg<FMT, BM, BN>;
+  v4i a[C::CA];
+  v4i w[C::CW];
+  uint32_t s[C::NS > 0 ? C::NS : 1];
+};
+
+template <int FMT, int EPI, int BM, int BN>
+__global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __restrict__ A,
+                                                           const uint8_t* __restrict__ As,
+                                                           const uint8_t* __restrict__ W,
+                                                           const uint8_t* __restrict__ Ws, int M, int N, int K,
+                                                           void* __restrict__ Y, int tiles_m, int tiles_n) {
+  using C = PipeCfg<FMT, BM, BN>;
+  using T = PipeTraits<FMT>;
+  constexpr int TM = C::TM, TN = C::TN, P = C::P;
+  constexpr int CMAX = C::CA > C::CW ? C::CA : C::CW;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int half = lane >> 5, lrow = lane & 31;
+
+  // XCD-aware tile order
+  const int pid = blockIdx.x, nt = tiles_m * tiles_n;
+  const int v = (nt % 8 == 0) ? (pid % 8) * (nt / 8) + pid / 8 : pid;
+  constexpr int GM = 4;
+  const int group = v / (GM * tiles_n), first_m = group * GM;
+  const int gsz = min(tiles_m - first_m, GM);
+  const int tm = first_m + (v % (GM * tiles_n)) % gsz, tn = (v % (GM * tiles_n)) / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const uint32_t ld = FMT == 1 ? (uint32_t)K / 2 : (FMT == 2 ? (uint32_t)K : 2u * (uint32_t)K);  // row bytes
+  const uint32_t ksb = (uint32_t)K / 32;
+  const int nk = K / T::kStepElems;
+
+  const uint32_t a_rows = (uint32_t)min(BM, M - m0), w_rows = (uint32_t)min(BN, N - n0);
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(A + (size_t)m0 * ld), 0, (int)(a_rows * ld), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(W + (size_t)n0 * ld), 0, (int)(w_rows * ld), 0x00020000);
+  __amdgpu_buffer_rsrc_t rsa = ra, rsw = rw;
+  if constexpr (T::kScaled) {
+    rsa = __builtin_amdgcn_make_buffer_rsrc((void*)(As + (size_t)m0 * ksb), 0, (int)(a_rows * ksb), 0x00020000);
+    rsw = __builtin_amdgcn_make_buffer_rsrc((void*)(Ws + (size_t)n0 * ksb), 0, (int)(w_rows * ksb), 0x00020000);
+  }
+
+  // This thread's chunks: rows tid/4 + 64 i, logical chunk tid % 4.
+  const int crow = tid >> 2, cchk = tid & 3;
+  uint32_t g_off[CMAX], l_off[CMAX];
+#pragma unroll
+  for (int i = 0; i < CMAX; ++i) {
+    const int r = crow + 64 * i;
+    g_off[i] = (uint32_t)r * ld + 16u * (uint32_t)cchk;
+    l_off[i] = (uint32_t)r * kRowBytes + 16u * (uint32_t)(cchk ^ swz(r));
+  }
+
+  StageRegs<FMT, BM, BN> R[P];
+
+  // Loads of stages past the end use an offset beyond every buffer range:
+  // the hardware returns zeros without a memory access, so the prefetch
+  // needs no branch (a branch around it would make the compiler's load
+  // counter wait for everything at the join).
+  constexpr uint32_t kPastEnd = 0x80000000u;
+  auto load = [&](StageRegs<FMT, BM, BN>& r, int s) {
+    const uint32_t kb = s < nk ? (uint32_t)s * kRowBytes : kPastEnd;
+#pragma unroll
+    for (int i = 0; i < C::CA; ++i)
+      r.a[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, g_off[i] + kb, 0, 0));
+#pragma unroll
+    for (int i = 0; i < C::CW; ++i)
+      r.w[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rw, g_off[i] + kb, 0, 0));
+    if constexpr (T::kScaled) {
+      // Scale rows 0..BM-1 of A then 0..BN-1 of W, one dword per thread and
+      // load; the A / W choice is per load (256 x 256) or per wave
+      // (128 x 128), so the buffer resource stays scalar.
+      const uint32_t sk = s >= nk ? kPastEnd : (FMT == 1 ? (uint32_t)s * 4u : (uint32_t)(s >> 1) * 4u);
+      if constexpr (C::NS == 2) {
+        r.s[0] = __builtin_amdgcn_raw_buffer_load_b32(rsa, (uint32_t)tid * ksb + sk, 0, 0);
+        r.s[1] = __builtin_amdgcn_raw_buffer_load_b32(rsw, (uint32_t)tid * ksb + sk, 0, 0);
+      } else {
+        static_assert(C::NS == 1 && BM == 128 && BN == 128, "scale load split");
+        if (wave < 2)
+          r.s[0] = __builtin_amdgcn_raw_buffer_load_b32(rsa, (uint32_t)tid * ksb + sk, 0, 0);
+        else
+          r.s[0] = __builtin_amdgcn_raw_buffer_load_b32(rsw, (uint32_t)(tid - 128) * ksb + sk, 0, 0);
+      }
+    }
+  };
+  auto store = [&](const StageRegs<FMT, BM, BN>& r, uint8_t* st) {
+#pragma unroll
+    for (int i = 0; i < C::CA; ++i) *reinterpret_cast<v4i*>(st + l_off[i]) = r.a[i];
+#pragma unroll
+    for (int i = 0; i < C::CW; ++i) *reinterpret_cast<v4i*>(st + C::SA + l_off[i]) = r.w[i];
+    if constexpr (T::kScaled) {
+#pragma unroll
+      for (int j = 0; j < C::NS; ++j)
+        *reinterpret_cast<uint32_t*>(st + C::SA + C::SW + 4 * (tid + 256 * j)) = r.s[j];
+    }
+  };
+
+  v16f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  // All of a stage's LDS reads are issued before its first MFMA, and each
+  // row's scales come as one dword (the four bytes of the row's stage; the
+  // lane's byte is extracted per slice), so no MFMA waits on a read issued
+  // just before it.
+  auto compute = [&](int s, const uint8_t* st) {
+    constexpr int KK = T::kKK;
+    const uint8_t* sc = st + C::SA + C::SW;
+    v4i fa[KK][TM][FMT == 2 ? 2 : 1], fb[KK][TN][FMT == 2 ? 2 : 1];
+    uint32_t sa[TM], sb[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = wm * (BM / 2) + i * 32 + lrow;
+      const uint8_t* row = st + r * kRowBytes;
+      const int z = swz(r);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        if constexpr (FMT == 2) {
+          fa[kk][i][0] = *reinterpret_cast<const v4i*>(row + 16 * (half ^ z));
+          fa[kk][i][1] = *reinterpret_cast<const v4i*>(row + 16 * ((2 + half) ^ z));
+        } else {
+          fa[kk][i][0] = *reinterpret_cast<const v4i*>(row + 16 * ((kk * 2 + half) ^ z));
+        }
+      }
+      if constexpr (T::kScaled) sa[i] = *reinterpret_cast<const uint32_t*>(sc + r * 4);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int r = wn * (BN / 2) + j * 32 + lrow;
+      const uint8_t* row = st + C::SA + r * kRowBytes;
+      const int z = swz(r);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        if constexpr (FMT == 2) {
+          fb[kk][j][0] = *reinterpret_cast<const v4i*>(row + 16 * (half ^ z));
+          fb[kk][j][1] = *reinterpret_cast<const v4i*>(row + 16 * ((2 + half) ^ z));
+        } else {
+          fb[kk][j][0] = *reinterpret_cast<const v4i*>(row + 16 * ((kk * 2 + half) ^ z));
+        }
+      }
+      if constexpr (T::kScaled) sb[j] = *reinterpret_cast<const uint32_t*>(sc + 4 * BM + r * 4);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      // byte of the scale dword: MXFP4 slice kk, lane half; MXFP8 this
+      // stage's pair of blocks (low or high half of the dword), lane half
+      const uint32_t sh = FMT == 1 ? 16u * kk + 8u * half : 16u * (uint32_t)(s & 1) + 8u * half;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          if constexpr (FMT == 3) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, fb[kk][j][0]),
+                                                                 __builtin_bit_cast(v8bf, fa[kk][i][0]), acc[i][j],
+                                                                 0, 0, 0);
+          } else {
+            const v4i* qa = fa[kk][i];
+            const v4i* qb = fb[kk][j];
+            const v8i a_op = FMT == 1 ? v8i{qa[0].x, qa[0].y, qa[0].z, qa[0].w, 0, 0, 0, 0}
+                                      : v8i{qa[0].x, qa[0].y, qa[0].z, qa[0].w,
+                                            qa[FMT == 2].x, qa[FMT == 2].y, qa[FMT == 2].z, qa[FMT == 2].w};
+            const v8i b_op = FMT == 1 ? v8i{qb[0].x, qb[0].y, qb[0].z, qb[0].w, 0, 0, 0, 0}
+                                      : v8i{qb[0].x, qb[0].y, qb[0].z, qb[0].w,
+                                            qb[FMT == 2].x, qb[FMT == 2].y, qb[FMT == 2].z, qb[FMT == 2].w};
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                b_op, a_op, acc[i][j], T::kCbsz, T::kCbsz, 0, (int)__builtin_amdgcn_ubfe(sb[j], sh, 8), 0,
+                (int)__builtin_amdgcn_ubfe(sa[i], sh, 8));
+          }
+        }
+    }
+  };
+
+  uint8_t* const lds0 = smem;
+  uint8_t* const lds1 = smem + C::STAGE;
+
+  // Step s (register slot J = s % P): write stage s+1 from its slot into the
+  // other LDS buffer, refill that slot with stage s+1+P, compute stage s.
+  auto step = [&](auto Jc, int s) {
+    constexpr int J = decltype(Jc)::value;
+    constexpr int Jn = (J + 1) % P;
+    uint8_t* cur = (J % 2) ? lds1 : lds0;
+    uint8_t* nxt = (J % 2) ? lds0 : lds1;
+    store(R[Jn], nxt);  // past the last stage this writes zeros nobody reads
+    load(R[Jn], s + 1 + P);
+    // keep the refill ahead of the matrix work (the scheduler would sink it
+    // below, shortening the prefetch distance by a step)
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s, cur);
+    lds_barrier();
+  };
+
+  // prologue: fill the ring, publish stage 0
+#pragma unroll
+  for (int t = 0; t < P; ++t) {
+    load(R[t], t);
+    // issue order = slot order, so the loop's per-slot load-count waits hold
+    // on entry as well
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  store(R[0], lds0);
+  load(R[0], P);
+  __builtin_amdgcn_sched_barrier(0);
+  lds_barrier();
+
+  int s = 0;
+  for (; s + P <= nk; s += P) {
+    step(std::integral_constant<int, 0>{}, s);
+    step(std::integral_constant<int, 1>{}, s + 1);
+    if constexpr (P == 4) {
+      step(std::integral_constant<int, 2>{}, s + 2);
+      step(std::integral_constant<int, 3>{}, s + 3);
+    }
+  }
+  if (s < nk) step(std::integral_constant<int, 0>{}, s++);
+  if (s < nk) step(std::integral_constant<int, 1>{}, s++);
+  if constexpr (P == 4) {
+    if (s < nk) step(std::integral_constant<int, 2>{}, s++);
+  }
+
+  // Epilogue.  The W tile is the MFMA's first operand, so the accumulator
+  // is the transposed tile: lane l, element r holds row m = l % 32 of the A
+  // tile and column n = 8 (r / 4) + 4 half + r % 4 of the W tile, i.e. four
+  // consecutive columns of one output row per group r / 4.  Results go
+  // through a per-wave LDS strip of 32 rows (BF16: the quadrant's full
+  // width; FP32: half of it per pass), so every global store is a 16-byte
+  // chunk of a row.
+  constexpr int WN = BN / 2;                        // columns of a wave's quadrant
+  constexpr int EB = EPI == kEpiStoreF32 ? 4 : 2;   // output element bytes
+  constexpr int SC = WN * 2 / EB;                   // strip columns per pass
+  constexpr int NP = WN / SC;                       // passes per strip
+  constexpr int EPC = 16 / EB;                      // elements per 16-byte chunk
+  constexpr int RSTR = SC * EB + 16;                // strip row stride in bytes (16-byte aligned)
+  constexpr int CPR = SC * EB / 16;                 // chunks per strip row
+  constexpr int RPI = 64 / CPR;                     // strip rows per wave-wide read
+  static_assert(4 * 32 * RSTR <= 2 * C::STAGE, "epilogue strips fit in the stage buffers");
+  uint8_t* const strip = smem + wave * 32 * RSTR;
+  const int n_wave = n0 + wn * WN;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int m_strip = m0 + wm * (BM / 2) + i * 32;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+#pragma unroll
+      for (int jj = 0; jj < TN / NP; ++jj) {
+        const int j = p * (TN / NP) + jj;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          uint8_t* dst = strip + lrow * RSTR + (jj * 32 + 8 * g + 4 * half) * EB;
+          if constexpr (EPI == kEpiStoreF32) {
+            *reinterpret_cast<float4*>(dst) =
+                float4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          } else {
+            uint32_t b[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              uint32_t v = f32_to_bf16(acc[i][j][4 * g + t]);
+              if constexpr (EPI == kEpiSiluBf16) {
+                const float z = bf16_to_f32(v);
+                v = f32_to_bf16(z / (1.0f + expf(-z)));
+              }
+              b[t] = v;
+            }
+            *reinterpret_cast<uint2*>(dst) = uint2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+          }
+        }
+      }
+      // a wave's LDS accesses complete in order: the reads below see the
+      // writes above, and the next pass's writes follow these reads
+#pragma unroll
+      for (int t = 0; t < 32 / RPI; ++t) {
+        const int rho = t * RPI + lane / CPR, q = lane % CPR;
+        const uint4 v = *reinterpret_cast<const uint4*>(strip + rho * RSTR + 16 * q);
+        const int m = m_strip + rho, n = n_wave + p * SC + EPC * q;
+        if (m >= M || n >= N) continue;
+        const bool whole = N % EPC == 0 && n + EPC <= N;
+        if constexpr (EPI == kEpiStoreF32) {
+          float* yrow = reinterpret_cast<float*>(Y) + (int64_t)m * N;
+          if (whole) {
+            *reinterpret_cast<uint4*>(yrow + n) = v;
+          } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            for (int e = 0; e < 4; ++e)
+              if (n + e < N) yrow[n + e] = __builtin_bit_cast(float, w[e]);
+          }
+        } else {
+          uint16_t* yrow = reinterpret_cast<uint16_t*>(Y) + (int64_t)m * N;
+          uint32_t w[4] = {v.x, v.y, v.z, v.w};
+          if constexpr (EPI == kEpiResAddBf16) {
+            uint32_t h[4];
+            if (whole) {
+              const uint4 hv = *reinterpret_cast<const uint4*>(yrow + n);
+              h[0] = hv.x, h[1] = hv.y, h[2] = hv.z, h[3] = hv.w;
+            } else {
+              for (int e = 0; e < 4; ++e) {
+                const uint32_t lo = n + 2 * e < N ? yrow[n + 2 * e] : 0u;
+                const uint32_t hi = n + 2 * e + 1 < N ? yrow[n + 2 * e + 1] : 0u;
+                h[e] = lo | (hi << 16);
+              }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t lo = f32_to_bf16(bf16_to_f32(h[e] & 0xFFFFu) + bf16_to_f32(w[e] & 0xFFFFu));
+              const uint32_t hi = f32_to_bf16(bf16_to_f32(h[e] >> 16) + bf16_to_f32(w[e] >> 16));
+              w[e] = lo | (hi << 16);
+            }
+          }
+          if (whole) {
+            *reinterpret_cast<uint4*>(yrow + n) = uint4{w[0], w[1], w[2], w[3]};
+          } else {
+            for (int e = 0; e < 8; ++e)
+              if (n + e < N) yrow[n + e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+          }
+        }
+      }
+    }
+  }
+}
+
+// The pipelined path applies when K is a whole number of stages and one
+// tile's operand rows fit a 32-bit buffer range.  MXFP8 also needs K % 128
+// == 0: its scale dword covers two stages, so the scale rows must be whole,
+// aligned dwords.
+bool gemm_pipe_supported(int fmt, int64_t M, int64_t N, int64_t K) {
+  const int step = fmt == 1 ? 128 : (fmt == 2 ? 128 : 32);
+  if (K % step || K < step) return false;
+  const int64_t ld = fmt == 1 ? K / 2 : (fmt == 2 ? K : 2 * K);
+  return 256 * ld < (int64_t)0x7FFFFFFF && M > 0 && N > 0;
+}
+
+template <int FMT, int EPI, int BM, int BN>
+static hipError_t launch_pipe_t(const void* a, const uint8_t* as, const void* w, const uint8_t* ws, int64_t M,
+                                int64_t N, int64_t K, void* y, hipStream_t stream) {
+  const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
+  gemm_pipe_kernel<FMT, EPI, BM, BN><<<tm * tn, 256, 0, stream>>>(static_cast<const uint8_t*>(a), as,
+                                                                    static_cast<const uint8_t*>(w), ws, (int)M,
+                                                                    (int)N, (int)K, y, tm, tn);
+  return hipGetLastError();
+}
+
+template <int FMT, int EPI>
+static hipError_t launch_pipe_e(const void* a, const uint8_t* as, const void* w, const uint8_t* ws, int64_t M,
+                                int64_t N, int64_t K, void* y, hipStream_t stream) {
+  // 256 x 256 tiles when they fill the 256 CUs at least once, else 128 x 128
+  const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+  if (big >= 256) return launch_pipe_t<FMT, EPI, 256, 256>(a, as, w, ws, M, N, K, y, stream);
+  return launch_pipe_t<FMT, EPI, 128, 128>(a, as, w, ws, M, N, K, y, stream);
+}
+
+template <int FMT>
+static hipError_t launch_pipe_f(int epi, const void* a, const uint8_t* as, const void* w, const uint8_t* ws,
+                                int64_t M, int64_t N, int64_t K, void* y, hipStream_t stream) {
+  switch (epi) {
+    case kEpiStoreBf16: return launch_pipe_e<FMT, kEpiStoreBf16>(a, as, w, ws, M, N, K, y, stream);
+    case kEpiStoreF32: return launch_pipe_e<FMT, kEpiStoreF32>(a, as, w, ws, M, N, K, y, stream);
+    case kEpiSiluBf16: return launch_pipe_e<FMT, kEpiSiluBf16>(a, as, w, ws, M, N, K, y, stream);
+    default: return launch_pipe_e<FMT, kEpiResAddBf16>(a, as, w, ws, M, N, K, y, stream);
+  }
+}
+
+hipError_t launch_gemm_pipe(int fmt, int epi, const void* a, const uint8_t* a_scales, const void* w,
+                            const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y, hipStream_t stream) {
+  if (fmt == 1) return launch_pipe_f<1>(epi, a, a_scales, w, w_scales, M, N, K, y, stream);
+  if (fmt == 2) return launch_pipe_f<2>(epi, a, a_scales, w, w_scales, M, N, K, y, stream);
+  return launch_pipe_f<3>(epi, a, a_scales, w, w_scales, M, N, K, y, stream);
+}
+
+}  // namespace rq

@@ -15,10 +15,20 @@ enum Epilogue {
   kEpiResAddBf16 = 3  // y = bf16(y + bf16(acc))   (in place)
 };
 
-// fmt: 1 = MXFP4, 2 = MXFP8, 3 = BF16 (scale pointers ignored)
+// fmt: 1 = MXFP4, 2 = MXFP8, 3 = BF16 (scale pointers ignored).  Picks the
+// pipelined kernel when it applies, else the general one.
 hipError_t launch_gemm(int fmt, int epi, const void* a, const uint8_t* a_scales, const void* w,
                        const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y,
                        hipStream_t stream);
+// The general kernel (any K % 32 == 0) and the pipelined one (K a whole
+// number of 64-byte stages).
+hipError_t launch_gemm_basic(int fmt, int epi, const void* a, const uint8_t* a_scales, const void* w,
+                             const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y,
+                             hipStream_t stream);
+bool gemm_pipe_supported(int fmt, int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_pipe(int fmt, int epi, const void* a, const uint8_t* a_scales, const void* w,
+                            const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y,
+                            hipStream_t stream);
 
 // Primary block quantization of rows [rows x K] into codes/scales whose
 // row strides are ldc_bytes / lds_bytes (room for appended columns).

@@ -13,7 +13,7 @@ from oracle import formats as F
 from oracle import quant as Q
 from oracle import gemm as G
 from synthetic import workloads as W
-from tests.gpu_util import REL_FRO, REL_FRO_MXFP8, check_bf16, check_f32, dev, dev_bf16, host, host_bits, log, rel_fro
+from tests.gpu_util import ACC_REL_MXFP8, REL_FRO, REL_FRO_MXFP8, check_bf16, check_f32, dev, dev_bf16, host, host_bits, log, rel_fro
 
 pytestmark = pytest.mark.gpu
 
@@ -22,6 +22,10 @@ MX = [(L.RQ_MXFP4, F.FMT_MXFP4), (L.RQ_MXFP8, F.FMT_MXFP8)]
 
 def rel_bar(ofmt):
     return REL_FRO_MXFP8 if ofmt == F.FMT_MXFP8 else REL_FRO
+
+
+def acc_rel(ofmt):
+    return ACC_REL_MXFP8 if ofmt == F.FMT_MXFP8 else None
 
 
 def random_codes(rng, rows, K, ofmt):
@@ -77,7 +81,43 @@ def test_multi_tile_ragged(fmt, ofmt, M, N, K):
     check_f32(y, ref, bound, "F32 output", rel_bar(ofmt))
     yb = run_mx(fmt, ofmt, ac, as_, wc, ws, L.RQ_OUT_BF16)
     assert np.array_equal(yb, F.f32_to_bf16(y.astype(np.float32))), "BF16 output != RNE(F32 output)"
-    check_bf16(yb, ref, bound, "BF16 output", k=K)
+    check_bf16(yb, ref, bound, "BF16 output", k=K, acc_rel=acc_rel(ofmt))
+
+
+@pytest.mark.parametrize("fmt,ofmt", MX)
+@pytest.mark.parametrize("M,N,K", [(512, 384, 512), (4096, 4096, 256), (300, 200, 1280)])
+def test_scale_association_every_block(fmt, ofmt, M, N, K):
+    """Every code 1.0 and a distinct scale per (row, block): y[m, n] =
+    32 sum_b 2^(sa[m,b] + sw[n,b] - 254) exactly (a 10-bit exponent spread
+    keeps every partial sum exact), for the 128 and 256 tile paths."""
+    rng = np.random.default_rng(K + M)
+    nb = K // 32
+    as_ = rng.integers(125, 131, (M, nb)).astype(np.uint8)
+    ws = rng.integers(125, 131, (N, nb)).astype(np.uint8)
+    code = 0x2 if ofmt == F.FMT_MXFP4 else 0x38
+    log(f"scale association fmt={ofmt} M={M} N={N} K={K}")
+    y = run_mx(fmt, ofmt, np.full((M, K), code, np.uint8), as_, np.full((N, K), code, np.uint8), ws)
+    want = 32.0 * (np.ldexp(1.0, as_.astype(int) - 127) @ np.ldexp(1.0, ws.astype(int) - 127).T)
+    assert np.array_equal(y, want), f"scale/layout mismatch, first bad {np.argwhere(y != want)[:4]}"
+
+
+@pytest.mark.parametrize("fmt,ofmt", MX + [(L.RQ_BF16, None)])
+@pytest.mark.parametrize("M,N,K", [(4000, 4100, 384), (4096, 4096, 128), (3969, 4097, 1152)])
+def test_large_tiles_ragged_sampled(fmt, ofmt, M, N, K):
+    """Shapes with at least 256 tiles of 256 x 256 (the large-tile path),
+    ragged in M and N, K of one stage, an odd number of stages and a long
+    tail; the oracle runs on sampled rows that include the last one."""
+    rng = np.random.default_rng(M + 3 * N + K)
+    a = F.f64_to_bf16(rng.standard_t(3, (M, K)))
+    w = F.f64_to_bf16(rng.normal(0, 0.02, (N, K)))
+    rows = np.union1d(rng.choice(M, 24, replace=False), [0, M - 1])
+    log(f"large-tile gemm fmt={fmt} M={M} N={N} K={K}")
+    if fmt == L.RQ_BF16:
+        y = host(api.gemm(fmt, dev_bf16(a), None, dev_bf16(w), None, K, L.RQ_OUT_F32))[rows]
+        da, dw = F.bf16_to_f64(a[rows]), F.bf16_to_f64(w)
+        check_f32(y, G.matmul_f64(da, dw), G.abs_bound(da, dw), "large-tile BF16")
+        return
+    sampled_rows_check(fmt, ofmt, a, w, rows, f"large-tile {ofmt} {M}x{N}x{K}")
 
 
 @pytest.mark.parametrize("M,N,K", [(200, 130, 96), (129, 257, 512), (64, 64, 32)])
@@ -124,7 +164,7 @@ def sampled_rows_check(fmt, ofmt, a_bits, w_bits, rows, what):
     da, dw = Q.dequantize_mx(oa, osa, ofmt), Q.dequantize_mx(ow, osw, ofmt)
     ref = G.matmul_f64(da, dw)
     rf = check_f32(y, ref, G.abs_bound(da, dw), what, rel_bar(ofmt))
-    check_bf16(yb, ref, G.abs_bound(da, dw), what, k=K)
+    check_bf16(yb, ref, G.abs_bound(da, dw), what, k=K, acc_rel=acc_rel(ofmt))
     log(f"{what}: rel fro {rf:.2e}")
 
 
