@@ -7,6 +7,7 @@
 //    article, setup paragraph);
 //  * FP8 per-token-head-tile-128 KV quantize-on-write (Day-0 page, section
 //    III.3.3 with the section V listing's amax/448 scale).
+#include "rq_cvt.h"
 #include "rq_device.h"
 #include "rq_internal.h"
 
@@ -75,22 +76,13 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict
 #pragma unroll
       for (int i = 0; i < 8; ++i) m = max(m, v[i] & 0x7FFFu);
       m = quad_max_u(m);  // the quad is active together: chunks % 4 == 0
-      const int e = mx_block_exp<Fm>(m);
-      if constexpr (FMT == 1) {
-        uint32_t wd = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) wd |= mx_encode<Fm>(v[i], e) << (4 * i);
-        *reinterpret_cast<uint32_t*>(out + row * (D / 2) + c * 4) = wd;
-      } else {
-        uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          w0 |= mx_encode<Fm>(v[i], e) << (8 * i);
-          w1 |= mx_encode<Fm>(v[4 + i], e) << (8 * i);
-        }
-        *reinterpret_cast<uint2*>(out + row * D + c * 8) = make_uint2(w0, w1);
-      }
-      if ((c & 3) == 0) out_scales[row * (D / 32) + (c >> 2)] = (uint8_t)(e + 127);
+      const uint32_t sb = (uint32_t)(mx_block_exp<Fm>(m) + 127);
+      const uint4 pk = make_uint4(v[0] | v[1] << 16, v[2] | v[3] << 16, v[4] | v[5] << 16, v[6] | v[7] << 16);
+      if constexpr (FMT == 1)
+        *reinterpret_cast<uint32_t*>(out + row * (D / 2) + c * 4) = cvt8_e2m1(pk, e8m0_to_f32(sb));
+      else
+        *reinterpret_cast<uint2*>(out + row * D + c * 8) = cvt8_e4m3(pk, e8m0_to_f32(sb));
+      if ((c & 3) == 0) out_scales[row * (D / 32) + (c >> 2)] = (uint8_t)sb;
     }
   }
 }

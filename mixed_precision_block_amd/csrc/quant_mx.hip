@@ -8,10 +8,13 @@
 // follow the ARCQuant page ("Methodologie": residual of the primary stage
 // on the selected channels, re-quantized and concatenated along K).
 //
-// Layout of work: one thread owns 8 consecutive elements (one 16-byte BF16
-// load); the four threads of a lane quad own one 32-element block and share
-// its amax through two DPP quad permutes.  Loads and stores of a wave are
-// contiguous (1 KiB of BF16 in, 256 B / 512 B of codes out).  HBM-bound.
+// Layout of work: a wave owns 64 consecutive 8-element chunks of one row
+// (one 16-byte BF16 load per lane); the four lanes of a quad own one
+// 32-element block and share its amax through two DPP quad permutes.  The
+// element encode is the hardware scaled conversion (rq_cvt.h), four
+// instructions per lane.  Loads and stores of a wave are contiguous (1 KiB
+// of BF16 in, 256 B / 512 B of codes out).  HBM-bound.
+#include "rq_cvt.h"
 #include "rq_device.h"
 #include "rq_internal.h"
 
@@ -24,50 +27,47 @@ __device__ __forceinline__ uint32_t quad_max(uint32_t m) {
   return m;
 }
 
-// Encode 8 BF16 values (bit patterns in v[0..7]) with block exponent e and
-// store them: FP4 -> one dword (element 2j in the low nibble of byte j),
-// FP8 -> two dwords.
+// Encode 8 BF16 values (packed two per dword, element 2i in the low half of
+// dword i) with block scale byte sb and store them: FP4 -> one dword
+// (element 2j in the low nibble of byte j), FP8 -> two dwords.
 template <class Fmt>
-__device__ __forceinline__ void encode_store8(const uint32_t v[8], int e, uint8_t* dst) {
-  if constexpr (Fmt::kMantBits == 1) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w |= mx_encode<Fmt>(v[i], e) << (4 * i);
-    *reinterpret_cast<uint32_t*>(dst) = w;
-  } else {
-    uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      w0 |= mx_encode<Fmt>(v[i], e) << (8 * i);
-      w1 |= mx_encode<Fmt>(v[4 + i], e) << (8 * i);
-    }
-    *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
-  }
+__device__ __forceinline__ void encode_store8(uint4 q, uint32_t sb, uint8_t* dst) {
+  const float scale = e8m0_to_f32(sb);
+  if constexpr (Fmt::kMantBits == 1)
+    *reinterpret_cast<uint32_t*>(dst) = cvt8_e2m1(q, scale);
+  else
+    *reinterpret_cast<uint2*>(dst) = cvt8_e4m3(q, scale);
 }
 
+__device__ __forceinline__ uint32_t amax8(uint4 q) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = max(m, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+  return m;
+}
+
+// Rows are cut into segments of 64 chunks (512 elements); wave u of the
+// grid owns segment u % segs of row u / segs.
 template <class Fmt>
-__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t rows,
-                                                         int64_t K, uint8_t* __restrict__ codes,
+__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x, uint32_t rows,
+                                                         int64_t K, uint32_t segs, uint8_t* __restrict__ codes,
                                                          uint8_t* __restrict__ scales, int64_t ldc,
                                                          int64_t lds) {
   constexpr int kElemBytesNum = Fmt::kMantBits == 1 ? 1 : 2;  // bytes per 2 elements
-  const int64_t cpr = K >> 3;  // 8-element chunks per row
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const bool active = gid < rows * cpr;  // whole quads are in or out (cpr % 4 == 0)
-  const int64_t row = active ? gid / cpr : 0;
-  const int64_t c = active ? gid - row * cpr : 0;
+  const uint32_t unit = blockIdx.x * 4u + (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t row = unit / segs, seg = unit - row * segs;
+  if (row >= rows) return;
+  const uint32_t cpr = (uint32_t)(K >> 3);  // chunks per row, a multiple of 4
+  const uint32_t c = seg * 64u + (threadIdx.x & 63u);
+  const bool active = c < cpr;  // whole quads are in or out
   uint4 q = make_uint4(0, 0, 0, 0);
-  if (active) q = *reinterpret_cast<const uint4*>(x + row * K + c * 8);
-  uint32_t v[8] = {q.x & 0xFFFFu, q.x >> 16, q.y & 0xFFFFu, q.y >> 16,
-                   q.z & 0xFFFFu, q.z >> 16, q.w & 0xFFFFu, q.w >> 16};
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) m = max(m, v[i] & 0x7FFFu);
-  m = quad_max(m);
-  const int e = mx_block_exp<Fmt>(m);
+  if (active) q = *reinterpret_cast<const uint4*>(x + (int64_t)row * K + (int64_t)c * 8);
+  const uint32_t m = quad_max(amax8(q));
+  const uint32_t sb = (uint32_t)(mx_block_exp<Fmt>(m) + 127);
   if (!active) return;
-  encode_store8<Fmt>(v, e, codes + row * ldc + c * 4 * kElemBytesNum);
-  if ((c & 3) == 0) scales[row * lds + (c >> 2)] = (uint8_t)(e + 127);
+  encode_store8<Fmt>(q, sb, codes + (int64_t)row * ldc + (int64_t)c * 4 * kElemBytesNum);
+  if ((c & 3) == 0) scales[(int64_t)row * lds + (c >> 2)] = (uint8_t)sb;
 }
 
 // Appended columns: element j of row m comes from channel idx[j]; RESIDUAL
@@ -106,14 +106,12 @@ __global__ __launch_bounds__(256) void quant_append_kernel(const uint16_t* __res
     }
     v[i] = xb;
   }
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) m = max(m, v[i] & 0x7FFFu);
-  m = quad_max(m);
-  const int e = mx_block_exp<Fmt>(m);
+  const uint4 q = make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
+  const uint32_t m = quad_max(amax8(q));
+  const uint32_t sb = (uint32_t)(mx_block_exp<Fmt>(m) + 127);
   if (!active) return;
-  encode_store8<Fmt>(v, e, codes + row * ldc + (K + c * 8) / 2 * kElemBytesNum);
-  if ((c & 3) == 0) scales[row * lds + (K >> 5) + (c >> 2)] = (uint8_t)(e + 127);
+  encode_store8<Fmt>(q, sb, codes + row * ldc + (K + c * 8) / 2 * kElemBytesNum);
+  if ((c & 3) == 0) scales[row * lds + (K >> 5) + (c >> 2)] = (uint8_t)sb;
 }
 
 // Column amax: a workgroup owns 64 channels; its four waves stride over the
@@ -136,12 +134,14 @@ static inline unsigned grid_for(int64_t threads) { return (unsigned)((threads + 
 
 hipError_t launch_quant_rows(int fmt, const uint16_t* x, int64_t rows, int64_t K, uint8_t* codes,
                              uint8_t* scales, int64_t ldc, int64_t lds, hipStream_t stream) {
-  const unsigned g = grid_for(rows * (K / 8));
-  if (g == 0) return hipSuccess;
+  if (rows == 0 || K == 0) return hipSuccess;
+  const int64_t segs = (K / 8 + 63) / 64, units = rows * segs;
+  if (units > 0x7FFFFFFFll || rows > 0xFFFFFFFFll) return hipErrorInvalidValue;
+  const unsigned g = (unsigned)((units + 3) / 4);
   if (fmt == 1)
-    quant_rows_kernel<FmtE2M1><<<g, 256, 0, stream>>>(x, rows, K, codes, scales, ldc, lds);
+    quant_rows_kernel<FmtE2M1><<<g, 256, 0, stream>>>(x, (uint32_t)rows, K, (uint32_t)segs, codes, scales, ldc, lds);
   else
-    quant_rows_kernel<FmtE4M3><<<g, 256, 0, stream>>>(x, rows, K, codes, scales, ldc, lds);
+    quant_rows_kernel<FmtE4M3><<<g, 256, 0, stream>>>(x, (uint32_t)rows, K, (uint32_t)segs, codes, scales, ldc, lds);
   return hipGetLastError();
 }
 

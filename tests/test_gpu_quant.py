@@ -62,6 +62,29 @@ def test_every_value_under_several_scales(fmt, ofmt):
         assert_same(blk, fmt, ofmt, f"all values under amax {amax}")
 
 
+@pytest.mark.parametrize("fmt,ofmt,emax", [(L.RQ_MXFP4, F.FMT_MXFP4, 125), (L.RQ_MXFP8, F.FMT_MXFP8, 119)])
+def test_every_value_under_every_block_exponent(fmt, ofmt, emax):
+    """For every block exponent e that BF16 inputs can produce, every BF16
+    value (both signs) that the scale 2^e covers, in blocks whose max is
+    Qmax 2^e (so the block exponent is exactly e)."""
+    bits = finite_bf16()
+    vals = F.bf16_to_f64(bits)
+    qmax = F.FORMATS[ofmt]["qmax"]
+    blocks = []
+    for e in range(-127, emax + 1):
+        amax = qmax * 2.0 ** e
+        sel = bits[np.abs(vals) <= amax]
+        n = (sel.size + 30) // 31
+        flat = np.zeros(n * 31, np.uint16)
+        flat[:sel.size] = sel
+        blk = np.zeros((n, 32), np.uint16)
+        blk[:, :31] = flat.reshape(n, 31)
+        blk[:, 31] = F.f64_to_bf16(np.array([amax]))[0]
+        blocks.append(blk)
+    x = np.concatenate(blocks)
+    assert_same(x, fmt, ofmt, f"all values under every block exponent -127..{emax}")
+
+
 @pytest.mark.parametrize("fmt,ofmt", FMTS)
 def test_workload_tensors(fmt, ofmt):
     assert_same(W.c1_gemm_mxfp4()["a"], fmt, ofmt, "config-1 A")
