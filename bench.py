@@ -302,6 +302,9 @@ def measure_gemv(torch, np, api, L, W, dev):
         planes.append((N, K, api.pack_nibble_planes(q, s)))
         del q, s
     ys = {N: torch.empty((B, N), dtype=torch.int16, device=dev) for _, _, N in lins}
+    # one split-K workspace, large enough for every shape (launches are stream-ordered)
+    wsb = max(L.rq_gemv_workspace_bytes(B, N, K) for _, K, N in lins)
+    wsp = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
 
     def low_bytes(N, K):
         return N * K // 2 + N * K // 32 * 2 + B * K * 2 + B * N * 2
@@ -317,7 +320,7 @@ def measure_gemv(torch, np, api, L, W, dev):
     def lm_low():
         c = copies[it[0] % 4]
         it[0] += 1
-        L.rq_gemv_nibble_escalate(xs[K], B, K, N, c[0], c[1], c[2], None, L.RQ_LOW, ys[N])
+        L.rq_gemv_nibble_escalate(xs[K], B, K, N, c[0], c[1], c[2], None, L.RQ_LOW, wsp, wsb, ys[N])
 
     ms = time_calls(torch, lm_low, 40)
     gb = low_bytes(N, K) / (ms * 1e-3) / 1e9
@@ -328,7 +331,7 @@ def measure_gemv(torch, np, api, L, W, dev):
 
     def sweep(phase):
         for N, K, (hi, lo, st) in planes:
-            L.rq_gemv_nibble_escalate(xs[K], B, K, N, hi, lo, st, flags, phase, ys[N])
+            L.rq_gemv_nibble_escalate(xs[K], B, K, N, hi, lo, st, flags, phase, wsp, wsb, ys[N])
 
     tot_low = sum(low_bytes(N, K) for N, K, _ in planes)
     nf = int(flags.sum().item())

@@ -208,12 +208,19 @@ rq_status rq_pack_nibble_planes(const int8_t *w, const uint16_t *scales_f16,
  * x_bf16 [B x K] BF16 with B in [1, 16]; planes/scales from
  * rq_pack_nibble_planes; flags [B] uint8 (device; may be NULL for RQ_LOW);
  * y_bf16 [B x N] BF16.  FP32 accumulation, BF16 output.
+ * workspace: device scratch of ws_bytes >= rq_gemv_workspace_bytes(B, N,
+ * K) bytes (caller-owned, contents irrelevant) lets shapes with few 64-row
+ * tiles split K over more workgroups; NULL / smaller runs them unsplit.
+ * The result is the same bits either way only up to FP32 summation
+ * order; a given (shape, workspace) choice is deterministic.
  */
+size_t rq_gemv_workspace_bytes(int64_t B, int64_t N, int64_t K);
 rq_status rq_gemv_nibble_escalate(const void *x_bf16, int64_t B, int64_t K,
                                   int64_t N, const uint8_t *w_hi,
                                   const uint8_t *w_lo,
                                   const uint16_t *scales_tiled,
                                   const uint8_t *flags, int phase,
+                                  void *workspace, size_t ws_bytes,
                                   void *y_bf16, void *stream);
 
 /*

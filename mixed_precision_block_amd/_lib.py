@@ -53,7 +53,8 @@ _SIGNATURES = {
     "rq_nibble_plane_bytes": (_SZ, [_I64, _I64]),
     "rq_nibble_scale_bytes": (_SZ, [_I64, _I64]),
     "rq_pack_nibble_planes": (_INT, [_P, _P, _I64, _I64, _P, _P, _P, _P]),
-    "rq_gemv_nibble_escalate": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _INT, _P, _P]),
+    "rq_gemv_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "rq_gemv_nibble_escalate": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _INT, _P, _SZ, _P, _P]),
     "rq_escalation_gate": (_INT, [_P, _I64, _I64, _F, _F, _P, _P, _P]),
     "rq_kv_quantize": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P]),
 }
@@ -157,10 +158,15 @@ def rq_pack_nibble_planes(w, scales, N, K, hi, lo, scales_tiled, stream=None):
                                                                 _ptr(scales_tiled), _stream(stream)))
 
 
-def rq_gemv_nibble_escalate(x, B, K, N, w_hi, w_lo, scales_tiled, flags, phase, y, stream=None):
+def rq_gemv_workspace_bytes(B, N, K):
+    return lib().rq_gemv_workspace_bytes(B, N, K)
+
+
+def rq_gemv_nibble_escalate(x, B, K, N, w_hi, w_lo, scales_tiled, flags, phase, workspace, ws_bytes, y,
+                            stream=None):
     _check("rq_gemv_nibble_escalate",
            lib().rq_gemv_nibble_escalate(_ptr(x), B, K, N, _ptr(w_hi), _ptr(w_lo), _ptr(scales_tiled), _ptr(flags),
-                                         phase, _ptr(y), _stream(stream)))
+                                         phase, _ptr(workspace), ws_bytes, _ptr(y), _stream(stream)))
 
 
 def rq_escalation_gate(logits, B, V, tau, delta, flags, stats, stream=None):

@@ -90,12 +90,15 @@ def pack_nibble_planes(w, scales_f16, stream=None):
     return hi, lo, st
 
 
-def gemv_nibble_escalate(x, N, planes, flags=None, phase=L.RQ_BOTH, y=None, stream=None):
+def gemv_nibble_escalate(x, N, planes, flags=None, phase=L.RQ_BOTH, y=None, stream=None, split=True):
+    """split=False runs every shape unsplit (no workspace)."""
     B, K = x.shape
     hi, lo, st = planes
     if y is None:
         y = torch.empty((B, N), dtype=torch.bfloat16, device=x.device)
-    L.rq_gemv_nibble_escalate(x, B, K, N, hi, lo, st, flags, phase, y, stream)
+    wsb = L.rq_gemv_workspace_bytes(B, N, K) if split else 0
+    ws = _u8((wsb,), x.device) if wsb else None
+    L.rq_gemv_nibble_escalate(x, B, K, N, hi, lo, st, flags, phase, ws, wsb, y, stream)
     return y
 
 

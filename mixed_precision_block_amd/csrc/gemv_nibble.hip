@@ -6,17 +6,21 @@
 // (two's complement) and lo = w & 15, tiled by 64 rows so that a wave's
 // 64 lanes read 64 consecutive 16-byte chunks (one 32-element block of 64
 // rows = 1 KiB, fully coalesced).  Inside a chunk, dword q holds the
-// nibbles of k = 8q + 2j in bits 4j+3..4j and of k + 1 in bits 4j+19..4j+16,
-// so one bit-field extract per element and one dword merge per pair give
-// the BF16 pair (w_k, w_{k+1}) that v_dot2_f32_bf16 multiplies with the
-// token pair (x_k, x_{k+1}) -- a plain aligned dword of the BF16 row.
+// nibbles of k = 8q + 2j in bits 4j+3..4j and of k + 1 in bits 4j+19..4j+16.
+// Two masks per dword move every nibble to the top of a byte (the signed
+// byte is then 16 * hi, or with lo merged in, the int8 weight); one
+// sub-dword conversion per element and one pack per pair give the exact
+// BF16 pair (w_k, w_{k+1}) that v_dot2_f32_bf16 multiplies with the token
+// pair (x_k, x_{k+1}) -- a plain aligned dword of the BF16 row.
 //
 // Work split: a workgroup owns 64 rows; its four waves take interleaved
 // 32-blocks of K; per block each lane turns its 16 bytes into 16 exact BF16
-// pairs once and reuses them for every token (x comes through the scalar
-// cache: the address is wave-uniform).  FP32 block partials are scaled by
-// the block's FP16 scale (x16 for the top nibble, exact) and accumulated;
-// the four waves' sums are added in a fixed order through LDS.
+// pairs once and reuses them for every token (low pass: the block's x for
+// all tokens is one coalesced 1 KiB load per wave, broadcast through LDS;
+// escalation: the few flagged tokens' x come through the scalar cache, the
+// address being wave-uniform).  FP32 block partials are scaled by
+// the block's FP16 scale and accumulated; the four waves' sums are added in
+// a fixed order through LDS.
 #include "rq_device.h"
 #include "rq_internal.h"
 
@@ -24,41 +28,165 @@ namespace rq {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ int sbfe(uint32_t v, int off, int w) {
-  return __builtin_amdgcn_sbfe((int)v, off, w);
-}
-// Two small exact integers -> packed BF16 pair (truncation is exact).
-__device__ __forceinline__ bf16x2 pack_ints(int a, int b) {
-  const uint32_t fa = __builtin_bit_cast(uint32_t, (float)a);
-  const uint32_t fb = __builtin_bit_cast(uint32_t, (float)b);
-  return __builtin_bit_cast(bf16x2, (fa >> 16) | (fb & 0xFFFF0000u));
-}
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
 __device__ __forceinline__ float f16_to_f32(uint16_t s) { return (float)__builtin_bit_cast(_Float16, s); }
 
-// The 16 pairs of a hi-plane chunk: pair p = 4q + j covers k = 8q+2j, +1.
-__device__ __forceinline__ void unpack_hi(const uint4 d, bf16x2 wp[16]) {
-  const uint32_t dq[4] = {d.x, d.y, d.z, d.w};
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) wp[4 * q + j] = pack_ints(sbfe(dq[q], 4 * j, 4), sbfe(dq[q], 16 + 4 * j, 4));
+// float of the signed byte N of e: one sub-dword (SDWA) conversion with
+// sign extension.
+template <int N>
+__device__ __forceinline__ float sbyte_f32(uint32_t e) {
+  float r;
+  if constexpr (N == 0)
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(r) : "v"(e));
+  else if constexpr (N == 1)
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(e));
+  else if constexpr (N == 2)
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(e));
+  else
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(e));
+  return r;
+}
+// Two small exact values -> BF16 pair (the conversion is exact).
+__device__ __forceinline__ bf16x2 pk(float a, float b) { return (bf16x2){(__bf16)a, (__bf16)b}; }
+
+// Nibble position p of a dword (bits 4p..4p+3) is k = 8q + 2p for p < 4
+// and k = 8q + 2(p - 4) + 1 for p >= 4.  Byte n of e0 holds position 2n,
+// byte n of e1 position 2n + 1, as signed bytes: pair j = (k = 8q + 2j,
+// k + 1) is (e0 byte 0, e0 byte 2) for j = 0, (e1 0, e1 2) for j = 1,
+// (e0 1, e0 3) for j = 2 and (e1 1, e1 3) for j = 3.
+__device__ __forceinline__ void pairs_from_bytes(uint32_t e0, uint32_t e1, bf16x2* wp) {
+  wp[0] = pk(sbyte_f32<0>(e0), sbyte_f32<2>(e0));
+  wp[1] = pk(sbyte_f32<0>(e1), sbyte_f32<2>(e1));
+  wp[2] = pk(sbyte_f32<1>(e0), sbyte_f32<3>(e0));
+  wp[3] = pk(sbyte_f32<1>(e1), sbyte_f32<3>(e1));
 }
 
-// Full 8-bit weights from the hi and lo chunks: byte (hi << 4 | lo) is the
-// int8 weight.  E0 bytes hold nibble positions 0,2,4,6 and E1 positions
-// 1,3,5,7; pair j combines positions j and j + 4.
+// 16 * hi for the 16 pairs of a hi-plane chunk: moving each nibble to the
+// top of its byte makes the signed byte 16 * hi.
+__device__ __forceinline__ void unpack_hi16(const uint4 d, bf16x2 wp[16]) {
+  const uint32_t dq[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) pairs_from_bytes((dq[q] << 4) & 0xF0F0F0F0u, dq[q] & 0xF0F0F0F0u, wp + 4 * q);
+}
+
+// Full 8-bit weights: byte (hi << 4 | lo) of a nibble position is the
+// int8 weight.
 __device__ __forceinline__ void unpack_full(const uint4 dh, const uint4 dl, bf16x2 wp[16]) {
   const uint32_t h[4] = {dh.x, dh.y, dh.z, dh.w};
   const uint32_t l[4] = {dl.x, dl.y, dl.z, dl.w};
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t e0 = ((h[q] << 4) & 0xF0F0F0F0u) | (l[q] & 0x0F0F0F0Fu);
-    const uint32_t e1 = (h[q] & 0xF0F0F0F0u) | ((l[q] >> 4) & 0x0F0F0F0Fu);
+  for (int q = 0; q < 4; ++q)
+    pairs_from_bytes(((h[q] << 4) & 0xF0F0F0F0u) | (l[q] & 0x0F0F0F0Fu),
+                     (h[q] & 0xF0F0F0F0u) | ((l[q] >> 4) & 0x0F0F0F0Fu), wp + 4 * q);
+}
+
+// Both passes share one loop: a workgroup owns 64 rows and the K-blocks
+// [b0, b1) of its slice (grid y splits K when there are too few row tiles
+// to fill the chip); wave w takes blocks b0 + w, b0 + w + 4, ...  The
+// workgroup computes TB accumulator slots; slot t is token tok[t] for
+// t < nt.  The four waves' sums meet in LDS in a fixed order; with one
+// slice the workgroup writes BF16 outputs, otherwise FP32 partials to
+// ws[slice][token][row] (16 token rows per slice) that gemv_reduce_kernel
+// adds in slice order.
+constexpr int kWsTokens = 16;
+
+template <int TB, bool kFull>
+__device__ __forceinline__ void gemv_tile(const uint16_t* __restrict__ x, int B, int K, int N,
+                                          const uint8_t* __restrict__ hi, const uint8_t* __restrict__ lo,
+                                          const uint16_t* __restrict__ sc, const int* tok, int nt,
+                                          uint16_t* __restrict__ y, float* __restrict__ ws, float (*red)[TB][64],
+                                          uint4* xs) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tile = blockIdx.x, slice = blockIdx.y, nslice = gridDim.y;
+  const int nb = K >> 5;
+  const int per = (nb + nslice - 1) / nslice;
+  const int b0 = slice * per, b1 = min(nb, b0 + per);
+  const size_t tbase = (size_t)tile * nb * 64 + lane;
+  const uint4* hp = reinterpret_cast<const uint4*>(hi) + tbase;
+  const uint4* lp = reinterpret_cast<const uint4*>(lo) + tbase;
+  const uint16_t* sp = sc + tbase;
+  // Low pass: x of the current block for all tokens -- lane l fetches 8
+  // values (16 bytes) of token l / 4 one block ahead, the wave parks them
+  // in its own 1 KiB LDS slot, and every lane reads them back as broadcasts.
+  const int xt_l = (lane >> 2) < B ? (lane >> 2) : B - 1;
+  const uint4* xg = reinterpret_cast<const uint4*>(x + (size_t)xt_l * K) + (lane & 3);
+  uint4* const xslot = xs + wave * 64;
+  float acc[TB];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t e = (j & 1) ? e1 : e0;
-      wp[4 * q + j] = pack_ints(sbfe(e, 8 * (j >> 1), 8), sbfe(e, 8 * (2 + (j >> 1)), 8));
+  for (int t = 0; t < TB; ++t) acc[t] = 0.0f;
+
+  int b = b0 + wave;
+  uint4 xv = make_uint4(0, 0, 0, 0);
+  if (!kFull && b < b1) xv = xg[(size_t)b * 4];
+  // escalation (memory-bound): the next block's planes load one block ahead
+  uint4 nh = make_uint4(0, 0, 0, 0), nl = make_uint4(0, 0, 0, 0);
+  uint16_t ns = 0;
+  if (kFull && b < b1) {
+    nh = hp[(size_t)b * 64];
+    nl = lp[(size_t)b * 64];
+    ns = sp[(size_t)b * 64];
+  }
+  for (; b < b1; b += 4) {
+    uint4 dh, dl = make_uint4(0, 0, 0, 0);
+    float s;
+    if constexpr (kFull) {
+      dh = nh, dl = nl;
+      s = f16_to_f32(ns);
+      const int bn = b + 4 < b1 ? b + 4 : b;  // the last block reloads itself
+      nh = hp[(size_t)bn * 64];
+      nl = lp[(size_t)bn * 64];
+      ns = sp[(size_t)bn * 64];
+    } else {
+      dh = hp[(size_t)b * 64];
+      s = f16_to_f32(sp[(size_t)b * 64]);
+    }
+    if constexpr (!kFull) {
+      // a wave's LDS accesses complete in order: this write follows the
+      // reads of the previous block and precedes the reads below
+      xslot[lane] = xv;
+      const int bn = b + 4 < b1 ? b + 4 : b;  // next block's x (the last reloads itself)
+      xv = xg[(size_t)bn * 4];
+    }
+    bf16x2 wp[16];
+    if constexpr (kFull)
+      unpack_full(dh, dl, wp);
+    else
+      unpack_hi16(dh, wp);
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      if (kFull && t >= nt) continue;  // wave-uniform; the low pass computes every slot
+      uint32_t xq[16];
+      if constexpr (kFull) {
+        // the few flagged tokens: x straight through the scalar cache
+        const uint32_t* xt = reinterpret_cast<const uint32_t*>(x) + ((size_t)tok[t] * K + 32 * (size_t)b) / 2;
+#pragma unroll
+        for (int p = 0; p < 16; ++p) xq[p] = xt[p];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint4 v = xslot[4 * t + i];
+          xq[4 * i] = v.x, xq[4 * i + 1] = v.y, xq[4 * i + 2] = v.z, xq[4 * i + 3] = v.w;
+        }
+      }
+      float blk = 0.0f;
+#pragma unroll
+      for (int p = 0; p < 16; ++p) blk = __builtin_amdgcn_fdot2_f32_bf16(wp[p], as_bf16x2(xq[p]), blk, false);
+      acc[t] = fmaf(blk, s, acc[t]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TB; ++t) red[wave][t][lane] = acc[t];
+  __syncthreads();
+  for (int o = threadIdx.x; o < TB * 64; o += 256) {
+    const int t = o >> 6, l = o & 63;
+    const int n = tile * 64 + l;
+    if (t >= nt) continue;
+    const float v = ((red[0][t][l] + red[1][t][l]) + red[2][t][l]) + red[3][t][l];
+    if (nslice == 1) {
+      if (n < N) y[(size_t)tok[t] * N + n] = (uint16_t)f32_to_bf16(v);
+    } else {
+      ws[((size_t)slice * kWsTokens + tok[t]) * (gridDim.x * 64) + n] = v;
     }
   }
 }
@@ -66,98 +194,55 @@ __device__ __forceinline__ void unpack_full(const uint4 dh, const uint4 dl, bf16
 template <int TB>
 __global__ __launch_bounds__(256) void gemv_low_kernel(const uint16_t* __restrict__ x, int B, int K, int N,
                                                        const uint8_t* __restrict__ hi,
-                                                       const uint16_t* __restrict__ sc, uint16_t* __restrict__ y) {
+                                                       const uint16_t* __restrict__ sc, uint16_t* __restrict__ y,
+                                                       float* __restrict__ ws) {
   __shared__ float red[4][TB][64];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tile = blockIdx.x;
-  const int nb = K >> 5;
-  const uint4* hp = reinterpret_cast<const uint4*>(hi) + (size_t)tile * nb * 64 + lane;
-  const uint16_t* sp = sc + (size_t)tile * nb * 64 + lane;
-  const uint32_t* x32 = reinterpret_cast<const uint32_t*>(x);
-  float acc[TB];
+  __shared__ uint4 xs[4 * 64];
+  int tok[TB];
 #pragma unroll
-  for (int t = 0; t < TB; ++t) acc[t] = 0.0f;
-
-  for (int b = wave; b < nb; b += 4) {
-    const uint4 d = hp[(size_t)b * 64];
-    const float s = f16_to_f32(sp[(size_t)b * 64]) * 16.0f;
-    bf16x2 wp[16];
-    unpack_hi(d, wp);
-#pragma unroll
-    for (int t = 0; t < TB; ++t) {
-      const int tt = t < B ? t : B - 1;
-      const uint32_t* xt = x32 + ((size_t)tt * K + 32 * (size_t)b) / 2;
-      float blk = 0.0f;
-#pragma unroll
-      for (int p = 0; p < 16; ++p) blk = __builtin_amdgcn_fdot2_f32_bf16(wp[p], as_bf16x2(xt[p]), blk, false);
-      acc[t] = fmaf(blk, s, acc[t]);
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < TB; ++t) red[wave][t][lane] = acc[t];
-  __syncthreads();
-  for (int o = threadIdx.x; o < TB * 64; o += 256) {
-    const int t = o >> 6, l = o & 63;
-    const int n = tile * 64 + l;
-    if (t < B && n < N) {
-      const float v = ((red[0][t][l] + red[1][t][l]) + red[2][t][l]) + red[3][t][l];
-      y[(size_t)t * N + n] = (uint16_t)f32_to_bf16(v);
-    }
-  }
+  for (int t = 0; t < TB; ++t) tok[t] = t;
+  gemv_tile<TB, false>(x, B, K, N, hi, nullptr, sc, tok, B < TB ? B : TB, y, ws, red, xs);
 }
 
-template <int TB>
+// Escalation: workgroup z takes the flagged tokens of rank 4z .. 4z + 3
+// (ranks in token order); groups past the last flagged token exit at once.
+constexpr int kEscTokens = 4;
+
 __global__ __launch_bounds__(256) void gemv_escalate_kernel(const uint16_t* __restrict__ x, int B, int K, int N,
                                                             const uint8_t* __restrict__ hi,
                                                             const uint8_t* __restrict__ lo,
                                                             const uint16_t* __restrict__ sc,
                                                             const uint8_t* __restrict__ flags,
-                                                            uint16_t* __restrict__ y) {
-  __shared__ float red[4][TB][64];
+                                                            uint16_t* __restrict__ y, float* __restrict__ ws) {
+  __shared__ float red[4][kEscTokens][64];
   uint32_t fmask = 0;
   for (int t = 0; t < B; ++t) fmask |= (flags[t] != 0 ? 1u : 0u) << t;
   fmask = __builtin_amdgcn_readfirstlane(fmask);
-  if (fmask == 0) return;  // nothing flagged: no weight traffic
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tile = blockIdx.x;
-  const int nb = K >> 5;
-  const uint4* hp = reinterpret_cast<const uint4*>(hi) + (size_t)tile * nb * 64 + lane;
-  const uint4* lp = reinterpret_cast<const uint4*>(lo) + (size_t)tile * nb * 64 + lane;
-  const uint16_t* sp = sc + (size_t)tile * nb * 64 + lane;
-  const uint32_t* x32 = reinterpret_cast<const uint32_t*>(x);
-  float acc[TB];
+  for (int r = 0; r < kEscTokens * (int)blockIdx.z; ++r) fmask &= fmask - 1u;  // drop earlier groups
+  if (fmask == 0) return;  // nothing (more) flagged: no weight traffic
+  int tok[kEscTokens];
+  int nt = 0;
 #pragma unroll
-  for (int t = 0; t < TB; ++t) acc[t] = 0.0f;
+  for (int t = 0; t < kEscTokens; ++t) {
+    tok[t] = fmask ? __builtin_ctz(fmask) : 0;
+    nt += fmask ? 1 : 0;
+    fmask &= fmask - 1u;
+  }
+  gemv_tile<kEscTokens, true>(x, B, K, N, hi, lo, sc, tok, nt, y, ws, red, nullptr);
+}
 
-  for (int b = wave; b < nb; b += 4) {
-    const uint4 dh = hp[(size_t)b * 64];
-    const uint4 dl = lp[(size_t)b * 64];
-    const float s = f16_to_f32(sp[(size_t)b * 64]);
-    bf16x2 wp[16];
-    unpack_full(dh, dl, wp);
-#pragma unroll
-    for (int t = 0; t < TB; ++t) {
-      if (!((fmask >> t) & 1u)) continue;  // wave-uniform branch
-      const uint32_t* xt = x32 + ((size_t)t * K + 32 * (size_t)b) / 2;
-      float blk = 0.0f;
-#pragma unroll
-      for (int p = 0; p < 16; ++p) blk = __builtin_amdgcn_fdot2_f32_bf16(wp[p], as_bf16x2(xt[p]), blk, false);
-      acc[t] = fmaf(blk, s, acc[t]);
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < TB; ++t) red[wave][t][lane] = acc[t];
-  __syncthreads();
-  for (int o = threadIdx.x; o < TB * 64; o += 256) {
-    const int t = o >> 6, l = o & 63;
-    const int n = tile * 64 + l;
-    if (t < B && ((fmask >> t) & 1u) && n < N) {
-      const float v = ((red[0][t][l] + red[1][t][l]) + red[2][t][l]) + red[3][t][l];
-      y[(size_t)t * N + n] = (uint16_t)f32_to_bf16(v);
-    }
-  }
+// y[t][n] = BF16(sum over slices of ws[slice][t][n]) in slice order, for
+// every token (flags == nullptr) or the flagged ones.
+__global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restrict__ ws, int nslice, int B, int N,
+                                                          int Np, const uint8_t* __restrict__ flags,
+                                                          uint16_t* __restrict__ y) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)B * N) return;
+  const int t = (int)(i / N), n = (int)(i - (int64_t)t * N);
+  if (flags && !flags[t]) return;
+  float v = 0.0f;
+  for (int sl = 0; sl < nslice; ++sl) v += ws[((size_t)sl * kWsTokens + t) * Np + n];
+  y[i] = (uint16_t)f32_to_bf16(v);
 }
 
 // One thread per (padded row, 32-block): 32 int8 weights -> one 16-byte
@@ -200,39 +285,72 @@ hipError_t launch_pack_nibble_planes(const int8_t* w, const uint16_t* scales, in
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_low(const uint16_t* x, int64_t B, int64_t K, int64_t N, const uint8_t* hi,
-                           const uint16_t* scales, uint16_t* y, hipStream_t stream) {
-  const unsigned g = (unsigned)((N + 63) / 64);
-  if (g == 0) return hipSuccess;
-  const int b = (int)B, k = (int)K, n = (int)N;
-  if (B <= 1)
-    gemv_low_kernel<1><<<g, 256, 0, stream>>>(x, b, k, n, hi, scales, y);
-  else if (B <= 2)
-    gemv_low_kernel<2><<<g, 256, 0, stream>>>(x, b, k, n, hi, scales, y);
-  else if (B <= 4)
-    gemv_low_kernel<4><<<g, 256, 0, stream>>>(x, b, k, n, hi, scales, y);
-  else if (B <= 8)
-    gemv_low_kernel<8><<<g, 256, 0, stream>>>(x, b, k, n, hi, scales, y);
-  else
-    gemv_low_kernel<16><<<g, 256, 0, stream>>>(x, b, k, n, hi, scales, y);
+static int gemv_tb(int64_t B) { return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B <= 8 ? 8 : 16; }
+
+// K slices per row tile: one when the row tiles alone give 256 workgroups,
+// else enough for about 512 workgroups, each keeping at least one block
+// per wave.
+int gemv_slices(int64_t N, int64_t K) {
+  const int64_t tiles = (N + 63) / 64, nb = K / 32;
+  if (tiles == 0 || tiles >= 256) return 1;
+  int64_t s = (512 + tiles - 1) / tiles;
+  const int64_t cap = nb / 4 > 1 ? nb / 4 : 1;
+  return (int)(s < cap ? s : cap);
+}
+
+size_t gemv_workspace_bytes(int64_t B, int64_t N, int64_t K) {
+  (void)B;
+  const int s = gemv_slices(N, K);
+  return s > 1 ? (size_t)s * kWsTokens * ((N + 63) / 64 * 64) * sizeof(float) : 0;
+}
+
+static int slices_for(int64_t B, int64_t N, int64_t K, size_t ws_bytes) {
+  const int s = gemv_slices(N, K);
+  return (s > 1 && ws_bytes >= gemv_workspace_bytes(B, N, K)) ? s : 1;
+}
+
+static hipError_t launch_reduce(const float* ws, int nslice, int64_t B, int64_t N, const uint8_t* flags,
+                                uint16_t* y, hipStream_t stream) {
+  const int64_t total = B * N;
+  gemv_reduce_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(ws, nslice, (int)B, (int)N,
+                                                                          (int)((N + 63) / 64 * 64), flags, y);
   return hipGetLastError();
+}
+
+hipError_t launch_gemv_low(const uint16_t* x, int64_t B, int64_t K, int64_t N, const uint8_t* hi,
+                           const uint16_t* scales, uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const unsigned tiles = (unsigned)((N + 63) / 64);
+  if (tiles == 0) return hipSuccess;
+  const int ns = slices_for(B, N, K, ws_bytes);
+  const dim3 grid(tiles, ns);
+  const int b = (int)B, k = (int)K, n = (int)N;
+  float* w = static_cast<float*>(ws);
+  switch (gemv_tb(B)) {
+    case 1: gemv_low_kernel<1><<<grid, 256, 0, stream>>>(x, b, k, n, hi, scales, y, w); break;
+    case 2: gemv_low_kernel<2><<<grid, 256, 0, stream>>>(x, b, k, n, hi, scales, y, w); break;
+    case 4: gemv_low_kernel<4><<<grid, 256, 0, stream>>>(x, b, k, n, hi, scales, y, w); break;
+    case 8: gemv_low_kernel<8><<<grid, 256, 0, stream>>>(x, b, k, n, hi, scales, y, w); break;
+    default: gemv_low_kernel<16><<<grid, 256, 0, stream>>>(x, b, k, n, hi, scales, y, w); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && ns > 1) e = launch_reduce(w, ns, B, N, nullptr, y, stream);
+  return e;
 }
 
 hipError_t launch_gemv_escalate(const uint16_t* x, int64_t B, int64_t K, int64_t N, const uint8_t* hi,
                                 const uint8_t* lo, const uint16_t* scales, const uint8_t* flags, uint16_t* y,
-                                hipStream_t stream) {
-  const unsigned g = (unsigned)((N + 63) / 64);
-  if (g == 0) return hipSuccess;
+                                void* ws, size_t ws_bytes, hipStream_t stream) {
+  const unsigned tiles = (unsigned)((N + 63) / 64);
+  if (tiles == 0) return hipSuccess;
+  const int ns = slices_for(B, N, K, ws_bytes);
   const int b = (int)B, k = (int)K, n = (int)N;
-  if (B <= 2)
-    gemv_escalate_kernel<2><<<g, 256, 0, stream>>>(x, b, k, n, hi, lo, scales, flags, y);
-  else if (B <= 4)
-    gemv_escalate_kernel<4><<<g, 256, 0, stream>>>(x, b, k, n, hi, lo, scales, flags, y);
-  else if (B <= 8)
-    gemv_escalate_kernel<8><<<g, 256, 0, stream>>>(x, b, k, n, hi, lo, scales, flags, y);
-  else
-    gemv_escalate_kernel<16><<<g, 256, 0, stream>>>(x, b, k, n, hi, lo, scales, flags, y);
-  return hipGetLastError();
+  float* w = static_cast<float*>(ws);
+  // up to four groups of four flagged tokens
+  const dim3 grid3(tiles, ns, (unsigned)((B + kEscTokens - 1) / kEscTokens));
+  gemv_escalate_kernel<<<grid3, 256, 0, stream>>>(x, b, k, n, hi, lo, scales, flags, y, w);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && ns > 1) e = launch_reduce(w, ns, B, N, flags, y, stream);
+  return e;
 }
 
 }  // namespace rq

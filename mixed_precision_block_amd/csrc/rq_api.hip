@@ -258,9 +258,14 @@ rq_status rq_pack_nibble_planes(const int8_t* w, const uint16_t* scales_f16, int
                     "rq_pack_nibble_planes launch");
 }
 
+size_t rq_gemv_workspace_bytes(int64_t B, int64_t N, int64_t K) {
+  if (B < 1 || B > 16 || N <= 0 || K <= 0 || K % 32) return 0;
+  return rq::gemv_workspace_bytes(B, N, K);
+}
+
 rq_status rq_gemv_nibble_escalate(const void* x_bf16, int64_t B, int64_t K, int64_t N, const uint8_t* w_hi,
                                   const uint8_t* w_lo, const uint16_t* scales_tiled, const uint8_t* flags, int phase,
-                                  void* y_bf16, void* stream) {
+                                  void* workspace, size_t ws_bytes, void* y_bf16, void* stream) {
   if (!x_bf16 || !w_hi || !scales_tiled || !y_bf16) return fail(RQ_EINVAL, "rq_gemv_nibble_escalate: null pointer");
   if (phase != RQ_LOW && phase != RQ_ESCALATE && phase != RQ_BOTH)
     return fail(RQ_EINVAL, "rq_gemv_nibble_escalate: unknown phase %d", phase);
@@ -271,13 +276,16 @@ rq_status rq_gemv_nibble_escalate(const void* x_bf16, int64_t B, int64_t K, int6
     return fail(RQ_ESHAPE, "rq_gemv_nibble_escalate: need K > 0, K %% 32 == 0");
   if (!aligned16(x_bf16) || !aligned16(w_hi) || (w_lo && !aligned16(w_lo)))
     return fail(RQ_EALIGN, "rq_gemv_nibble_escalate: x and planes must be 16-byte aligned");
+  if (workspace && !aligned16(workspace)) return fail(RQ_EALIGN, "rq_gemv_nibble_escalate: workspace must be 16-byte aligned");
   if (rq_status s = need_device(); s != RQ_OK) return s;
   hipStream_t st = as_stream(stream);
   const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
   uint16_t* y = static_cast<uint16_t*>(y_bf16);
   hipError_t e = hipSuccess;
-  if (phase & RQ_LOW) e = rq::launch_gemv_low(x, B, K, N, w_hi, scales_tiled, y, st);
-  if (e == hipSuccess && (phase & RQ_ESCALATE)) e = rq::launch_gemv_escalate(x, B, K, N, w_hi, w_lo, scales_tiled, flags, y, st);
+  const size_t wsb = workspace ? ws_bytes : 0;
+  if (phase & RQ_LOW) e = rq::launch_gemv_low(x, B, K, N, w_hi, scales_tiled, y, workspace, wsb, st);
+  if (e == hipSuccess && (phase & RQ_ESCALATE))
+    e = rq::launch_gemv_escalate(x, B, K, N, w_hi, w_lo, scales_tiled, flags, y, workspace, wsb, st);
   return hip_status(e, "rq_gemv_nibble_escalate launch");
 }
 

@@ -52,11 +52,16 @@ hipError_t launch_rmsnorm(int fmt, const uint16_t* h, int64_t rows, int64_t D, f
 hipError_t launch_pack_nibble_planes(const int8_t* w, const uint16_t* scales, int64_t N, int64_t K,
                                      uint8_t* hi, uint8_t* lo, uint16_t* scales_tiled,
                                      hipStream_t stream);
+// Workspace (FP32 partials of split-K launches) of rq_gemv_nibble_escalate;
+// 0 when the shape needs no split.  With less workspace than this the
+// kernels run unsplit.
+size_t gemv_workspace_bytes(int64_t B, int64_t N, int64_t K);
 hipError_t launch_gemv_low(const uint16_t* x, int64_t B, int64_t K, int64_t N, const uint8_t* hi,
-                           const uint16_t* scales, uint16_t* y, hipStream_t stream);
+                           const uint16_t* scales, uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream);
 hipError_t launch_gemv_escalate(const uint16_t* x, int64_t B, int64_t K, int64_t N,
                                 const uint8_t* hi, const uint8_t* lo, const uint16_t* scales,
-                                const uint8_t* flags, uint16_t* y, hipStream_t stream);
+                                const uint8_t* flags, uint16_t* y, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
 hipError_t launch_gate(const uint16_t* logits, int64_t B, int64_t V, float tau, float delta,
                        uint8_t* flags, float* stats, hipStream_t stream);
 hipError_t launch_kv_quant(const uint16_t* x, int64_t T, int64_t H, int64_t D, uint8_t* codes,

@@ -113,9 +113,9 @@ def test_recurrent_prefill_validation():
 
 
 def test_gemv_and_gate_validation():
-    g = [A16, 16, 1024, 64, A16, A16, A16, A16, L.RQ_BOTH, A16]
+    g = [A16, 16, 1024, 64, A16, A16, A16, A16, L.RQ_BOTH, None, 0, A16]
     for i, v, want in [(1, 0, L.RQ_ESHAPE), (1, 17, L.RQ_ESHAPE), (2, 1000, L.RQ_ESHAPE), (8, 4, L.RQ_EINVAL),
-                       (5, None, L.RQ_EINVAL), (7, None, L.RQ_EINVAL)]:
+                       (5, None, L.RQ_EINVAL), (7, None, L.RQ_EINVAL), (9, A16 + 4, L.RQ_EALIGN)]:
         a = list(g)
         a[i] = v
         assert status_of(rq.rq_gemv_nibble_escalate, *a) == want, (i, v)
@@ -125,6 +125,12 @@ def test_gemv_and_gate_validation():
     assert status_of(rq.rq_gemv_nibble_escalate, *lowonly) in (L.RQ_OK, L.RQ_ENODEV)
     assert status_of(rq.rq_escalation_gate, A16, 0, 100, 1.0, 0.1, A16, None) == L.RQ_ESHAPE
     assert status_of(rq.rq_kv_quantize, A16, 4, 2, 100, A16, A16) == L.RQ_ESHAPE
+    # split-K workspace: few row tiles -> slices x 16 token rows x padded rows x FP32; many tiles or bad shapes -> 0
+    assert rq.rq_gemv_workspace_bytes(16, 1024, 1024) == 8 * 16 * 1024 * 4
+    assert rq.rq_gemv_workspace_bytes(1, 100, 1024) == 8 * 16 * 128 * 4
+    assert rq.rq_gemv_workspace_bytes(16, 151936, 1024) == 0
+    assert rq.rq_gemv_workspace_bytes(16, 1024, 100) == 0
+    assert rq.rq_gemv_workspace_bytes(17, 1024, 1024) == 0
     assert rq.rq_nibble_plane_bytes(100, 64) == 128 * 32
     assert rq.rq_nibble_scale_bytes(100, 64) == 128 * 2 * 2
 

@@ -53,10 +53,10 @@ def test_pack_layout():
     assert np.array_equal(host(st).view(np.uint16), ts)
 
 
-def run(x, w, scales, flags, phase, N):
+def run(x, w, scales, flags, phase, N, split=True):
     planes = gpu_planes(w, scales)
     fl = None if flags is None else dev(np.asarray(flags, np.uint8))
-    return host_bits(api.gemv_nibble_escalate(dev_bf16(x), N, planes, fl, phase))
+    return host_bits(api.gemv_nibble_escalate(dev_bf16(x), N, planes, fl, phase, split=split))
 
 
 def test_worked_example():
@@ -74,18 +74,21 @@ def test_worked_example():
     assert F.bf16_to_f64(run(xb, w, s, [0, 1], L.RQ_BOTH, 2)).ravel().tolist() == g["y_mixed"]
 
 
+@pytest.mark.parametrize("split", [True, False])
 @pytest.mark.parametrize("B", [1, 2, 5, 16])
-@pytest.mark.parametrize("N,K", [(200, 96), (64, 32), (1000, 1024)])
-def test_small_against_oracle(B, N, K):
+@pytest.mark.parametrize("N,K", [(200, 96), (64, 32), (1000, 1024), (130, 3072)])
+def test_small_against_oracle(B, N, K, split):
+    """Few row tiles: with a workspace the launch splits K over workgroups
+    (slices of 1..32 blocks, some empty), without one it does not."""
     d = W.c5_linear(3, B=B, N=N, K=K)
     flags = np.zeros(B, np.uint8)
     flags[::3] = 1
-    log(f"gemv B={B} N={N} K={K}")
-    y_low = run(d["x"], d["w"], d["scales"], None, L.RQ_LOW, N)
+    log(f"gemv B={B} N={N} K={K} split={split} workspace={L.rq_gemv_workspace_bytes(B, N, K)}")
+    y_low = run(d["x"], d["w"], d["scales"], None, L.RQ_LOW, N, split)
     hi, _ = V.split_nibbles(d["w"])
     check_bf16(y_low, V.low_pass(d["x"], d["w"], d["scales"]),
                V.abs_bound(d["x"], 16 * hi.astype(np.int64), d["scales"]), "low pass", k=K)
-    y = run(d["x"], d["w"], d["scales"], flags, L.RQ_BOTH, N)
+    y = run(d["x"], d["w"], d["scales"], flags, L.RQ_BOTH, N, split)
     ref = V.low_pass(d["x"], d["w"], d["scales"])
     ref[flags == 1] = V.full_pass(d["x"][flags == 1], d["w"], d["scales"])
     bound = V.abs_bound(d["x"], d["w"], d["scales"]) + V.abs_bound(d["x"], 16 * hi.astype(np.int64), d["scales"])
