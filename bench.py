@@ -32,16 +32,19 @@ sys.path.insert(0, ROOT)
 
 PEAK = {"mxfp4": 10.1e15, "mxfp8": 5.0e15, "bf16": 2.5e15, "hbm": 8.0e12}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_mxfp8_qwen3_linear_set.json")
-GEMM_SRC = os.path.join(ROOT, "mixed_precision_block_amd", "csrc", "gemm.hip")
+GEMM_SRCS = [os.path.join(ROOT, "mixed_precision_block_amd", "csrc", f) for f in ("gemm.hip", "gemm_pipe.hip")]
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():
@@ -52,7 +55,7 @@ def measured_traffic():
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("gemm_source_sha256_16") != source_hash(GEMM_SRC):
+    if t.get("gemm_source_sha256_16") != source_hash(GEMM_SRCS):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -102,6 +105,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-rows", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run plain 256 MiB device copies (the reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (no multi-GPU path is built).",
@@ -120,6 +125,14 @@ def main():
         sys.exit(1)
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": src.numel(), "copies": 5}), flush=True)
+        return
 
     def to_dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev)
@@ -179,7 +192,7 @@ def main():
         "config": {"workload": "qwen3-0.6b linear set (q,k,v,o,gate,up,down), 4096-token prefill, "
                                "MXFP8 W/A, dynamic per-32 activation quantization + block-scaled GEMM",
                    "tokens": M, "gemm_gflop_per_step": round(flops_step / 1e9, 2)},
-        "roofline": {"bound": "mfma", "kernel": "gemm_kernel<MXFP8, BF16 out>",
+        "roofline": {"bound": "mfma", "kernel": "gemm_pipe_kernel<MXFP8, BF16 out, 128x128 tiles>",
                      "achieved": round(achieved / 1e12, 2), "peak": PEAK["mxfp8"] / 1e12, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK["mxfp8"], 4), "traffic": traffic,
                      "avg_launch_us": round(gemm_ms * 1e3, 2)},
