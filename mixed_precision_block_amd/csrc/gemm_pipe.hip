@@ -4,18 +4,20 @@
 // item 3: block scales applied inside the matrix core), organized for
 // throughput on large problems:
 //
-// * Every pipeline stage holds one 64-byte chunk of each row of the A and W
-//   tiles: 128 K of MXFP4, 64 K of MXFP8 or 32 K of BF16, so each stage
-//   carries the same matrix-core work (1024 cycles per wave at 256 x 256).
+// * A pipeline stage holds one RB-byte chunk (RB = 128, or 64 where K does
+//   not divide) of every row of the A and W tiles: 2 RB elements of MXFP4,
+//   RB of MXFP8 or RB / 2 of BF16, so each stage carries the same
+//   matrix-core work whatever the format.  128-byte chunks are whole cache
+//   lines for the global loads.
 // * Global loads are buffer loads (the resource spans the tile's rows, so
 //   rows past M or N read as zeros) into a ring of P register slots, issued
 //   P stages ahead; each stage is then written to one of two LDS buffers
-//   while the other feeds the MFMAs.  The loop is unrolled over the ring so
-//   every register slot is static, and the compiler's load counters wait
-//   exactly for the slot being written out.
-// * LDS rows are 64 bytes; the 16-byte chunk c of row r sits at chunk
-//   c ^ ((r >> 1 ^ r >> 3) & 3), which keeps the 16-byte fragment reads of
-//   8 or 16 consecutive rows on distinct banks.
+//   while the other feeds the MFMAs.  The loop is unrolled over the ring and
+//   the two buffers so every register slot is static, and the compiler's
+//   load counters wait exactly for the slot being written out.
+// * LDS rows are RB bytes of 16-byte chunks, XOR-swizzled per row so that
+//   the fragment reads of consecutive rows hit distinct banks (checked for
+//   both 32- and 64-bank LDS models).
 // * Four waves in a 2 x 2 arrangement, each owning a (BM/2) x (BN/2)
 //   quadrant of (BM/64) x (BN/64) MFMA tiles of 32 x 32; accumulators live
 //   in AGPRs.
@@ -27,7 +29,8 @@
 // Operand layout per MFMA is the one pinned for gemm.hip: FP4 lane half h
 // holds K [32h, 32h+32) of a 64-deep slice; FP8 lane half h holds
 // K [16h, 16h+16) and [32+16h, 32+16h+16); BF16 lane half h holds 8
-// elements at 8h of a 16-deep slice.
+// elements at 8h of a 16-deep slice.  Slice kk's block scales are bytes
+// 2 kk and 2 kk + 1 of the row's stage scales, lane half h taking 2 kk + h.
 #include <type_traits>
 
 #include "rq_device.h"
@@ -40,63 +43,82 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-template <int FMT>
+template <int FMT, int RB>
 struct PipeTraits;
-// One scale dword per row per stage: the four blocks of an MXFP4 stage, or
-// for MXFP8 the dword at (s / 2) * 4 holding this stage's two blocks and
-// its neighbour's.
-template <>
-struct PipeTraits<1> {  // MXFP4: 128 K per stage, two 64-deep MFMA slices
-  static constexpr int kStepElems = 128, kKK = 2, kCbsz = 4;
+template <int RB>
+struct PipeTraits<1, RB> {  // MXFP4: 2 RB K per stage in 64-deep slices
+  static constexpr int kStepElems = 2 * RB, kKK = 2 * RB / 64, kCbsz = 4, kSBPR = 2 * RB / 32;
   static constexpr bool kScaled = true;
 };
-template <>
-struct PipeTraits<2> {  // MXFP8: 64 K per stage, one slice
-  static constexpr int kStepElems = 64, kKK = 1, kCbsz = 0;
+template <int RB>
+struct PipeTraits<2, RB> {  // MXFP8: RB K per stage in 64-deep slices
+  static_assert(RB == 128, "MXFP8 stages are 128 bytes (whole scale dwords)");
+  static constexpr int kStepElems = RB, kKK = RB / 64, kCbsz = 0, kSBPR = RB / 32;
   static constexpr bool kScaled = true;
 };
-template <>
-struct PipeTraits<3> {  // BF16: 32 K per stage, two 16-deep slices
-  static constexpr int kStepElems = 32, kKK = 2, kCbsz = 0;
+template <int RB>
+struct PipeTraits<3, RB> {  // BF16: RB / 2 K per stage in 16-deep slices
+  static constexpr int kStepElems = RB / 2, kKK = RB / 32, kCbsz = 0, kSBPR = 0;
   static constexpr bool kScaled = false;
 };
 
-constexpr int kRowBytes = 64;
-
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// Chunk swizzle of LDS row r.  64-byte rows: chunk bits (r1 ^ r3, r2 ^ r4);
+// 128-byte rows: chunk bits (r0 ^ r3, r2, r1).
+template <int RB>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (RB == 64)
+    return ((r >> 1) ^ (r >> 3)) & 3;
+  else
+    return ((r ^ (r >> 3)) & 1) | ((r >> 1) & 2) | ((r << 1) & 4);
+}
 
 // Publish LDS writes and wait for every wave (no wait on global loads).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int FMT, int BM, int BN>
+template <int FMT, int BM, int BN, int RB>
 struct PipeCfg {
-  using T = PipeTraits<FMT>;
-  static constexpr int TM = BM / 64, TN = BN / 64;                // MFMA tiles per wave
-  static constexpr int CA = BM / 64, CW = BN / 64;                // 16-byte chunks per thread per stage
-  static constexpr int SA = BM * kRowBytes, SW = BN * kRowBytes;  // LDS bytes of the A / W tile
-  static constexpr int SS = T::kScaled ? (BM + BN) * 4 : 0;       // scale dwords
+  using T = PipeTraits<FMT, RB>;
+  static constexpr int TM = BM / 64, TN = BN / 64;            // MFMA tiles per wave
+  static constexpr int CPR = RB / 16;                         // 16-byte chunks per row
+  static constexpr int RPL = 256 / CPR;                       // rows per wave-group load
+  static constexpr int CA = BM / RPL, CW = BN / RPL;          // 16-byte chunks per thread per stage
+  static constexpr int SA = BM * RB, SW = BN * RB;            // LDS bytes of the A / W tile
+  static constexpr int SBPR = T::kSBPR;                       // scale bytes per row per stage
+  static constexpr int SS = (BM + BN) * SBPR;                 // scale bytes per stage
   static constexpr int STAGE = SA + SW + SS;
-  static constexpr int NS = T::kScaled ? (BM + BN) / 256 : 0;     // scale loads per thread
-  static constexpr int P = BM == 256 ? 2 : 4;                     // register ring depth
+  static constexpr int NS = T::kScaled ? (BM + BN) / 256 : 0;  // scale rows per thread
+  static constexpr int SLOT = 4 * (CA + CW);                  // VGPRs of one ring slot
+  static constexpr int P = SLOT >= 64 ? 1 : (SLOT >= 32 ? 2 : 4);  // register ring depth
+  static constexpr int U = P == 1 ? 2 : P;                    // steps per unrolled loop turn
 };
 
-template <int FMT, int BM, int BN>
+template <int SBPR>
+struct ScaleWord {
+  using type = uint32_t;
+};
+template <>
+struct ScaleWord<8> {
+  using type = uint2;
+};
+
+template <int FMT, int BM, int BN, int RB>
 struct StageRegs {
-  using C = PipeCfg<FMT, BM, BN>;
+  using C = PipeCfg<FMT, BM, BN, RB>;
   v4i a[C::CA];
   v4i w[C::CW];
-  uint32_t s[C::NS > 0 ? C::NS : 1];
+  typename ScaleWord<C::SBPR>::type s[C::NS > 0 ? C::NS : 1];
 };
 
-template <int FMT, int EPI, int BM, int BN>
+template <int FMT, int EPI, int BM, int BN, int RB>
 __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __restrict__ A,
                                                            const uint8_t* __restrict__ As,
                                                            const uint8_t* __restrict__ W,
                                                            const uint8_t* __restrict__ Ws, int M, int N, int K,
                                                            void* __restrict__ Y, int tiles_m, int tiles_n) {
-  using C = PipeCfg<FMT, BM, BN>;
-  using T = PipeTraits<FMT>;
-  constexpr int TM = C::TM, TN = C::TN, P = C::P;
+  using C = PipeCfg<FMT, BM, BN, RB>;
+  using T = PipeTraits<FMT, RB>;
+  using SW_t = typename ScaleWord<C::SBPR>::type;
+  constexpr int TM = C::TM, TN = C::TN, P = C::P, U = C::U;
   constexpr int CMAX = C::CA > C::CW ? C::CA : C::CW;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::STAGE];
 
@@ -129,25 +151,25 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
     rsw = __builtin_amdgcn_make_buffer_rsrc((void*)(Ws + (size_t)n0 * ksb), 0, (int)(w_rows * ksb), 0x00020000);
   }
 
-  // This thread's chunks: rows tid/4 + 64 i, logical chunk tid % 4.
-  const int crow = tid >> 2, cchk = tid & 3;
+  // This thread's chunks: rows tid / CPR + RPL i, logical chunk tid % CPR.
+  const int crow = tid / C::CPR, cchk = tid % C::CPR;
   uint32_t g_off[CMAX], l_off[CMAX];
 #pragma unroll
   for (int i = 0; i < CMAX; ++i) {
-    const int r = crow + 64 * i;
+    const int r = crow + C::RPL * i;
     g_off[i] = (uint32_t)r * ld + 16u * (uint32_t)cchk;
-    l_off[i] = (uint32_t)r * kRowBytes + 16u * (uint32_t)(cchk ^ swz(r));
+    l_off[i] = (uint32_t)r * RB + 16u * (uint32_t)(cchk ^ swz<RB>(r));
   }
 
-  StageRegs<FMT, BM, BN> R[P];
+  StageRegs<FMT, BM, BN, RB> R[P];
 
   // Loads of stages past the end use an offset beyond every buffer range:
   // the hardware returns zeros without a memory access, so the prefetch
   // needs no branch (a branch around it would make the compiler's load
   // counter wait for everything at the join).
   constexpr uint32_t kPastEnd = 0x80000000u;
-  auto load = [&](StageRegs<FMT, BM, BN>& r, int s) {
-    const uint32_t kb = s < nk ? (uint32_t)s * kRowBytes : kPastEnd;
+  auto load = [&](StageRegs<FMT, BM, BN, RB>& r, int s) {
+    const uint32_t kb = s < nk ? (uint32_t)s * RB : kPastEnd;
 #pragma unroll
     for (int i = 0; i < C::CA; ++i)
       r.a[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, g_off[i] + kb, 0, 0));
@@ -155,23 +177,29 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
     for (int i = 0; i < C::CW; ++i)
       r.w[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rw, g_off[i] + kb, 0, 0));
     if constexpr (T::kScaled) {
-      // Scale rows 0..BM-1 of A then 0..BN-1 of W, one dword per thread and
+      // Scale rows 0..BM-1 of A then 0..BN-1 of W, SBPR bytes per row and
       // load; the A / W choice is per load (256 x 256) or per wave
       // (128 x 128), so the buffer resource stays scalar.
-      const uint32_t sk = s >= nk ? kPastEnd : (FMT == 1 ? (uint32_t)s * 4u : (uint32_t)(s >> 1) * 4u);
+      const uint32_t sk = s >= nk ? kPastEnd : (uint32_t)s * C::SBPR;
+      auto ld_s = [&](__amdgpu_buffer_rsrc_t rs, uint32_t row) -> SW_t {
+        if constexpr (C::SBPR == 8)
+          return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, row * ksb + sk, 0, 0));
+        else
+          return __builtin_amdgcn_raw_buffer_load_b32(rs, row * ksb + sk, 0, 0);
+      };
       if constexpr (C::NS == 2) {
-        r.s[0] = __builtin_amdgcn_raw_buffer_load_b32(rsa, (uint32_t)tid * ksb + sk, 0, 0);
-        r.s[1] = __builtin_amdgcn_raw_buffer_load_b32(rsw, (uint32_t)tid * ksb + sk, 0, 0);
+        r.s[0] = ld_s(rsa, (uint32_t)tid);
+        r.s[1] = ld_s(rsw, (uint32_t)tid);
       } else {
         static_assert(C::NS == 1 && BM == 128 && BN == 128, "scale load split");
         if (wave < 2)
-          r.s[0] = __builtin_amdgcn_raw_buffer_load_b32(rsa, (uint32_t)tid * ksb + sk, 0, 0);
+          r.s[0] = ld_s(rsa, (uint32_t)tid);
         else
-          r.s[0] = __builtin_amdgcn_raw_buffer_load_b32(rsw, (uint32_t)(tid - 128) * ksb + sk, 0, 0);
+          r.s[0] = ld_s(rsw, (uint32_t)(tid - 128));
       }
     }
   };
-  auto store = [&](const StageRegs<FMT, BM, BN>& r, uint8_t* st) {
+  auto store = [&](const StageRegs<FMT, BM, BN, RB>& r, uint8_t* st) {
 #pragma unroll
     for (int i = 0; i < C::CA; ++i) *reinterpret_cast<v4i*>(st + l_off[i]) = r.a[i];
 #pragma unroll
@@ -179,7 +207,7 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
     if constexpr (T::kScaled) {
 #pragma unroll
       for (int j = 0; j < C::NS; ++j)
-        *reinterpret_cast<uint32_t*>(st + C::SA + C::SW + 4 * (tid + 256 * j)) = r.s[j];
+        *reinterpret_cast<SW_t*>(st + C::SA + C::SW + C::SBPR * (tid + 256 * j)) = r.s[j];
     }
   };
 
@@ -191,72 +219,87 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // All of a stage's LDS reads are issued before its first MFMA, and each
-  // row's scales come as one dword (the four bytes of the row's stage; the
-  // lane's byte is extracted per slice), so no MFMA waits on a read issued
-  // just before it.
-  auto compute = [&](int s, const uint8_t* st) {
+  // A stage in slices of 64 K (16 K for BF16): each slice's fragments are
+  // read from LDS, then its MFMAs issue (the compiler interleaves the next
+  // slice's reads with them).  Each row's scales for the stage come as one
+  // dword (two for 128-byte MXFP4 stages); the lane's byte is extracted per
+  // slice.
+  auto compute = [&](const uint8_t* st) {
     constexpr int KK = T::kKK;
+    constexpr int NQ = FMT == 2 ? 2 : 1;  // 16-byte chunks per lane per fragment
     const uint8_t* sc = st + C::SA + C::SW;
-    v4i fa[KK][TM][FMT == 2 ? 2 : 1], fb[KK][TN][FMT == 2 ? 2 : 1];
-    uint32_t sa[TM], sb[TN];
+    SW_t sa[TM], sb[TN];
+    int za[TM], zb[TN];
+    if constexpr (T::kScaled) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int r = wm * (BM / 2) + i * 32 + lrow;
-      const uint8_t* row = st + r * kRowBytes;
-      const int z = swz(r);
+      for (int i = 0; i < TM; ++i)
+        sa[i] = *reinterpret_cast<const SW_t*>(sc + (wm * (BM / 2) + i * 32 + lrow) * C::SBPR);
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        if constexpr (FMT == 2) {
-          fa[kk][i][0] = *reinterpret_cast<const v4i*>(row + 16 * (half ^ z));
-          fa[kk][i][1] = *reinterpret_cast<const v4i*>(row + 16 * ((2 + half) ^ z));
-        } else {
-          fa[kk][i][0] = *reinterpret_cast<const v4i*>(row + 16 * ((kk * 2 + half) ^ z));
-        }
-      }
-      if constexpr (T::kScaled) sa[i] = *reinterpret_cast<const uint32_t*>(sc + r * 4);
+      for (int j = 0; j < TN; ++j)
+        sb[j] = *reinterpret_cast<const SW_t*>(sc + (BM + wn * (BN / 2) + j * 32 + lrow) * C::SBPR);
     }
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int r = wn * (BN / 2) + j * 32 + lrow;
-      const uint8_t* row = st + C::SA + r * kRowBytes;
-      const int z = swz(r);
+    for (int i = 0; i < TM; ++i) za[i] = swz<RB>(wm * (BM / 2) + i * 32 + lrow);
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        if constexpr (FMT == 2) {
-          fb[kk][j][0] = *reinterpret_cast<const v4i*>(row + 16 * (half ^ z));
-          fb[kk][j][1] = *reinterpret_cast<const v4i*>(row + 16 * ((2 + half) ^ z));
-        } else {
-          fb[kk][j][0] = *reinterpret_cast<const v4i*>(row + 16 * ((kk * 2 + half) ^ z));
-        }
-      }
-      if constexpr (T::kScaled) sb[j] = *reinterpret_cast<const uint32_t*>(sc + 4 * BM + r * 4);
-    }
+    for (int j = 0; j < TN; ++j) zb[j] = swz<RB>(wn * (BN / 2) + j * 32 + lrow);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      // byte of the scale dword: MXFP4 slice kk, lane half; MXFP8 this
-      // stage's pair of blocks (low or high half of the dword), lane half
-      const uint32_t sh = FMT == 1 ? 16u * kk + 8u * half : 16u * (uint32_t)(s & 1) + 8u * half;
+      v4i fa[TM][NQ], fb[TN][NQ];
+      // 16-byte chunk(s) of this slice for the lane's half
+      const int c0 = FMT == 2 ? kk * 4 + half : kk * 2 + half;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const uint8_t* row = st + (wm * (BM / 2) + i * 32 + lrow) * RB;
+        fa[i][0] = *reinterpret_cast<const v4i*>(row + 16 * (c0 ^ za[i]));
+        if constexpr (NQ == 2) fa[i][1] = *reinterpret_cast<const v4i*>(row + 16 * ((c0 + 2) ^ za[i]));
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const uint8_t* row = st + C::SA + (wn * (BN / 2) + j * 32 + lrow) * RB;
+        fb[j][0] = *reinterpret_cast<const v4i*>(row + 16 * (c0 ^ zb[j]));
+        if constexpr (NQ == 2) fb[j][1] = *reinterpret_cast<const v4i*>(row + 16 * ((c0 + 2) ^ zb[j]));
+      }
+      // scale byte 2 kk + half of the row's stage scales
+      const int sbyte = 2 * kk + half;
+      uint32_t esa[TM], esb[TN];
+      if constexpr (T::kScaled) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          uint32_t w32;
+          if constexpr (C::SBPR == 8)
+            w32 = (sbyte >> 2) ? sa[i].y : sa[i].x;
+          else
+            w32 = sa[i];
+          esa[i] = __builtin_amdgcn_ubfe(w32, 8 * (sbyte & 3), 8);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          uint32_t w32;
+          if constexpr (C::SBPR == 8)
+            w32 = (sbyte >> 2) ? sb[j].y : sb[j].x;
+          else
+            w32 = sb[j];
+          esb[j] = __builtin_amdgcn_ubfe(w32, 8 * (sbyte & 3), 8);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           if constexpr (FMT == 3) {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, fb[kk][j][0]),
-                                                                 __builtin_bit_cast(v8bf, fa[kk][i][0]), acc[i][j],
-                                                                 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, fb[j][0]),
+                                                                 __builtin_bit_cast(v8bf, fa[i][0]), acc[i][j], 0,
+                                                                 0, 0);
           } else {
-            const v4i* qa = fa[kk][i];
-            const v4i* qb = fb[kk][j];
-            const v8i a_op = FMT == 1 ? v8i{qa[0].x, qa[0].y, qa[0].z, qa[0].w, 0, 0, 0, 0}
-                                      : v8i{qa[0].x, qa[0].y, qa[0].z, qa[0].w,
-                                            qa[FMT == 2].x, qa[FMT == 2].y, qa[FMT == 2].z, qa[FMT == 2].w};
-            const v8i b_op = FMT == 1 ? v8i{qb[0].x, qb[0].y, qb[0].z, qb[0].w, 0, 0, 0, 0}
-                                      : v8i{qb[0].x, qb[0].y, qb[0].z, qb[0].w,
-                                            qb[FMT == 2].x, qb[FMT == 2].y, qb[FMT == 2].z, qb[FMT == 2].w};
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                b_op, a_op, acc[i][j], T::kCbsz, T::kCbsz, 0, (int)__builtin_amdgcn_ubfe(sb[j], sh, 8), 0,
-                (int)__builtin_amdgcn_ubfe(sa[i], sh, 8));
+            const v4i qa0 = fa[i][0], qa1 = fa[i][NQ - 1];
+            const v4i qb0 = fb[j][0], qb1 = fb[j][NQ - 1];
+            const v8i a_op = FMT == 1 ? v8i{qa0.x, qa0.y, qa0.z, qa0.w, 0, 0, 0, 0}
+                                      : v8i{qa0.x, qa0.y, qa0.z, qa0.w, qa1.x, qa1.y, qa1.z, qa1.w};
+            const v8i b_op = FMT == 1 ? v8i{qb0.x, qb0.y, qb0.z, qb0.w, 0, 0, 0, 0}
+                                      : v8i{qb0.x, qb0.y, qb0.z, qb0.w, qb1.x, qb1.y, qb1.z, qb1.w};
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b_op, a_op, acc[i][j], T::kCbsz,
+                                                                         T::kCbsz, 0, (int)esb[j], 0,
+                                                                         (int)esa[i]);
           }
         }
     }
@@ -265,8 +308,9 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
   uint8_t* const lds0 = smem;
   uint8_t* const lds1 = smem + C::STAGE;
 
-  // Step s (register slot J = s % P): write stage s+1 from its slot into the
-  // other LDS buffer, refill that slot with stage s+1+P, compute stage s.
+  // Step s (unrolled position J = s % U, register slot J % P): write stage
+  // s+1 from its slot into the other LDS buffer, refill that slot with stage
+  // s+1+P, compute stage s.
   auto step = [&](auto Jc, int s) {
     constexpr int J = decltype(Jc)::value;
     constexpr int Jn = (J + 1) % P;
@@ -277,7 +321,7 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
     // keep the refill ahead of the matrix work (the scheduler would sink it
     // below, shortening the prefetch distance by a step)
     __builtin_amdgcn_sched_barrier(0);
-    compute(s, cur);
+    compute(cur);
     lds_barrier();
   };
 
@@ -295,17 +339,17 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
   lds_barrier();
 
   int s = 0;
-  for (; s + P <= nk; s += P) {
+  for (; s + U <= nk; s += U) {
     step(std::integral_constant<int, 0>{}, s);
     step(std::integral_constant<int, 1>{}, s + 1);
-    if constexpr (P == 4) {
+    if constexpr (U == 4) {
       step(std::integral_constant<int, 2>{}, s + 2);
       step(std::integral_constant<int, 3>{}, s + 3);
     }
   }
   if (s < nk) step(std::integral_constant<int, 0>{}, s++);
-  if (s < nk) step(std::integral_constant<int, 1>{}, s++);
-  if constexpr (P == 4) {
+  if constexpr (U == 4) {
+    if (s < nk) step(std::integral_constant<int, 1>{}, s++);
     if (s < nk) step(std::integral_constant<int, 2>{}, s++);
   }
 
@@ -408,34 +452,52 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
   }
 }
 
-// The pipelined path applies when K is a whole number of stages and one
-// tile's operand rows fit a 32-bit buffer range.  MXFP8 also needs K % 128
-// == 0: its scale dword covers two stages, so the scale rows must be whole,
-// aligned dwords.
+// The pipelined path applies when K is a whole number of 64-byte stages
+// (128-byte ones for MXFP8, whose scale rows must be whole dwords) and one
+// tile's operand rows fit a 32-bit buffer range.  128-byte stages are used
+// when K allows.
+static int pipe_row_bytes(int fmt, int64_t K) {
+  const int64_t e128 = fmt == 1 ? 256 : (fmt == 2 ? 128 : 64);
+  const int64_t e64 = fmt == 1 ? 128 : (fmt == 2 ? 0 : 32);
+  if (K % e128 == 0) return 128;
+  if (e64 && K % e64 == 0) return 64;
+  return 0;
+}
+
 bool gemm_pipe_supported(int fmt, int64_t M, int64_t N, int64_t K) {
-  const int step = fmt == 1 ? 128 : (fmt == 2 ? 128 : 32);
-  if (K % step || K < step) return false;
+  if (K <= 0 || pipe_row_bytes(fmt, K) == 0) return false;
   const int64_t ld = fmt == 1 ? K / 2 : (fmt == 2 ? K : 2 * K);
   return 256 * ld < (int64_t)0x7FFFFFFF && M > 0 && N > 0;
 }
 
-template <int FMT, int EPI, int BM, int BN>
+template <int FMT, int EPI, int BM, int BN, int RB>
 static hipError_t launch_pipe_t(const void* a, const uint8_t* as, const void* w, const uint8_t* ws, int64_t M,
                                 int64_t N, int64_t K, void* y, hipStream_t stream) {
   const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
-  gemm_pipe_kernel<FMT, EPI, BM, BN><<<tm * tn, 256, 0, stream>>>(static_cast<const uint8_t*>(a), as,
-                                                                    static_cast<const uint8_t*>(w), ws, (int)M,
-                                                                    (int)N, (int)K, y, tm, tn);
+  gemm_pipe_kernel<FMT, EPI, BM, BN, RB><<<tm * tn, 256, 0, stream>>>(static_cast<const uint8_t*>(a), as,
+                                                                        static_cast<const uint8_t*>(w), ws, (int)M,
+                                                                        (int)N, (int)K, y, tm, tn);
   return hipGetLastError();
+}
+
+template <int FMT, int EPI, int RB>
+static hipError_t launch_pipe_r(const void* a, const uint8_t* as, const void* w, const uint8_t* ws, int64_t M,
+                                int64_t N, int64_t K, void* y, hipStream_t stream) {
+  // 256 x 256 tiles when they fill the 256 CUs at least once, else 128 x 128
+  const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+  if (big >= 256) return launch_pipe_t<FMT, EPI, 256, 256, RB>(a, as, w, ws, M, N, K, y, stream);
+  return launch_pipe_t<FMT, EPI, 128, 128, RB>(a, as, w, ws, M, N, K, y, stream);
 }
 
 template <int FMT, int EPI>
 static hipError_t launch_pipe_e(const void* a, const uint8_t* as, const void* w, const uint8_t* ws, int64_t M,
                                 int64_t N, int64_t K, void* y, hipStream_t stream) {
-  // 256 x 256 tiles when they fill the 256 CUs at least once, else 128 x 128
-  const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
-  if (big >= 256) return launch_pipe_t<FMT, EPI, 256, 256>(a, as, w, ws, M, N, K, y, stream);
-  return launch_pipe_t<FMT, EPI, 128, 128>(a, as, w, ws, M, N, K, y, stream);
+  if constexpr (FMT == 2) {
+    return launch_pipe_r<FMT, EPI, 128>(a, as, w, ws, M, N, K, y, stream);
+  } else {
+    if (pipe_row_bytes(FMT, K) == 128) return launch_pipe_r<FMT, EPI, 128>(a, as, w, ws, M, N, K, y, stream);
+    return launch_pipe_r<FMT, EPI, 64>(a, as, w, ws, M, N, K, y, stream);
+  }
 }
 
 template <int FMT>
