@@ -1,12 +1,16 @@
 #!/usr/bin/env python3
 """One-GPU benchmark of the block-quantized matmul path on MI355X.
 
-Main line (the JSON `value`): the Qwen3-0.6B-shaped linear set of a
-4096-token prefill in MXFP8 weights and activations.  One step = for each of
-the seven linears, dynamic per-32 MXFP8 quantization of its BF16
-activations (rq_quantize) and the block-scaled GEMM against weights
-quantized once (rq_gemm, BF16 output).  value = GEMM FLOP per step (128.85
-GFLOP) / wall time per step, in TFLOP/s, inputs resident in HBM.
+Main line (the JSON `value`): the Qwen3-0.6B-shaped linear set of one layer
+for a 4096-token prefill, MXFP8 weights and activations.  q/k/v read the
+same hidden state and gate/up the same MLP input, as in the model, so a step
+is four groups -- qkv (1024 -> 2048 + 1024 + 1024), o (2048 -> 1024),
+gate_up (1024 -> 3072 + 3072), down (3072 -> 1024) -- each one dynamic
+per-32 MXFP8 quantization of the group's BF16 input (rq_quantize) and one
+block-scaled GEMM (rq_gemm, BF16 output) against the members' weights,
+quantized once and stacked along N.  value = GEMM FLOP per step (128.85
+GFLOP, all seven linears) / wall time per step, in TFLOP/s, inputs resident
+in HBM.
 
 `roofline` covers the dominant kernel (the MXFP8 GEMM): algorithmic FLOP
 (2 M N K per launch) over its average launch time from HIP events recorded
@@ -138,25 +142,23 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev)
 
     # ------------------------------------------------------ main workload --
-    log("generating the Qwen3-0.6B linear set at 4096 tokens (seeded)")
+    log("generating the Qwen3-0.6B linear set of one layer at 4096 tokens (seeded)")
     M = 4096
-    lin = []
-    for i in range(7):
-        d = W.c2_linear(i, M=M)
-        K, N = d["a"].shape[1], d["w"].shape[0]
-        a = to_dev(d["a"])
-        wq = api.quantize(to_dev(d["w"]), L.RQ_MXFP8)  # weights: quantized once
-        lin.append(dict(name=d["name"], K=K, N=N, a=a, wc=wq[0], ws=wq[1],
-                        ac=torch.empty((M, K), dtype=torch.uint8, device=dev),
-                        as_=torch.empty((M, K // 32), dtype=torch.uint8, device=dev),
-                        y=torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
-    flops_step = sum(2.0 * M * l["K"] * l["N"] for l in lin)
+    groups = []
+    for g in W.c2_layer(M=M):
+        K, N = g["a"].shape[1], g["w"].shape[0]
+        wq = api.quantize(to_dev(g["w"]), L.RQ_MXFP8)  # weights: quantized once (per row: stacking commutes)
+        groups.append(dict(name=g["name"], K=K, N=N, a=to_dev(g["a"]), wc=wq[0], ws=wq[1],
+                           ac=torch.empty((M, K), dtype=torch.uint8, device=dev),
+                           as_=torch.empty((M, K // 32), dtype=torch.uint8, device=dev),
+                           y=torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
+    flops_step = sum(2.0 * M * g["K"] * g["N"] for g in groups)
 
     def step(tm=None):
-        for l in lin:
-            L.rq_quantize(l["a"], M, l["K"], L.RQ_MXFP8, None, 0, L.RQ_APPEND_NONE, l["ac"], l["as_"])
+        for g in groups:
+            L.rq_quantize(g["a"], M, g["K"], L.RQ_MXFP8, None, 0, L.RQ_APPEND_NONE, g["ac"], g["as_"])
             s = tm.start() if tm else None
-            L.rq_gemm(L.RQ_MXFP8, l["ac"], l["as_"], l["wc"], l["ws"], M, l["N"], l["K"], L.RQ_OUT_BF16, l["y"])
+            L.rq_gemm(L.RQ_MXFP8, g["ac"], g["as_"], g["wc"], g["ws"], M, g["N"], g["K"], L.RQ_OUT_BF16, g["y"])
             if tm:
                 tm.stop(s)
 
@@ -170,8 +172,8 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    gemm_ms = tm.total_ms() / (args.steps * len(lin))  # average launch
-    achieved = flops_step / len(lin) / (gemm_ms * 1e-3)
+    gemm_ms = tm.total_ms() / (args.steps * len(groups))  # average launch
+    achieved = flops_step / len(groups) / (gemm_ms * 1e-3)
     log(f"main: {ms_step:.3f} ms/step, GEMM avg launch {gemm_ms * 1e3:.1f} us")
     value = flops_step / (ms_step * 1e-3) / 1e12
     traffic = measured_traffic()
@@ -189,16 +191,19 @@ def main():
         "vs_baseline": None,
         "dtype": "mxfp8",
         "data": "synthetic (seeded, shapes and distributions of the Qwen3-0.6B linear set)",
-        "config": {"workload": "qwen3-0.6b linear set (q,k,v,o,gate,up,down), 4096-token prefill, "
-                               "MXFP8 W/A, dynamic per-32 activation quantization + block-scaled GEMM",
-                   "tokens": M, "gemm_gflop_per_step": round(flops_step / 1e9, 2)},
-        "roofline": {"bound": "mfma", "kernel": "gemm_pipe_kernel<MXFP8, BF16 out, 128x128 tiles>",
+        "config": {"workload": "qwen3-0.6b linear set of one layer (q,k,v,o,gate,up,down), 4096-token prefill, "
+                               "MXFP8 W/A, dynamic per-32 activation quantization + block-scaled GEMM; "
+                               "q/k/v and gate/up share their inputs and run as one GEMM each",
+                   "tokens": M, "gemm_gflop_per_step": round(flops_step / 1e9, 2),
+                   "gemms_per_step": [f"{g['name']} {M}x{g['N']}x{g['K']}" for g in groups]},
+        "roofline": {"bound": "mfma", "kernel": "gemm_pipe_kernel<MXFP8, BF16 out> (256x256 tiles for qkv and "
+                               "gate_up, 128x128 for o and down)",
                      "achieved": round(achieved / 1e12, 2), "peak": PEAK["mxfp8"] / 1e12, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK["mxfp8"], 4), "traffic": traffic,
                      "avg_launch_us": round(gemm_ms * 1e3, 2)},
     }
-    for l in lin:
-        del l["ac"], l["as_"], l["y"], l["a"]
+    for g in groups:
+        del g["ac"], g["as_"], g["y"], g["a"]
     if not args.no_rows:
         line["rows"] = measure_rows(torch, np, api, L, W, to_dev, dev)
     if not args.no_cpu_baseline:
@@ -364,8 +369,9 @@ def measure_gemv(torch, np, api, L, W, dev):
 
 def cpu_baseline(np, W):
     """The CPU oracle (float64 NumPy) on a bounded sample of the main
-    workload: 256 activation rows of each of the seven linears, weights
-    dequantized outside the timed region; repeated for about 10 s."""
+    workload: 256 rows of each group's input, quantize + GEMM against the
+    group's stacked weights (dequantized outside the timed region),
+    repeated for about 10 s."""
     import threadpoolctl
     from oracle import formats as F
     from oracle import quant as Q
@@ -373,10 +379,8 @@ def cpu_baseline(np, W):
 
     rows = 256
     work = []
-    for i in range(7):
-        d = W.c2_linear(i, M=rows)
-        wd = Q.quantize_dequantize(d["w"], F.FMT_MXFP8)
-        work.append((d["a"], wd))
+    for g in W.c2_layer(M=rows):
+        work.append((g["a"], Q.quantize_dequantize(g["w"], F.FMT_MXFP8)))
     flop = sum(2.0 * rows * a.shape[1] * wd.shape[0] for a, wd in work)
     info = threadpoolctl.threadpool_info()
     cores = max([i.get("num_threads", 1) for i in info] or [1])
@@ -391,8 +395,8 @@ def cpu_baseline(np, W):
             break
     dt = (time.perf_counter() - t0) / n
     return {"value": round(flop / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{rows} of 4096 rows of each of the 7 linears (quantize + float64 GEMM + BF16 rounding), "
-                      f"{n} repetitions, {dt:.3f} s each"}
+            "sample": f"{rows} of 4096 rows of each of the 4 layer inputs (quantize + float64 GEMM against the "
+                      f"stacked weights + BF16 rounding), {n} repetitions, {dt:.3f} s each"}
 
 
 if __name__ == "__main__":

@@ -78,6 +78,24 @@ def c2_linear(i, M=4096):
     return dict(name=name, a=to_bf16_bits(a), w=to_bf16_bits(w), outliers=ch)
 
 
+# Inputs of one transformer layer: q/k/v read the same (normed) hidden
+# state and gate/up the same MLP input, so a layer has four activation
+# tensors.  Each group's input is the first member's c2_linear activation;
+# its weights are the members' matrices stacked along N.
+QWEN3_GROUPS = (("qkv", (0, 1, 2)), ("o", (3,)), ("gate_up", (4, 5)), ("down", (6,)))
+
+
+def c2_layer(M=4096):
+    """The linear set of one layer as four GEMMs on shared inputs: list of
+    dict(name, members, a [M x K] BF16 bits, w [sum N x K] BF16 bits, Ns)."""
+    out = []
+    for gname, members in QWEN3_GROUPS:
+        ds = [c2_linear(i, M=M) for i in members]
+        out.append(dict(name=gname, members=[d["name"] for d in ds], a=ds[0]["a"],
+                        w=np.concatenate([d["w"] for d in ds], axis=0), Ns=[d["w"].shape[0] for d in ds]))
+    return out
+
+
 # ------------------------------------------------------------ config 3 --
 
 def c3_arc(M=4096, K=4096, N=4096, n_outliers=64):

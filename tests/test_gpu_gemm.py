@@ -176,6 +176,31 @@ def test_config2_linear_set_full_size_sampled():
         sampled_rows_check(L.RQ_MXFP8, F.FMT_MXFP8, d["a"], d["w"], rows, f"config-2 {d['name']}")
 
 
+@pytest.mark.parametrize("gi", [0, 2])
+def test_config2_stacked_group_equals_separate_linears(gi):
+    """q/k/v (gate/up) on their shared input as one GEMM against the stacked
+    weights (256 x 256 tiles) gives bit for bit the members' own GEMMs
+    (128 x 128 tiles): per-row block scales make stacking commute with
+    quantization, and every output's K order is the same in both tilings.
+    Sampled rows of the stacked output are also checked against the oracle."""
+    g = W.c2_layer()[gi]
+    M, K = g["a"].shape
+    ac, as_ = quantize_on_gpu(g["a"], L.RQ_MXFP8)
+    wc, ws = quantize_on_gpu(g["w"], L.RQ_MXFP8)
+    log(f"stacked {g['name']}: {M}x{g['w'].shape[0]}x{K}")
+    y = host_bits(api.gemm(L.RQ_MXFP8, ac, as_, wc, ws, K, L.RQ_OUT_BF16))
+    n0 = 0
+    for name, n in zip(g["members"], g["Ns"]):
+        ym = host_bits(api.gemm(L.RQ_MXFP8, ac, as_, wc[n0:n0 + n], ws[n0:n0 + n], K, L.RQ_OUT_BF16))
+        assert np.array_equal(y[:, n0:n0 + n], ym), f"{name}: stacked != separate"
+        n0 += n
+    rows = np.sort(np.random.default_rng(gi).choice(M, 16, replace=False))
+    oa, osa = Q.quantize_mx(g["a"][rows], F.FMT_MXFP8)
+    ow, osw = Q.quantize_mx(g["w"], F.FMT_MXFP8)
+    da, dw = Q.dequantize_mx(oa, osa, F.FMT_MXFP8), Q.dequantize_mx(ow, osw, F.FMT_MXFP8)
+    check_bf16(y[rows], G.matmul_f64(da, dw), G.abs_bound(da, dw), g["name"], k=K, acc_rel=ACC_REL_MXFP8)
+
+
 def test_config3_plain_full_size_sampled():
     d = W.c3_arc()
     rows = np.sort(np.random.default_rng(3).choice(4096, 32, replace=False))
