@@ -18,9 +18,10 @@
 // * LDS rows are RB bytes of 16-byte chunks, XOR-swizzled per row so that
 //   the fragment reads of consecutive rows hit distinct banks (checked for
 //   both 32- and 64-bank LDS models).
-// * Four waves in a 2 x 2 arrangement, each owning a (BM/2) x (BN/2)
-//   quadrant of (BM/64) x (BN/64) MFMA tiles of 32 x 32; accumulators live
-//   in AGPRs.
+// * WMW x WNW waves, each owning a (BM/WMW) x (BN/WNW) quadrant of MFMA
+//   tiles of 32 x 32; accumulators live in AGPRs.  256 x 256 tiles use
+//   eight waves (two per SIMD, so one wave's waits and LDS writes overlap
+//   the other's MFMAs), 128 x 128 tiles four (two workgroups share a CU).
 // * Workgroups are ordered so that consecutive tiles land on the same XCD
 //   (the dispatcher deals workgroups round-robin over the 8 XCDs) and each
 //   XCD's tiles form a compact block of 4 M-tiles, sharing A and W panels in
@@ -75,21 +76,28 @@ __device__ __forceinline__ int swz(int r) {
 // Publish LDS writes and wait for every wave (no wait on global loads).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int FMT, int BM, int BN, int RB>
+template <int FMT, int BM, int BN, int RB, int WMW, int WNW>
 struct PipeCfg {
   using T = PipeTraits<FMT, RB>;
-  static constexpr int TM = BM / 64, TN = BN / 64;            // MFMA tiles per wave
-  static constexpr int CPR = RB / 16;                         // 16-byte chunks per row
-  static constexpr int RPL = 256 / CPR;                       // rows per wave-group load
-  static constexpr int CA = BM / RPL, CW = BN / RPL;          // 16-byte chunks per thread per stage
-  static constexpr int SA = BM * RB, SW = BN * RB;            // LDS bytes of the A / W tile
-  static constexpr int SBPR = T::kSBPR;                       // scale bytes per row per stage
-  static constexpr int SS = (BM + BN) * SBPR;                 // scale bytes per stage
+  static constexpr int NW = WMW * WNW, NT = 64 * NW;              // waves, threads
+  static constexpr int TM = BM / 32 / WMW, TN = BN / 32 / WNW;    // MFMA tiles per wave
+  static constexpr int WM = BM / WMW, WN = BN / WNW;              // wave quadrant
+  static constexpr int CPR = RB / 16;                             // 16-byte chunks per row
+  static constexpr int RPL = NT / CPR;                            // rows per workgroup-wide load
+  static constexpr int CA = BM / RPL, CW = BN / RPL;              // 16-byte chunks per thread per stage
+  static constexpr int SA = BM * RB, SW = BN * RB;                // LDS bytes of the A / W tile
+  static constexpr int SBPR = T::kSBPR;                           // scale bytes per row per stage
+  static constexpr int SS = (BM + BN) * SBPR;                     // scale bytes per stage
   static constexpr int STAGE = SA + SW + SS;
-  static constexpr int NS = T::kScaled ? (BM + BN) / 256 : 0;  // scale rows per thread
-  static constexpr int SLOT = 4 * (CA + CW);                  // VGPRs of one ring slot
-  static constexpr int P = SLOT >= 64 ? 1 : (SLOT >= 32 ? 2 : 4);  // register ring depth
-  static constexpr int U = P == 1 ? 2 : P;                    // steps per unrolled loop turn
+  static constexpr int NS = T::kScaled ? (BM + BN) / NT : 0;      // scale rows per thread
+  static constexpr int SLOT = 4 * (CA + CW);                      // VGPRs of one ring slot
+  // register ring depth: one slot when the slot is large or two waves share
+  // a SIMD (the compiler still renames it one stage ahead)
+  static constexpr int P = (SLOT >= 64 || NW > 4) ? 1 : (SLOT >= 32 ? 2 : 4);
+  static constexpr int U = P == 1 ? 2 : P;                        // steps per unrolled loop turn
+  static_assert(CA * RPL == BM && CW * RPL == BN, "whole chunk rows per thread");
+  static_assert(!T::kScaled || NS * NT == BM + BN, "whole scale rows per thread");
+  static_assert(BM % 64 == 0, "A / W scale rows split on a wave boundary");
 };
 
 template <int SBPR>
@@ -101,21 +109,22 @@ struct ScaleWord<8> {
   using type = uint2;
 };
 
-template <int FMT, int BM, int BN, int RB>
+template <int FMT, int BM, int BN, int RB, int WMW, int WNW>
 struct StageRegs {
-  using C = PipeCfg<FMT, BM, BN, RB>;
+  using C = PipeCfg<FMT, BM, BN, RB, WMW, WNW>;
   v4i a[C::CA];
   v4i w[C::CW];
   typename ScaleWord<C::SBPR>::type s[C::NS > 0 ? C::NS : 1];
 };
 
-template <int FMT, int EPI, int BM, int BN, int RB>
-__global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __restrict__ A,
-                                                           const uint8_t* __restrict__ As,
-                                                           const uint8_t* __restrict__ W,
-                                                           const uint8_t* __restrict__ Ws, int M, int N, int K,
-                                                           void* __restrict__ Y, int tiles_m, int tiles_n) {
-  using C = PipeCfg<FMT, BM, BN, RB>;
+template <int FMT, int EPI, int BM, int BN, int RB, int WMW, int WNW>
+__global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint8_t* __restrict__ A,
+                                                                      const uint8_t* __restrict__ As,
+                                                                      const uint8_t* __restrict__ W,
+                                                                      const uint8_t* __restrict__ Ws, int M, int N,
+                                                                      int K, void* __restrict__ Y, int tiles_m,
+                                                                      int tiles_n) {
+  using C = PipeCfg<FMT, BM, BN, RB, WMW, WNW>;
   using T = PipeTraits<FMT, RB>;
   using SW_t = typename ScaleWord<C::SBPR>::type;
   constexpr int TM = C::TM, TN = C::TN, P = C::P, U = C::U;
@@ -124,7 +133,7 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WNW, wn = wave % WNW;
   const int half = lane >> 5, lrow = lane & 31;
 
   // XCD-aware tile order
@@ -161,14 +170,14 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
     l_off[i] = (uint32_t)r * RB + 16u * (uint32_t)(cchk ^ swz<RB>(r));
   }
 
-  StageRegs<FMT, BM, BN, RB> R[P];
+  StageRegs<FMT, BM, BN, RB, WMW, WNW> R[P];
 
   // Loads of stages past the end use an offset beyond every buffer range:
   // the hardware returns zeros without a memory access, so the prefetch
   // needs no branch (a branch around it would make the compiler's load
   // counter wait for everything at the join).
   constexpr uint32_t kPastEnd = 0x80000000u;
-  auto load = [&](StageRegs<FMT, BM, BN, RB>& r, int s) {
+  auto load = [&](StageRegs<FMT, BM, BN, RB, WMW, WNW>& r, int s) {
     const uint32_t kb = s < nk ? (uint32_t)s * RB : kPastEnd;
 #pragma unroll
     for (int i = 0; i < C::CA; ++i)
@@ -178,8 +187,9 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
       r.w[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rw, g_off[i] + kb, 0, 0));
     if constexpr (T::kScaled) {
       // Scale rows 0..BM-1 of A then 0..BN-1 of W, SBPR bytes per row and
-      // load; the A / W choice is per load (256 x 256) or per wave
-      // (128 x 128), so the buffer resource stays scalar.
+      // load: thread t takes rows t + NT j; BM is a multiple of the wave
+      // size, so the A / W choice is wave-uniform and the buffer resource
+      // stays scalar.
       const uint32_t sk = s >= nk ? kPastEnd : (uint32_t)s * C::SBPR;
       auto ld_s = [&](__amdgpu_buffer_rsrc_t rs, uint32_t row) -> SW_t {
         if constexpr (C::SBPR == 8)
@@ -187,19 +197,17 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
         else
           return __builtin_amdgcn_raw_buffer_load_b32(rs, row * ksb + sk, 0, 0);
       };
-      if constexpr (C::NS == 2) {
-        r.s[0] = ld_s(rsa, (uint32_t)tid);
-        r.s[1] = ld_s(rsw, (uint32_t)tid);
-      } else {
-        static_assert(C::NS == 1 && BM == 128 && BN == 128, "scale load split");
-        if (wave < 2)
-          r.s[0] = ld_s(rsa, (uint32_t)tid);
+#pragma unroll
+      for (int j = 0; j < C::NS; ++j) {
+        const int rho = tid + C::NT * j;  // wave-uniform side
+        if (__builtin_amdgcn_readfirstlane(rho) < BM)
+          r.s[j] = ld_s(rsa, (uint32_t)rho);
         else
-          r.s[0] = ld_s(rsw, (uint32_t)(tid - 128));
+          r.s[j] = ld_s(rsw, (uint32_t)(rho - BM));
       }
     }
   };
-  auto store = [&](const StageRegs<FMT, BM, BN, RB>& r, uint8_t* st) {
+  auto store = [&](const StageRegs<FMT, BM, BN, RB, WMW, WNW>& r, uint8_t* st) {
 #pragma unroll
     for (int i = 0; i < C::CA; ++i) *reinterpret_cast<v4i*>(st + l_off[i]) = r.a[i];
 #pragma unroll
@@ -207,7 +215,7 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
     if constexpr (T::kScaled) {
 #pragma unroll
       for (int j = 0; j < C::NS; ++j)
-        *reinterpret_cast<SW_t*>(st + C::SA + C::SW + C::SBPR * (tid + 256 * j)) = r.s[j];
+        *reinterpret_cast<SW_t*>(st + C::SA + C::SW + C::SBPR * (tid + C::NT * j)) = r.s[j];
     }
   };
 
@@ -221,27 +229,19 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
 
   // A stage in slices of 64 K (16 K for BF16): each slice's fragments are
   // read from LDS, then its MFMAs issue (the compiler interleaves the next
-  // slice's reads with them).  Each row's scales for the stage come as one
-  // dword (two for 128-byte MXFP4 stages); the lane's byte is extracted per
-  // slice.
+  // slice's reads with them).  Each row's scales come as one dword per two
+  // slices; the lane's byte is extracted per slice.
   auto compute = [&](const uint8_t* st) {
     constexpr int KK = T::kKK;
     constexpr int NQ = FMT == 2 ? 2 : 1;  // 16-byte chunks per lane per fragment
     const uint8_t* sc = st + C::SA + C::SW;
-    SW_t sa[TM], sb[TN];
     int za[TM], zb[TN];
-    if constexpr (T::kScaled) {
+    // the row's scale dword holding slices kk of the current pair
+    uint32_t sa[TM], sb[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        sa[i] = *reinterpret_cast<const SW_t*>(sc + (wm * (BM / 2) + i * 32 + lrow) * C::SBPR);
+    for (int i = 0; i < TM; ++i) za[i] = swz<RB>(wm * C::WM + i * 32 + lrow);
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        sb[j] = *reinterpret_cast<const SW_t*>(sc + (BM + wn * (BN / 2) + j * 32 + lrow) * C::SBPR);
-    }
-#pragma unroll
-    for (int i = 0; i < TM; ++i) za[i] = swz<RB>(wm * (BM / 2) + i * 32 + lrow);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) zb[j] = swz<RB>(wn * (BN / 2) + j * 32 + lrow);
+    for (int j = 0; j < TN; ++j) zb[j] = swz<RB>(wn * C::WN + j * 32 + lrow);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       v4i fa[TM][NQ], fb[TN][NQ];
@@ -249,38 +249,33 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
       const int c0 = FMT == 2 ? kk * 4 + half : kk * 2 + half;
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const uint8_t* row = st + (wm * (BM / 2) + i * 32 + lrow) * RB;
+        const uint8_t* row = st + (wm * C::WM + i * 32 + lrow) * RB;
         fa[i][0] = *reinterpret_cast<const v4i*>(row + 16 * (c0 ^ za[i]));
         if constexpr (NQ == 2) fa[i][1] = *reinterpret_cast<const v4i*>(row + 16 * ((c0 + 2) ^ za[i]));
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const uint8_t* row = st + C::SA + (wn * (BN / 2) + j * 32 + lrow) * RB;
+        const uint8_t* row = st + C::SA + (wn * C::WN + j * 32 + lrow) * RB;
         fb[j][0] = *reinterpret_cast<const v4i*>(row + 16 * (c0 ^ zb[j]));
         if constexpr (NQ == 2) fb[j][1] = *reinterpret_cast<const v4i*>(row + 16 * ((c0 + 2) ^ zb[j]));
       }
-      // scale byte 2 kk + half of the row's stage scales
+      // scale byte 2 kk + half of the row's stage scales: dword kk / 2
       const int sbyte = 2 * kk + half;
       uint32_t esa[TM], esb[TN];
       if constexpr (T::kScaled) {
+        if (kk % 2 == 0) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          uint32_t w32;
-          if constexpr (C::SBPR == 8)
-            w32 = (sbyte >> 2) ? sa[i].y : sa[i].x;
-          else
-            w32 = sa[i];
-          esa[i] = __builtin_amdgcn_ubfe(w32, 8 * (sbyte & 3), 8);
+          for (int i = 0; i < TM; ++i)
+            sa[i] = *reinterpret_cast<const uint32_t*>(sc + (wm * C::WM + i * 32 + lrow) * C::SBPR + 4 * (kk / 2));
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            sb[j] = *reinterpret_cast<const uint32_t*>(sc + (BM + wn * C::WN + j * 32 + lrow) * C::SBPR +
+                                                       4 * (kk / 2));
         }
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          uint32_t w32;
-          if constexpr (C::SBPR == 8)
-            w32 = (sbyte >> 2) ? sb[j].y : sb[j].x;
-          else
-            w32 = sb[j];
-          esb[j] = __builtin_amdgcn_ubfe(w32, 8 * (sbyte & 3), 8);
-        }
+        for (int i = 0; i < TM; ++i) esa[i] = __builtin_amdgcn_ubfe(sa[i], 8 * (sbyte & 3), 8);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) esb[j] = __builtin_amdgcn_ubfe(sb[j], 8 * (sbyte & 3), 8);
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -317,6 +312,9 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
     uint8_t* cur = (J % 2) ? lds1 : lds0;
     uint8_t* nxt = (J % 2) ? lds0 : lds1;
     store(R[Jn], nxt);  // past the last stage this writes zeros nobody reads
+    // two waves per SIMD leave no registers to refill a one-slot ring
+    // before it is written out
+    if constexpr (C::NW > 4) __builtin_amdgcn_sched_barrier(0);
     load(R[Jn], s + 1 + P);
     // keep the refill ahead of the matrix work (the scheduler would sink it
     // below, shortening the prefetch distance by a step)
@@ -360,7 +358,7 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
   // through a per-wave LDS strip of 32 rows (BF16: the quadrant's full
   // width; FP32: half of it per pass), so every global store is a 16-byte
   // chunk of a row.
-  constexpr int WN = BN / 2;                        // columns of a wave's quadrant
+  constexpr int WN = C::WN;                         // columns of a wave's quadrant
   constexpr int EB = EPI == kEpiStoreF32 ? 4 : 2;   // output element bytes
   constexpr int SC = WN * 2 / EB;                   // strip columns per pass
   constexpr int NP = WN / SC;                       // passes per strip
@@ -368,12 +366,12 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
   constexpr int RSTR = SC * EB + 16;                // strip row stride in bytes (16-byte aligned)
   constexpr int CPR = SC * EB / 16;                 // chunks per strip row
   constexpr int RPI = 64 / CPR;                     // strip rows per wave-wide read
-  static_assert(4 * 32 * RSTR <= 2 * C::STAGE, "epilogue strips fit in the stage buffers");
+  static_assert(C::NW * 32 * RSTR <= 2 * C::STAGE, "epilogue strips fit in the stage buffers");
   uint8_t* const strip = smem + wave * 32 * RSTR;
   const int n_wave = n0 + wn * WN;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int m_strip = m0 + wm * (BM / 2) + i * 32;
+    const int m_strip = m0 + wm * C::WM + i * 32;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
 #pragma unroll
@@ -470,13 +468,12 @@ bool gemm_pipe_supported(int fmt, int64_t M, int64_t N, int64_t K) {
   return 256 * ld < (int64_t)0x7FFFFFFF && M > 0 && N > 0;
 }
 
-template <int FMT, int EPI, int BM, int BN, int RB>
+template <int FMT, int EPI, int BM, int BN, int RB, int WMW, int WNW>
 static hipError_t launch_pipe_t(const void* a, const uint8_t* as, const void* w, const uint8_t* ws, int64_t M,
                                 int64_t N, int64_t K, void* y, hipStream_t stream) {
   const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
-  gemm_pipe_kernel<FMT, EPI, BM, BN, RB><<<tm * tn, 256, 0, stream>>>(static_cast<const uint8_t*>(a), as,
-                                                                        static_cast<const uint8_t*>(w), ws, (int)M,
-                                                                        (int)N, (int)K, y, tm, tn);
+  gemm_pipe_kernel<FMT, EPI, BM, BN, RB, WMW, WNW><<<tm * tn, 64 * WMW * WNW, 0, stream>>>(
+      static_cast<const uint8_t*>(a), as, static_cast<const uint8_t*>(w), ws, (int)M, (int)N, (int)K, y, tm, tn);
   return hipGetLastError();
 }
 
@@ -485,8 +482,8 @@ static hipError_t launch_pipe_r(const void* a, const uint8_t* as, const void* w,
                                 int64_t N, int64_t K, void* y, hipStream_t stream) {
   // 256 x 256 tiles when they fill the 256 CUs at least once, else 128 x 128
   const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
-  if (big >= 256) return launch_pipe_t<FMT, EPI, 256, 256, RB>(a, as, w, ws, M, N, K, y, stream);
-  return launch_pipe_t<FMT, EPI, 128, 128, RB>(a, as, w, ws, M, N, K, y, stream);
+  if (big >= 256) return launch_pipe_t<FMT, EPI, 256, 256, RB, 2, 4>(a, as, w, ws, M, N, K, y, stream);
+  return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 2>(a, as, w, ws, M, N, K, y, stream);
 }
 
 template <int FMT, int EPI>
