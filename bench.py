@@ -262,37 +262,95 @@ def measure_rows(torch, np, api, L, W, to_dev, dev):
     del a, w, pc, ps, qc, qs, y, w_aug, wsp
 
     # ---- recurrent prefill, 4096 x 2048, FFN 5632, 8 steps
-    d = W.c4_ramp()
-    h0 = to_dev(d["h0"])
-    w1, w2 = to_dev(d["w1"]), to_dev(d["w2"])
-    w1q, w2q = api.quantize(w1, L.RQ_MXFP4), api.quantize(w2, L.RQ_MXFP4)
-    S, D, F = 4096, 2048, 5632
-    wsb = L.rq_recurrent_prefill_workspace_bytes(S, D, F, L.RQ_MXFP4)
-    wsp = torch.empty(wsb, dtype=torch.uint8, device=dev)
-    h = torch.empty_like(h0)
-    res = {}
-    outs = {}
-    for name, sched in (("all_bf16", 0x00), ("ramp_steps1_6_mxfp4", 0x3F), ("uniform_mxfp4", 0xFF)):
-        def run(sched=sched):
-            L.rq_recurrent_prefill(h, S, D, F, w1, w2, w1q[0], w1q[1], w2q[0], w2q[1], L.RQ_MXFP4, sched, 8, 1e-6,
-                                   wsp, wsb)
-        ms = time_calls(torch, run, 5, warmup=1, before=lambda: h.copy_(h0))
-        h.copy_(h0)
-        run()
-        outs[name] = h.clone()
-        res[name] = {"ms": round(ms, 3)}
-    ref = outs["all_bf16"].view(torch.bfloat16).float()
-    for name in res:
-        x = outs[name].view(torch.bfloat16).float()
-        res[name]["final_state_rel_err_vs_all_bf16"] = float((x - ref).norm() / ref.norm())
-    res["ramp_speedup_vs_all_bf16"] = round(res["all_bf16"]["ms"] / res["ramp_steps1_6_mxfp4"]["ms"], 4)
-    rows["recurrent_prefill_4096x2048_ffn5632_r8"] = res
-    log(f"rows: RAMP {res}")
-    del h0, w1, w2, w1q, w2q, wsp, h, outs, ref
+    rows.update(measure_ramp(torch, api, L, W, to_dev, dev, time_calls))
 
     # ---- nibble GEMV: weights drawn on the GPU with the same recipe
     rows.update(measure_gemv(torch, np, api, L, W, dev))
     return rows
+
+
+def measure_ramp(torch, api, L, W, to_dev, dev, time_calls):
+    """Recurrent prefill rows: the four 8-step schedules (bit t-1 set = step
+    t quantized) on the random-weight block and on the tied, contractive
+    block; the block's per-step perturbation gain; the 32-step schedule with
+    steps 1-24 in MXFP8."""
+    S, D, F = 4096, 2048, 5632
+    out = {}
+    schedules = (("all_bf16", 0x00), ("ramp_steps1_6_mxfp4", 0x3F), ("uniform_mxfp4", 0xFF),
+                 ("early_bf16_steps1_2", 0xFC))
+
+    def run_block(d, tag, timed):
+        h0 = to_dev(d["h0"])
+        w1, w2 = to_dev(d["w1"]), to_dev(d["w2"])
+        w1q, w2q = api.quantize(w1, L.RQ_MXFP4), api.quantize(w2, L.RQ_MXFP4)
+        wsb = L.rq_recurrent_prefill_workspace_bytes(S, D, F, L.RQ_MXFP4)
+        wsp = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        h = torch.empty_like(h0)
+        res, outs = {}, {}
+
+        def run(sched, steps=8, src=h0):
+            h.copy_(src)
+            L.rq_recurrent_prefill(h, S, D, F, w1, w2, w1q[0], w1q[1], w2q[0], w2q[1], L.RQ_MXFP4, sched, steps,
+                                   1e-6, wsp, wsb)
+
+        for name, sched in schedules:
+            if timed:
+                ms = time_calls(torch, lambda: L.rq_recurrent_prefill(h, S, D, F, w1, w2, w1q[0], w1q[1], w2q[0],
+                                                                      w2q[1], L.RQ_MXFP4, sched, 8, 1e-6, wsp, wsb),
+                                5, warmup=1, before=lambda: h.copy_(h0))
+                res[name] = {"ms": round(ms, 3)}
+            else:
+                res[name] = {}
+            run(sched)
+            outs[name] = h.clone()
+        ref = outs["all_bf16"].view(torch.bfloat16).float()
+        for name in res:
+            x = outs[name].view(torch.bfloat16).float()
+            res[name]["final_state_rel_err_vs_all_bf16"] = float((x - ref).norm() / ref.norm())
+        # per-step perturbation gain of one BF16 step: ||f(h + d) - f(h)|| / ||d||
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(20261204)
+        hp = (h0.view(torch.bfloat16).float() + 1e-2 * torch.randn(h0.shape, generator=gen, device=dev))
+        hp = hp.to(torch.bfloat16).view(torch.int16)
+        run(0x00, 1, h0)
+        f0 = h.view(torch.bfloat16).float().clone()
+        run(0x00, 1, hp)
+        f1 = h.view(torch.bfloat16).float()
+        dlt = hp.view(torch.bfloat16).float() - h0.view(torch.bfloat16).float()
+        res["per_step_perturbation_gain"] = round(float((f1 - f0).norm() / dlt.norm()), 4)
+        log(f"rows: RAMP {tag} {res}")
+        return res, (h0, w1, w2, wsp, wsb, h)
+
+    res, (h0, w1, w2, wsp, wsb, h) = run_block(W.c4_ramp(), "random W", True)
+    res["ramp_speedup_vs_all_bf16"] = round(res["all_bf16"]["ms"] / res["ramp_steps1_6_mxfp4"]["ms"], 4)
+    out["recurrent_prefill_4096x2048_ffn5632_r8"] = res
+
+    # 32 steps, 1-24 in MXFP8 (the long fixed-budget schedule), against 32 BF16 steps
+    w1q8, w2q8 = api.quantize(w1, L.RQ_MXFP8), api.quantize(w2, L.RQ_MXFP8)
+    wsb8 = L.rq_recurrent_prefill_workspace_bytes(S, D, F, L.RQ_MXFP8)
+    wsp8 = torch.empty(wsb8, dtype=torch.uint8, device=dev)
+    r32 = {}
+    finals = {}
+    for name, sched in (("all_bf16", 0), ("steps1_24_mxfp8", (1 << 24) - 1), ("uniform_mxfp8", (1 << 32) - 1)):
+        def run32(sched=sched):
+            L.rq_recurrent_prefill(h, S, D, F, w1, w2, w1q8[0], w1q8[1], w2q8[0], w2q8[1], L.RQ_MXFP8, sched, 32,
+                                   1e-6, wsp8, wsb8)
+        ms = time_calls(torch, run32, 3, warmup=1, before=lambda: h.copy_(h0))
+        h.copy_(h0)
+        run32()
+        finals[name] = h.view(torch.bfloat16).float().clone()
+        r32[name] = {"ms": round(ms, 3)}
+    for name in r32:
+        r32[name]["final_state_rel_err_vs_all_bf16"] = float((finals[name] - finals["all_bf16"]).norm()
+                                                             / finals["all_bf16"].norm())
+    r32["speedup_vs_all_bf16"] = round(r32["all_bf16"]["ms"] / r32["steps1_24_mxfp8"]["ms"], 4)
+    out["recurrent_prefill_4096x2048_ffn5632_t32_k24_mxfp8"] = r32
+    log(f"rows: RAMP T=32 K=24 MXFP8 {r32}")
+    del h0, w1, w2, wsp, h, w1q8, w2q8, wsp8, finals
+
+    tied, _ = run_block(W.c4_ramp(tied=True), "tied W2 = -W1^T", False)
+    out["recurrent_prefill_tied_contractive_r8"] = tied
+    return out
 
 
 def gpu_int8_weights(torch, gen, N, K, dev):
@@ -356,6 +414,24 @@ def measure_gemv(torch, np, api, L, W, dev):
     tot_esc = sum(esc_bytes(N, K, nf) for N, K, _ in planes)
     ms_low = time_calls(torch, lambda: sweep(L.RQ_LOW), 10)
     ms_esc = time_calls(torch, lambda: sweep(L.RQ_ESCALATE), 10)
+    # the same 197-launch sweeps captured once in a HIP graph and replayed
+    graphs = {}
+    for phase in (L.RQ_LOW, L.RQ_ESCALATE):
+        sweep(phase)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            sweep(phase)
+        graphs[phase] = g
+    ms_low_g = time_calls(torch, graphs[L.RQ_LOW].replay, 10)
+    ms_esc_g = time_calls(torch, graphs[L.RQ_ESCALATE].replay, 10)
+    out["gemv_full_sweep_197_linears_low_pass_b16_hip_graph"] = {
+        "us": round(ms_low_g * 1e3, 1), "gb_s": round(tot_low / (ms_low_g * 1e-3) / 1e9, 1),
+        "frac_hbm": round(tot_low / (ms_low_g * 1e-3) / PEAK["hbm"], 4), "bytes": tot_low}
+    out["gemv_full_sweep_escalation_2_of_16_hip_graph"] = {
+        "us": round(ms_esc_g * 1e3, 1), "gb_s": round(tot_esc / (ms_esc_g * 1e-3) / 1e9, 1),
+        "frac_hbm": round(tot_esc / (ms_esc_g * 1e-3) / PEAK["hbm"], 4), "bytes": tot_esc}
+    del graphs
     out["gemv_full_sweep_197_linears_low_pass_b16"] = {
         "us": round(ms_low * 1e3, 1), "gb_s": round(tot_low / (ms_low * 1e-3) / 1e9, 1),
         "frac_hbm": round(tot_low / (ms_low * 1e-3) / PEAK["hbm"], 4), "bytes": tot_low,
