@@ -138,3 +138,29 @@ def test_deterministic():
     a = run(d["x"], d["w"], d["scales"], d["flags"], L.RQ_BOTH, d["w"].shape[0])
     b = run(d["x"], d["w"], d["scales"], d["flags"], L.RQ_BOTH, d["w"].shape[0])
     assert np.array_equal(a, b)
+
+
+def test_split_workspace_reused_across_calls():
+    """One workspace serves consecutive split calls of different shapes and
+    phases; every output equals a fresh-workspace run and the oracle."""
+    wsb = max(L.rq_gemv_workspace_bytes(16, n, k) for n, k in ((1000, 1024), (130, 3072), (64, 256)))
+    ws = torch.full((wsb,), 0x7F, dtype=torch.uint8, device="cuda")  # stale contents must not matter
+    for rep in range(2):
+        for i, (n, k) in enumerate(((1000, 1024), (130, 3072), (64, 256))):
+            d = W.c5_linear(i + 2, B=16, N=n, K=k)
+            planes = gpu_planes(d["w"], d["scales"])
+            fl = dev(d["flags"])
+            x = dev_bf16(d["x"])
+            y = torch.empty((16, n), dtype=torch.int16, device="cuda")
+            hi, lo, st = planes
+            assert L.rq_gemv_workspace_bytes(16, n, k) > 0
+            L.rq_gemv_nibble_escalate(x, 16, k, n, hi, lo, st, fl, L.RQ_BOTH, ws, wsb, y)
+            fresh = host_bits(api.gemv_nibble_escalate(x, n, planes, fl, L.RQ_BOTH))
+            assert np.array_equal(host_bits(y), fresh), (rep, n, k)
+            ref = V.low_pass(d["x"], d["w"], d["scales"])
+            f = d["flags"] == 1
+            ref[f] = V.full_pass(d["x"][f], d["w"], d["scales"])
+            hi8, _ = V.split_nibbles(d["w"])
+            bound = V.abs_bound(d["x"], d["w"], d["scales"]) + V.abs_bound(d["x"], 16 * hi8.astype(np.int64),
+                                                                            d["scales"])
+            check_bf16(host_bits(y), ref, bound, f"reuse {n}x{k}", k=k)
