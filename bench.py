@@ -432,6 +432,20 @@ def measure_gemv(torch, np, api, L, W, dev):
         "us": round(ms_esc_g * 1e3, 1), "gb_s": round(tot_esc / (ms_esc_g * 1e-3) / 1e9, 1),
         "frac_hbm": round(tot_esc / (ms_esc_g * 1e-3) / PEAK["hbm"], 4), "bytes": tot_esc}
     del graphs
+    # the same sweeps as one grouped launch per phase (a problem table in
+    # device memory; no split-K: the 197 problems give 7302 row tiles)
+    gys = [torch.empty((B, N), dtype=torch.bfloat16, device=dev) for N, _, _ in planes]
+    table = api.gemv_group([(xs[K], p, y) for (N, K, p), y in zip(planes, gys)], dev)
+    ms_low_grp = time_calls(torch, lambda: api.gemv_nibble_escalate_grouped(table, B, None, L.RQ_LOW), 10)
+    ms_esc_grp = time_calls(torch, lambda: api.gemv_nibble_escalate_grouped(table, B, flags, L.RQ_ESCALATE), 10)
+    out["gemv_full_sweep_197_linears_low_pass_b16_grouped"] = {
+        "us": round(ms_low_grp * 1e3, 1), "gb_s": round(tot_low / (ms_low_grp * 1e-3) / 1e9, 1),
+        "frac_hbm": round(tot_low / (ms_low_grp * 1e-3) / PEAK["hbm"], 4), "bytes": tot_low,
+        "launches": 1, "tiles": table[2]}
+    out["gemv_full_sweep_escalation_2_of_16_grouped"] = {
+        "us": round(ms_esc_grp * 1e3, 1), "gb_s": round(tot_esc / (ms_esc_grp * 1e-3) / 1e9, 1),
+        "frac_hbm": round(tot_esc / (ms_esc_grp * 1e-3) / PEAK["hbm"], 4), "bytes": tot_esc}
+    del table, gys
     out["gemv_full_sweep_197_linears_low_pass_b16"] = {
         "us": round(ms_low * 1e3, 1), "gb_s": round(tot_low / (ms_low * 1e-3) / 1e9, 1),
         "frac_hbm": round(tot_low / (ms_low * 1e-3) / PEAK["hbm"], 4), "bytes": tot_low,

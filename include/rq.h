@@ -224,6 +224,46 @@ rq_status rq_gemv_nibble_escalate(const void *x_bf16, int64_t B, int64_t K,
                                   void *y_bf16, void *stream);
 
 /*
+ * Grouped decode GEMV: one launch over many independent problems (the same
+ * operation as rq_gemv_nibble_escalate on each, same B and flags), for
+ * decode steps whose linears are launch-latency bound one by one.
+ *
+ * rq_gemv_problem: one problem; pointers as for rq_gemv_nibble_escalate
+ * (every x holds the same B tokens; w_lo may be NULL, and such a problem
+ * then takes only the low pass: the escalation skips it).  tile_start is
+ * filled by rq_gemv_group_plan.
+ *
+ * rq_gemv_group_plan (host): validates every entry (non-NULL x, w_hi,
+ * scales_tiled and y; N > 0; K > 0 with K % 32 == 0; 16-byte aligned x and
+ * planes), sets tile_start to the running sum of ceil(N / 64), and returns
+ * the total number of 64-row tiles, or -1 (with rq_last_error) if an entry
+ * is invalid or count < 1.
+ *
+ * rq_gemv_nibble_escalate_grouped: problems_dev is the planned array
+ * copied unchanged to device memory (count entries, 16-byte aligned,
+ * caller-owned); total_tiles is the plan's return value (workgroups past
+ * the last problem's tiles do nothing).  B in [1, 16]; flags as for
+ * rq_gemv_nibble_escalate, shared by all problems.  The device table is
+ * not validated again: it must be the plan's output.  Outputs are
+ * bit-identical to unsplit rq_gemv_nibble_escalate calls on each problem.
+ */
+typedef struct rq_gemv_problem {
+  const void *x_bf16;           /* [B x K] BF16 */
+  const uint8_t *w_hi;          /* hi plane */
+  const uint8_t *w_lo;          /* lo plane, or NULL for RQ_LOW only */
+  const uint16_t *scales_tiled; /* tiled FP16 scales */
+  void *y_bf16;                 /* [B x N] BF16 */
+  int64_t N, K;
+  int64_t tile_start;           /* set by rq_gemv_group_plan */
+} rq_gemv_problem;
+
+int64_t rq_gemv_group_plan(rq_gemv_problem *problems, int count);
+rq_status rq_gemv_nibble_escalate_grouped(const rq_gemv_problem *problems_dev,
+                                          int count, int64_t total_tiles,
+                                          int64_t B, const uint8_t *flags,
+                                          int phase, void *stream);
+
+/*
  * rq_escalation_gate -- entropy / margin gate over low-pass logits (same
  * article, setup paragraph: recompute when the output distribution's
  * entropy is above a threshold or the top-1/top-2 probability gap is

@@ -29,6 +29,13 @@ class RQError(RuntimeError):
         self.name = name
 
 
+class RqGemvProblem(ctypes.Structure):
+    """rq_gemv_problem: one problem of a grouped GEMV launch (include/rq.h)."""
+    _fields_ = [("x_bf16", ctypes.c_void_p), ("w_hi", ctypes.c_void_p), ("w_lo", ctypes.c_void_p),
+                ("scales_tiled", ctypes.c_void_p), ("y_bf16", ctypes.c_void_p), ("N", ctypes.c_int64),
+                ("K", ctypes.c_int64), ("tile_start", ctypes.c_int64)]
+
+
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _INT = ctypes.c_int
@@ -55,6 +62,8 @@ _SIGNATURES = {
     "rq_pack_nibble_planes": (_INT, [_P, _P, _I64, _I64, _P, _P, _P, _P]),
     "rq_gemv_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "rq_gemv_nibble_escalate": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _INT, _P, _SZ, _P, _P]),
+    "rq_gemv_group_plan": (_I64, [ctypes.POINTER(RqGemvProblem), _INT]),
+    "rq_gemv_nibble_escalate_grouped": (_INT, [_P, _INT, _I64, _I64, _P, _INT, _P]),
     "rq_escalation_gate": (_INT, [_P, _I64, _I64, _F, _F, _P, _P, _P]),
     "rq_kv_quantize": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P]),
 }
@@ -167,6 +176,21 @@ def rq_gemv_nibble_escalate(x, B, K, N, w_hi, w_lo, scales_tiled, flags, phase, 
     _check("rq_gemv_nibble_escalate",
            lib().rq_gemv_nibble_escalate(_ptr(x), B, K, N, _ptr(w_hi), _ptr(w_lo), _ptr(scales_tiled), _ptr(flags),
                                          phase, _ptr(workspace), ws_bytes, _ptr(y), _stream(stream)))
+
+
+def rq_gemv_group_plan(problems):
+    """problems: a ctypes array of RqGemvProblem (filled in place); returns
+    the total tile count or raises."""
+    total = lib().rq_gemv_group_plan(problems, len(problems))
+    if total < 0:
+        raise RQError(RQ_EINVAL, "rq_gemv_group_plan", lib().rq_last_error().decode())
+    return total
+
+
+def rq_gemv_nibble_escalate_grouped(problems_dev, count, total_tiles, B, flags, phase, stream=None):
+    _check("rq_gemv_nibble_escalate_grouped",
+           lib().rq_gemv_nibble_escalate_grouped(_ptr(problems_dev), count, total_tiles, B, _ptr(flags), phase,
+                                                 _stream(stream)))
 
 
 def rq_escalation_gate(logits, B, V, tau, delta, flags, stats, stream=None):

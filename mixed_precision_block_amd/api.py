@@ -102,6 +102,25 @@ def gemv_nibble_escalate(x, N, planes, flags=None, phase=L.RQ_BOTH, y=None, stre
     return y
 
 
+def gemv_group(problems, device="cuda"):
+    """Plan a grouped GEMV: problems is a list of (x, planes, y) with x [B x K]
+    BF16, planes from pack_nibble_planes, y [B x N].  Returns (table on the
+    device, count, total tiles) for gemv_nibble_escalate_grouped; the table
+    refers to the tensors, which must outlive it."""
+    arr = (L.RqGemvProblem * len(problems))()
+    for i, (x, (hi, lo, st), y) in enumerate(problems):
+        arr[i] = L.RqGemvProblem(x.data_ptr(), hi.data_ptr(), lo.data_ptr() if lo is not None else None,
+                                 st.data_ptr(), y.data_ptr(), y.shape[1], x.shape[1], 0)
+    total = L.rq_gemv_group_plan(arr)
+    host = torch.frombuffer(bytearray(bytes(arr)), dtype=torch.uint8)
+    return host.to(device), len(problems), total
+
+
+def gemv_nibble_escalate_grouped(table, B, flags=None, phase=L.RQ_BOTH, stream=None):
+    dev_table, count, total = table
+    L.rq_gemv_nibble_escalate_grouped(dev_table, count, total, B, flags, phase, stream)
+
+
 def escalation_gate(logits, tau, delta, stream=None):
     B, V = logits.shape
     flags = _u8((B,), logits.device)

@@ -91,10 +91,11 @@ struct PipeCfg {
   static constexpr int STAGE = SA + SW + SS;
   static constexpr int NS = T::kScaled ? (BM + BN) / NT : 0;      // scale rows per thread
   static constexpr int SLOT = 4 * (CA + CW);                      // VGPRs of one ring slot
-  // register ring depth: one slot when the slot is large or two waves share
-  // a SIMD (the compiler still renames it one stage ahead)
-  static constexpr int P = (SLOT >= 64 || NW > 4) ? 1 : (SLOT >= 32 ? 2 : 4);
-  static constexpr int U = P == 1 ? 2 : P;                        // steps per unrolled loop turn
+  // register ring depth: with two waves per SIMD three 16-VGPR slots or
+  // one larger slot; otherwise one slot when it is large (the compiler
+  // still renames it one stage ahead), two or four when small
+  static constexpr int P = NW > 4 ? (SLOT <= 16 ? 3 : 1) : (SLOT >= 64 ? 1 : (SLOT >= 32 ? 2 : 4));
+  static constexpr int U = P % 2 ? 2 * P : P;                     // steps per unrolled loop turn
   static_assert(CA * RPL == BM && CW * RPL == BN, "whole chunk rows per thread");
   static_assert(!T::kScaled || NS * NT == BM + BN, "whole scale rows per thread");
   static_assert(BM % 64 == 0, "A / W scale rows split on a wave boundary");
@@ -340,15 +341,24 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
   for (; s + U <= nk; s += U) {
     step(std::integral_constant<int, 0>{}, s);
     step(std::integral_constant<int, 1>{}, s + 1);
-    if constexpr (U == 4) {
-      step(std::integral_constant<int, 2>{}, s + 2);
-      step(std::integral_constant<int, 3>{}, s + 3);
-    }
+    if constexpr (U > 2) step(std::integral_constant<int, 2>{}, s + 2);
+    if constexpr (U > 3) step(std::integral_constant<int, 3>{}, s + 3);
+    if constexpr (U > 4) step(std::integral_constant<int, 4>{}, s + 4);
+    if constexpr (U > 5) step(std::integral_constant<int, 5>{}, s + 5);
   }
+  // the last nk % U steps keep their unrolled positions (slot and buffer)
   if (s < nk) step(std::integral_constant<int, 0>{}, s++);
-  if constexpr (U == 4) {
+  if constexpr (U > 2) {
     if (s < nk) step(std::integral_constant<int, 1>{}, s++);
+  }
+  if constexpr (U > 3) {
     if (s < nk) step(std::integral_constant<int, 2>{}, s++);
+  }
+  if constexpr (U > 4) {
+    if (s < nk) step(std::integral_constant<int, 3>{}, s++);
+  }
+  if constexpr (U > 5) {
+    if (s < nk) step(std::integral_constant<int, 4>{}, s++);
   }
 
   // Epilogue.  The W tile is the MFMA's first operand, so the accumulator

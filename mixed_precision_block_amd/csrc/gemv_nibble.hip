@@ -21,6 +21,7 @@
 // address being wave-uniform).  FP32 block partials are scaled by
 // the block's FP16 scale and accumulated; the four waves' sums are added in
 // a fixed order through LDS.
+#include "../../include/rq.h"
 #include "rq_device.h"
 #include "rq_internal.h"
 
@@ -95,10 +96,9 @@ __device__ __forceinline__ void gemv_tile(const uint16_t* __restrict__ x, int B,
                                           const uint8_t* __restrict__ hi, const uint8_t* __restrict__ lo,
                                           const uint16_t* __restrict__ sc, const int* tok, int nt,
                                           uint16_t* __restrict__ y, float* __restrict__ ws, float (*red)[TB][64],
-                                          uint4* xs) {
+                                          uint4* xs, int tile, int slice, int nslice) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tile = blockIdx.x, slice = blockIdx.y, nslice = gridDim.y;
   const int nb = K >> 5;
   const int per = (nb + nslice - 1) / nslice;
   const int b0 = slice * per, b1 = min(nb, b0 + per);
@@ -186,7 +186,7 @@ __device__ __forceinline__ void gemv_tile(const uint16_t* __restrict__ x, int B,
     if (nslice == 1) {
       if (n < N) y[(size_t)tok[t] * N + n] = (uint16_t)f32_to_bf16(v);
     } else {
-      ws[((size_t)slice * kWsTokens + tok[t]) * (gridDim.x * 64) + n] = v;
+      ws[((size_t)slice * kWsTokens + tok[t]) * ((size_t)((N + 63) / 64) * 64) + n] = v;
     }
   }
 }
@@ -201,12 +201,30 @@ __global__ __launch_bounds__(256) void gemv_low_kernel(const uint16_t* __restric
   int tok[TB];
 #pragma unroll
   for (int t = 0; t < TB; ++t) tok[t] = t;
-  gemv_tile<TB, false>(x, B, K, N, hi, nullptr, sc, tok, B < TB ? B : TB, y, ws, red, xs);
+  gemv_tile<TB, false>(x, B, K, N, hi, nullptr, sc, tok, B < TB ? B : TB, y, ws, red, xs, blockIdx.x, blockIdx.y,
+                       gridDim.y);
 }
 
 // Escalation: workgroup z takes the flagged tokens of rank 4z .. 4z + 3
 // (ranks in token order); groups past the last flagged token exit at once.
 constexpr int kEscTokens = 4;
+
+// The flagged tokens of rank 4 z .. 4 z + 3 (wave-uniform); returns their
+// count, 0 when none is left for this group.
+__device__ __forceinline__ int flagged_group(const uint8_t* __restrict__ flags, int B, int z, int tok[kEscTokens]) {
+  uint32_t fmask = 0;
+  for (int t = 0; t < B; ++t) fmask |= (flags[t] != 0 ? 1u : 0u) << t;
+  fmask = __builtin_amdgcn_readfirstlane(fmask);
+  for (int r = 0; r < kEscTokens * z; ++r) fmask &= fmask - 1u;  // drop earlier groups
+  int nt = 0;
+#pragma unroll
+  for (int t = 0; t < kEscTokens; ++t) {
+    tok[t] = fmask ? __builtin_ctz(fmask) : 0;
+    nt += fmask ? 1 : 0;
+    fmask &= fmask - 1u;
+  }
+  return nt;
+}
 
 __global__ __launch_bounds__(256) void gemv_escalate_kernel(const uint16_t* __restrict__ x, int B, int K, int N,
                                                             const uint8_t* __restrict__ hi,
@@ -215,20 +233,11 @@ __global__ __launch_bounds__(256) void gemv_escalate_kernel(const uint16_t* __re
                                                             const uint8_t* __restrict__ flags,
                                                             uint16_t* __restrict__ y, float* __restrict__ ws) {
   __shared__ float red[4][kEscTokens][64];
-  uint32_t fmask = 0;
-  for (int t = 0; t < B; ++t) fmask |= (flags[t] != 0 ? 1u : 0u) << t;
-  fmask = __builtin_amdgcn_readfirstlane(fmask);
-  for (int r = 0; r < kEscTokens * (int)blockIdx.z; ++r) fmask &= fmask - 1u;  // drop earlier groups
-  if (fmask == 0) return;  // nothing (more) flagged: no weight traffic
   int tok[kEscTokens];
-  int nt = 0;
-#pragma unroll
-  for (int t = 0; t < kEscTokens; ++t) {
-    tok[t] = fmask ? __builtin_ctz(fmask) : 0;
-    nt += fmask ? 1 : 0;
-    fmask &= fmask - 1u;
-  }
-  gemv_tile<kEscTokens, true>(x, B, K, N, hi, lo, sc, tok, nt, y, ws, red, nullptr);
+  const int nt = flagged_group(flags, B, blockIdx.z, tok);
+  if (nt == 0) return;  // nothing (more) flagged: no weight traffic
+  gemv_tile<kEscTokens, true>(x, B, K, N, hi, lo, sc, tok, nt, y, ws, red, nullptr, blockIdx.x, blockIdx.y,
+                              gridDim.y);
 }
 
 // y[t][n] = BF16(sum over slices of ws[slice][t][n]) in slice order, for
@@ -243,6 +252,52 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restric
   float v = 0.0f;
   for (int sl = 0; sl < nslice; ++sl) v += ws[((size_t)sl * kWsTokens + t) * Np + n];
   y[i] = (uint16_t)f32_to_bf16(v);
+}
+
+// Grouped launch: workgroup g of the grid takes 64-row tile
+// g - tile_start of the problem whose [tile_start, tile_start + ceil(N/64))
+// holds g (binary search over the table; every load is wave-uniform).
+__device__ __forceinline__ const rq_gemv_problem* find_problem(const rq_gemv_problem* __restrict__ probs, int count,
+                                                               int64_t g) {
+  int lo = 0, hi = count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (__builtin_amdgcn_readfirstlane((int)(probs[mid].tile_start <= g))) lo = mid;
+    else hi = mid - 1;
+  }
+  return probs + lo;
+}
+
+template <int TB>
+__global__ __launch_bounds__(256) void gemv_low_grouped_kernel(const rq_gemv_problem* __restrict__ probs, int count,
+                                                               int B) {
+  __shared__ float red[4][TB][64];
+  __shared__ uint4 xs[4 * 64];
+  const rq_gemv_problem* p = find_problem(probs, count, blockIdx.x);
+  const int64_t tile = (int64_t)blockIdx.x - p->tile_start;
+  if (tile < 0 || tile >= (p->N + 63) / 64) return;  // a total beyond the plan
+  int tok[TB];
+#pragma unroll
+  for (int t = 0; t < TB; ++t) tok[t] = t;
+  gemv_tile<TB, false>(static_cast<const uint16_t*>(p->x_bf16), B, (int)p->K, (int)p->N, p->w_hi, nullptr,
+                       p->scales_tiled, tok, B < TB ? B : TB, static_cast<uint16_t*>(p->y_bf16), nullptr, red, xs,
+                       (int)tile, 0, 1);
+}
+
+__global__ __launch_bounds__(256) void gemv_escalate_grouped_kernel(const rq_gemv_problem* __restrict__ probs,
+                                                                    int count, int B,
+                                                                    const uint8_t* __restrict__ flags) {
+  __shared__ float red[4][kEscTokens][64];
+  int tok[kEscTokens];
+  const int nt = flagged_group(flags, B, blockIdx.z, tok);
+  if (nt == 0) return;
+  const rq_gemv_problem* p = find_problem(probs, count, blockIdx.x);
+  const int64_t tile = (int64_t)blockIdx.x - p->tile_start;
+  // problems without a low plane take no escalation
+  if (p->w_lo == nullptr || tile < 0 || tile >= (p->N + 63) / 64) return;
+  gemv_tile<kEscTokens, true>(static_cast<const uint16_t*>(p->x_bf16), B, (int)p->K, (int)p->N, p->w_hi, p->w_lo,
+                              p->scales_tiled, tok, nt, static_cast<uint16_t*>(p->y_bf16), nullptr, red, nullptr,
+                              (int)tile, 0, 1);
 }
 
 // One thread per (padded row, 32-block): 32 int8 weights -> one 16-byte
@@ -351,6 +406,29 @@ hipError_t launch_gemv_escalate(const uint16_t* x, int64_t B, int64_t K, int64_t
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && ns > 1) e = launch_reduce(w, ns, B, N, flags, y, stream);
   return e;
+}
+
+hipError_t launch_gemv_grouped(const rq_gemv_problem* probs, int count, int64_t total_tiles, int64_t B,
+                               const uint8_t* flags, int phase, hipStream_t stream) {
+  if (total_tiles <= 0) return hipSuccess;
+  const int b = (int)B;
+  if (phase & 1) {
+    switch (gemv_tb(B)) {
+      case 1: gemv_low_grouped_kernel<1><<<(unsigned)total_tiles, 256, 0, stream>>>(probs, count, b); break;
+      case 2: gemv_low_grouped_kernel<2><<<(unsigned)total_tiles, 256, 0, stream>>>(probs, count, b); break;
+      case 4: gemv_low_grouped_kernel<4><<<(unsigned)total_tiles, 256, 0, stream>>>(probs, count, b); break;
+      case 8: gemv_low_grouped_kernel<8><<<(unsigned)total_tiles, 256, 0, stream>>>(probs, count, b); break;
+      default: gemv_low_grouped_kernel<16><<<(unsigned)total_tiles, 256, 0, stream>>>(probs, count, b); break;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (phase & 2) {
+    const dim3 grid((unsigned)total_tiles, 1, (unsigned)((B + kEscTokens - 1) / kEscTokens));
+    gemv_escalate_grouped_kernel<<<grid, 256, 0, stream>>>(probs, count, b, flags);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 }  // namespace rq

@@ -289,6 +289,53 @@ rq_status rq_gemv_nibble_escalate(const void* x_bf16, int64_t B, int64_t K, int6
   return hip_status(e, "rq_gemv_nibble_escalate launch");
 }
 
+int64_t rq_gemv_group_plan(rq_gemv_problem* problems, int count) {
+  if (!problems || count < 1) {
+    fail(RQ_EINVAL, "rq_gemv_group_plan: need problems and count >= 1");
+    return -1;
+  }
+  int64_t tiles = 0;
+  for (int i = 0; i < count; ++i) {
+    rq_gemv_problem& p = problems[i];
+    if (!p.x_bf16 || !p.w_hi || !p.scales_tiled || !p.y_bf16) {
+      fail(RQ_EINVAL, "rq_gemv_group_plan: problem %d has a null pointer", i);
+      return -1;
+    }
+    if (p.N <= 0 || p.K <= 0 || p.K % 32 || p.N > kInt32Max || p.K > kInt32Max) {
+      fail(RQ_ESHAPE, "rq_gemv_group_plan: problem %d needs N > 0, K > 0, K %% 32 == 0", i);
+      return -1;
+    }
+    if (!aligned16(p.x_bf16) || !aligned16(p.w_hi) || (p.w_lo && !aligned16(p.w_lo))) {
+      fail(RQ_EALIGN, "rq_gemv_group_plan: problem %d: x and planes must be 16-byte aligned", i);
+      return -1;
+    }
+    p.tile_start = tiles;
+    tiles += (p.N + 63) / 64;
+  }
+  if (tiles > kInt32Max) {
+    fail(RQ_ESHAPE, "rq_gemv_group_plan: too many tiles");
+    return -1;
+  }
+  ok();
+  return tiles;
+}
+
+rq_status rq_gemv_nibble_escalate_grouped(const rq_gemv_problem* problems_dev, int count, int64_t total_tiles,
+                                          int64_t B, const uint8_t* flags, int phase, void* stream) {
+  if (!problems_dev) return fail(RQ_EINVAL, "rq_gemv_nibble_escalate_grouped: null problem table");
+  if (phase != RQ_LOW && phase != RQ_ESCALATE && phase != RQ_BOTH)
+    return fail(RQ_EINVAL, "rq_gemv_nibble_escalate_grouped: unknown phase %d", phase);
+  if ((phase & RQ_ESCALATE) && !flags)
+    return fail(RQ_EINVAL, "rq_gemv_nibble_escalate_grouped: escalation needs flags");
+  if (count < 1 || total_tiles < 1 || total_tiles > kInt32Max)
+    return fail(RQ_ESHAPE, "rq_gemv_nibble_escalate_grouped: need count >= 1 and a planned tile total");
+  if (B < 1 || B > 16) return fail(RQ_ESHAPE, "rq_gemv_nibble_escalate_grouped: B must be in [1, 16]");
+  if (!aligned16(problems_dev)) return fail(RQ_EALIGN, "rq_gemv_nibble_escalate_grouped: table must be 16-byte aligned");
+  if (rq_status s = need_device(); s != RQ_OK) return s;
+  return hip_status(rq::launch_gemv_grouped(problems_dev, count, total_tiles, B, flags, phase, as_stream(stream)),
+                    "rq_gemv_nibble_escalate_grouped launch");
+}
+
 rq_status rq_escalation_gate(const void* logits_bf16, int64_t B, int64_t V, float tau, float delta, uint8_t* flags,
                              float* stats, void* stream) {
   if (!logits_bf16 || !flags) return fail(RQ_EINVAL, "rq_escalation_gate: null pointer");

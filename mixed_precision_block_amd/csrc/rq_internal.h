@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+struct rq_gemv_problem;  // include/rq.h
+
 namespace rq {
 
 // GEMM epilogues.  Y is [M x N] row-major.
@@ -62,6 +64,11 @@ hipError_t launch_gemv_escalate(const uint16_t* x, int64_t B, int64_t K, int64_t
                                 const uint8_t* hi, const uint8_t* lo, const uint16_t* scales,
                                 const uint8_t* flags, uint16_t* y, void* ws, size_t ws_bytes,
                                 hipStream_t stream);
+// One launch over many problems (rq_gemv_problem table in device memory,
+// tile_start set by rq_gemv_group_plan): phase 1 low pass, 2 escalation,
+// 3 both.
+hipError_t launch_gemv_grouped(const ::rq_gemv_problem* probs, int count, int64_t total_tiles, int64_t B,
+                               const uint8_t* flags, int phase, hipStream_t stream);
 hipError_t launch_gate(const uint16_t* logits, int64_t B, int64_t V, float tau, float delta,
                        uint8_t* flags, float* stats, hipStream_t stream);
 hipError_t launch_kv_quant(const uint16_t* x, int64_t T, int64_t H, int64_t D, uint8_t* codes,

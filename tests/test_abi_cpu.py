@@ -147,3 +147,28 @@ def test_select_channels_host_helper():
 def test_valid_call_without_device_reports_enodev():
     assert status_of(rq.rq_gemm, L.RQ_MXFP4, A16, A16, A16, A16, 4, 4, 64, 0, A16) == L.RQ_ENODEV
     assert b"no HIP device" in L.lib().rq_last_error()
+
+
+def test_gemv_group_plan_and_grouped_validation():
+    P = rq.RqGemvProblem
+    arr = (P * 3)()
+    for i, (n, k) in enumerate(((100, 64), (64, 32), (151936, 1024))):
+        arr[i] = P(A16, A16, None, A16, A16, n, k, 0)
+    assert rq.rq_gemv_group_plan(arr) == 2 + 1 + 2374
+    assert [arr[i].tile_start for i in range(3)] == [0, 2, 3]
+    for field, value in (("K", 33), ("N", 0), ("x_bf16", None), ("w_hi", A16 + 8)):
+        bad = (P * 1)()
+        bad[0] = P(A16, A16, None, A16, A16, 64, 32, 0)
+        setattr(bad[0], field, value)
+        with pytest.raises(L.RQError):
+            rq.rq_gemv_group_plan(bad)
+    g = [A16, 3, 2377, 16, A16, L.RQ_BOTH]
+    for i, v, want in [(0, None, L.RQ_EINVAL), (1, 0, L.RQ_ESHAPE), (2, 0, L.RQ_ESHAPE), (3, 17, L.RQ_ESHAPE),
+                       (4, None, L.RQ_EINVAL), (5, 9, L.RQ_EINVAL), (0, A16 + 4, L.RQ_EALIGN)]:
+        a = list(g)
+        a[i] = v
+        assert status_of(rq.rq_gemv_nibble_escalate_grouped, *a) == want, (i, v)
+    lowonly = list(g)
+    lowonly[4] = None
+    lowonly[5] = L.RQ_LOW
+    assert status_of(rq.rq_gemv_nibble_escalate_grouped, *lowonly) in (L.RQ_OK, L.RQ_ENODEV)

@@ -164,3 +164,39 @@ def test_split_workspace_reused_across_calls():
             bound = V.abs_bound(d["x"], d["w"], d["scales"]) + V.abs_bound(d["x"], 16 * hi8.astype(np.int64),
                                                                             d["scales"])
             check_bf16(host_bits(y), ref, bound, f"reuse {n}x{k}", k=k)
+
+
+@pytest.mark.parametrize("B", [1, 5, 16])
+def test_grouped_equals_per_problem(B):
+    """One grouped launch over mixed shapes (ragged N, one problem without a
+    low plane) gives the per-problem unsplit outputs bit for bit, in both
+    phases; a tile total beyond the plan changes nothing."""
+    shapes = [(200, 96), (64, 32), (1000, 1024), (130, 3072), (777, 256), (64, 64)]
+    rng = np.random.default_rng(B)
+    f = rng.random(B) < 0.5
+    f[0] = True
+    flags = dev(f.astype(np.uint8))
+    probs, want_low, want_both = [], [], []
+    for i, (n, k) in enumerate(shapes):
+        d = W.c5_linear(10 + i, N=n, K=k, B=B)
+        planes = gpu_planes(d["w"], d["scales"])
+        x = dev_bf16(d["x"])
+        if i == 4:
+            planes = (planes[0], None, planes[2])
+        want_low.append(host_bits(api.gemv_nibble_escalate(x, n, planes, None, L.RQ_LOW, split=False)))
+        want_both.append(host_bits(api.gemv_nibble_escalate(x, n, planes, flags, L.RQ_BOTH, split=False))
+                         if planes[1] is not None else want_low[-1])
+        probs.append((x, planes, torch.zeros((B, n), dtype=torch.bfloat16, device="cuda")))
+    table = api.gemv_group(probs)
+    assert table[2] == sum((n + 63) // 64 for n, _ in shapes)
+    for phase, want in ((L.RQ_LOW, want_low), (L.RQ_BOTH, want_both)):
+        for _, _, y in probs:
+            y.zero_()
+        api.gemv_nibble_escalate_grouped(table, B, flags if phase == L.RQ_BOTH else None, phase)
+        for i, (w, (_, _, y)) in enumerate(zip(want, probs)):
+            assert np.array_equal(host_bits(y), w), (phase, shapes[i])
+    over = (table[0], table[1], table[2] + 5)
+    api.gemv_nibble_escalate_grouped(over, B, flags, L.RQ_BOTH)
+    for i, (w, (_, _, y)) in enumerate(zip(want_both, probs)):
+        assert np.array_equal(host_bits(y), w), shapes[i]
+    log(f"grouped GEMV B={B}: {len(shapes)} problems, {table[2]} tiles, equal to per-problem calls")
