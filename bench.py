@@ -87,15 +87,26 @@ class Timer:
 
 
 def time_calls(torch, fn, iters, warmup=3, before=None):
-    """Mean per-call milliseconds of fn() from events around each call."""
+    """Mean per-call milliseconds of fn().  Without `before`, one pair of
+    events brackets the back-to-back calls (the host issues faster than the
+    GPU runs them, so this is device time); with it, events bracket each
+    call and the untimed `before` work runs in between."""
     for _ in range(warmup):
         if before:
             before()
         fn()
+    if before is None:
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
     tm = Timer(torch)
     for _ in range(iters):
-        if before:
-            before()
+        before()
         s = tm.start()
         fn()
         tm.stop(s)
@@ -154,25 +165,34 @@ def main():
                            y=torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
     flops_step = sum(2.0 * M * g["K"] * g["N"] for g in groups)
 
-    def step(tm=None):
-        for g in groups:
+    def step(ev=None):
+        for i, g in enumerate(groups):
             L.rq_quantize(g["a"], M, g["K"], L.RQ_MXFP8, None, 0, L.RQ_APPEND_NONE, g["ac"], g["as_"])
-            s = tm.start() if tm else None
+            if ev:
+                ev[i][0].record()
             L.rq_gemm(L.RQ_MXFP8, g["ac"], g["as_"], g["wc"], g["ws"], M, g["N"], g["K"], L.RQ_OUT_BF16, g["y"])
-            if tm:
-                tm.stop(s)
+            if ev:
+                ev[i][1].record()
 
     for _ in range(args.warmup):
         step()
+    # timed region: the steps alone, wall clock between synchronizations
     torch.cuda.synchronize()
-    tm = Timer(torch)
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(tm)
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    gemm_ms = tm.total_ms() / (args.steps * len(groups))  # average launch
+    # the same steps again with events (made beforehand) around every GEMM
+    # launch, for the GEMM's average launch duration
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in groups]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for ev in evs:
+        step(ev)
+    torch.cuda.synchronize()
+    gemm_ms = sum(s.elapsed_time(e) for ev in evs for s, e in ev) / (args.steps * len(groups))  # average launch
     achieved = flops_step / len(groups) / (gemm_ms * 1e-3)
     log(f"main: {ms_step:.3f} ms/step, GEMM avg launch {gemm_ms * 1e3:.1f} us")
     value = flops_step / (ms_step * 1e-3) / 1e12

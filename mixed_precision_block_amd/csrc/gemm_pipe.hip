@@ -9,19 +9,20 @@
 //   RB of MXFP8 or RB / 2 of BF16, so each stage carries the same
 //   matrix-core work whatever the format.  128-byte chunks are whole cache
 //   lines for the global loads.
-// * Global loads are buffer loads (the resource spans the tile's rows, so
-//   rows past M or N read as zeros) into a ring of P register slots, issued
-//   P stages ahead; each stage is then written to one of two LDS buffers
-//   while the other feeds the MFMAs.  The loop is unrolled over the ring and
-//   the two buffers so every register slot is static, and the compiler's
-//   load counters wait exactly for the slot being written out.
+// * Operands go straight from global memory into LDS (gfx950's 16-byte
+//   buffer loads to LDS; scales by 4-byte ones), NSTG stages deep: while one
+//   stage feeds the MFMAs the next NSTG - 1 are in flight.  No registers
+//   hold operands on the way and no LDS writes are issued by the waves.  The
+//   buffer resources span the tile's rows, so rows past M or N load zeros.
+//   Each step ends with one wait on this wave's loads of the next stage and
+//   one barrier.
 // * LDS rows are RB bytes of 16-byte chunks, XOR-swizzled per row so that
 //   the fragment reads of consecutive rows hit distinct banks (checked for
 //   both 32- and 64-bank LDS models).
 // * WMW x WNW waves, each owning a (BM/WMW) x (BN/WNW) quadrant of MFMA
 //   tiles of 32 x 32; accumulators live in AGPRs.  256 x 256 tiles use
-//   eight waves (two per SIMD, so one wave's waits and LDS writes overlap
-//   the other's MFMAs), 128 x 128 tiles four (two workgroups share a CU).
+//   eight waves (two per SIMD, so one wave's waits overlap the other's
+//   MFMAs), 128 x 128 tiles four.
 // * Workgroups are ordered so that consecutive tiles land on the same XCD
 //   (the dispatcher deals workgroups round-robin over the 8 XCDs) and each
 //   XCD's tiles form a compact block of 4 M-tiles, sharing A and W panels in
@@ -76,61 +77,50 @@ __device__ __forceinline__ int swz(int r) {
 // Publish LDS writes and wait for every wave (no wait on global loads).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int FMT, int BM, int BN, int RB, int WMW, int WNW>
-struct PipeCfg {
+// One wave-wide direct load into LDS: lane l's 16 (4) bytes land at
+// lds + 16 l (4 l).
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void load_lds4(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
+}
+
+template <int FMT, int BM, int BN, int RB, int WMW, int WNW, int NSTG>
+struct DmaCfg {
   using T = PipeTraits<FMT, RB>;
-  static constexpr int NW = WMW * WNW, NT = 64 * NW;              // waves, threads
-  static constexpr int TM = BM / 32 / WMW, TN = BN / 32 / WNW;    // MFMA tiles per wave
-  static constexpr int WM = BM / WMW, WN = BN / WNW;              // wave quadrant
-  static constexpr int CPR = RB / 16;                             // 16-byte chunks per row
-  static constexpr int RPL = NT / CPR;                            // rows per workgroup-wide load
-  static constexpr int CA = BM / RPL, CW = BN / RPL;              // 16-byte chunks per thread per stage
-  static constexpr int SA = BM * RB, SW = BN * RB;                // LDS bytes of the A / W tile
-  static constexpr int SBPR = T::kSBPR;                           // scale bytes per row per stage
-  static constexpr int SS = (BM + BN) * SBPR;                     // scale bytes per stage
+  static constexpr int NW = WMW * WNW, NT = 64 * NW;
+  static constexpr int TM = BM / 32 / WMW, TN = BN / 32 / WNW;
+  static constexpr int WM = BM / WMW, WN = BN / WNW;
+  static constexpr int CPR = RB / 16;                 // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;                // rows per wave-wide 16-byte DMA (1 KB)
+  static constexpr int IA = BM / RPI, IW = BN / RPI;  // DMAs per stage of the A / W tile
+  static constexpr int DPW = (IA + IW + NW - 1) / NW; // operand DMAs per wave per stage (the last waves may have fewer)
+  static constexpr int SA = BM * RB, SW = BN * RB;
+  static constexpr int SBPR = T::kSBPR;
+  static constexpr int SS = (BM + BN) * SBPR;
+  static constexpr int IS = SS / 256;                 // dword DMAs of the stage's scales (0 for BF16)
+  static constexpr int SPW = (IS + NW - 1) / NW;
+  static constexpr bool kEven = (IA + IW) % NW == 0 && IS % NW == 0;
+  static constexpr int DW = DPW + SPW;                // DMAs per wave per stage
   static constexpr int STAGE = SA + SW + SS;
-  static constexpr int NS = T::kScaled ? (BM + BN) / NT : 0;      // scale rows per thread
-  static constexpr int SLOT = 4 * (CA + CW);                      // VGPRs of one ring slot
-  // register ring depth: with two waves per SIMD three 16-VGPR slots or
-  // one larger slot; otherwise one slot when it is large (the compiler
-  // still renames it one stage ahead), two or four when small
-  static constexpr int P = NW > 4 ? (SLOT <= 16 ? 3 : 1) : (SLOT >= 64 ? 1 : (SLOT >= 32 ? 2 : 4));
-  static constexpr int U = P % 2 ? 2 * P : P;                     // steps per unrolled loop turn
-  static_assert(CA * RPL == BM && CW * RPL == BN, "whole chunk rows per thread");
-  static_assert(!T::kScaled || NS * NT == BM + BN, "whole scale rows per thread");
-  static_assert(BM % 64 == 0, "A / W scale rows split on a wave boundary");
+  static_assert(kEven || NSTG == 2, "deeper rings count each wave's loads: even splits only");
+  static_assert(SS % 256 == 0, "whole scale DMAs");
+  static_assert((BM * SBPR) % 256 == 0, "a scale DMA stays on one side");
+  static_assert(NSTG * STAGE <= 160 * 1024, "stages fit the LDS");
 };
 
-template <int SBPR>
-struct ScaleWord {
-  using type = uint32_t;
-};
-template <>
-struct ScaleWord<8> {
-  using type = uint2;
-};
-
-template <int FMT, int BM, int BN, int RB, int WMW, int WNW>
-struct StageRegs {
-  using C = PipeCfg<FMT, BM, BN, RB, WMW, WNW>;
-  v4i a[C::CA];
-  v4i w[C::CW];
-  typename ScaleWord<C::SBPR>::type s[C::NS > 0 ? C::NS : 1];
-};
-
-template <int FMT, int EPI, int BM, int BN, int RB, int WMW, int WNW>
+template <int FMT, int EPI, int BM, int BN, int RB, int WMW, int WNW, int NSTG>
 __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint8_t* __restrict__ A,
                                                                       const uint8_t* __restrict__ As,
                                                                       const uint8_t* __restrict__ W,
                                                                       const uint8_t* __restrict__ Ws, int M, int N,
                                                                       int K, void* __restrict__ Y, int tiles_m,
                                                                       int tiles_n) {
-  using C = PipeCfg<FMT, BM, BN, RB, WMW, WNW>;
+  using C = DmaCfg<FMT, BM, BN, RB, WMW, WNW, NSTG>;
   using T = PipeTraits<FMT, RB>;
-  using SW_t = typename ScaleWord<C::SBPR>::type;
-  constexpr int TM = C::TM, TN = C::TN, P = C::P, U = C::U;
-  constexpr int CMAX = C::CA > C::CW ? C::CA : C::CW;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::STAGE];
+  constexpr int TM = C::TM, TN = C::TN;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTG * C::STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -161,62 +151,52 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
     rsw = __builtin_amdgcn_make_buffer_rsrc((void*)(Ws + (size_t)n0 * ksb), 0, (int)(w_rows * ksb), 0x00020000);
   }
 
-  // This thread's chunks: rows tid / CPR + RPL i, logical chunk tid % CPR.
-  const int crow = tid / C::CPR, cchk = tid % C::CPR;
-  uint32_t g_off[CMAX], l_off[CMAX];
+  // Direct global-to-LDS loads: each wave-wide 16-byte load fills 1 KB of
+  // LDS, lane l at byte 16 l, i.e. RPI whole rows.  The swizzle is applied
+  // on the global side: the lane writing physical chunk p of row r reads
+  // logical chunk p ^ swz(r).
+  uint32_t voff[C::DPW];
 #pragma unroll
-  for (int i = 0; i < CMAX; ++i) {
-    const int r = crow + C::RPL * i;
-    g_off[i] = (uint32_t)r * ld + 16u * (uint32_t)cchk;
-    l_off[i] = (uint32_t)r * RB + 16u * (uint32_t)(cchk ^ swz<RB>(r));
+  for (int i = 0; i < C::DPW; ++i) {
+    const int q = wave * C::DPW + i;
+    const int r = (q < C::IA ? q : q - C::IA) * C::RPI + lane / C::CPR;
+    voff[i] = (uint32_t)r * ld + 16u * (uint32_t)((lane % C::CPR) ^ swz<RB>(r));
+  }
+  uint32_t soff[C::SPW > 0 ? C::SPW : 1];
+  if constexpr (T::kScaled) {
+#pragma unroll
+    for (int i = 0; i < C::SPW; ++i) {
+      const int q = wave * C::SPW + i;
+      const int rho = (q * 256 + 4 * lane) / C::SBPR;  // scale row (A rows, then W rows)
+      const int b = (4 * lane) % C::SBPR;
+      soff[i] = (uint32_t)(rho < BM ? rho : rho - BM) * ksb + (uint32_t)b;
+    }
   }
 
-  StageRegs<FMT, BM, BN, RB, WMW, WNW> R[P];
-
-  // Loads of stages past the end use an offset beyond every buffer range:
-  // the hardware returns zeros without a memory access, so the prefetch
-  // needs no branch (a branch around it would make the compiler's load
-  // counter wait for everything at the join).
+  // Stages past the end read at an offset beyond every buffer range (zeros,
+  // no memory access), so every step issues the same number of loads and
+  // the load-count waits below stay exact.
   constexpr uint32_t kPastEnd = 0x80000000u;
-  auto load = [&](StageRegs<FMT, BM, BN, RB, WMW, WNW>& r, int s) {
+  auto issue = [&](uint8_t* st, int s) {
     const uint32_t kb = s < nk ? (uint32_t)s * RB : kPastEnd;
 #pragma unroll
-    for (int i = 0; i < C::CA; ++i)
-      r.a[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, g_off[i] + kb, 0, 0));
-#pragma unroll
-    for (int i = 0; i < C::CW; ++i)
-      r.w[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rw, g_off[i] + kb, 0, 0));
-    if constexpr (T::kScaled) {
-      // Scale rows 0..BM-1 of A then 0..BN-1 of W, SBPR bytes per row and
-      // load: thread t takes rows t + NT j; BM is a multiple of the wave
-      // size, so the A / W choice is wave-uniform and the buffer resource
-      // stays scalar.
-      const uint32_t sk = s >= nk ? kPastEnd : (uint32_t)s * C::SBPR;
-      auto ld_s = [&](__amdgpu_buffer_rsrc_t rs, uint32_t row) -> SW_t {
-        if constexpr (C::SBPR == 8)
-          return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, row * ksb + sk, 0, 0));
-        else
-          return __builtin_amdgcn_raw_buffer_load_b32(rs, row * ksb + sk, 0, 0);
-      };
-#pragma unroll
-      for (int j = 0; j < C::NS; ++j) {
-        const int rho = tid + C::NT * j;  // wave-uniform side
-        if (__builtin_amdgcn_readfirstlane(rho) < BM)
-          r.s[j] = ld_s(rsa, (uint32_t)rho);
-        else
-          r.s[j] = ld_s(rsw, (uint32_t)(rho - BM));
-      }
+    for (int i = 0; i < C::DPW; ++i) {
+      const int q = wave * C::DPW + i;
+      if (!C::kEven && q >= C::IA + C::IW) break;
+      const bool is_a = q < C::IA;
+      uint8_t* dst = st + (is_a ? q * 1024 : C::SA + (q - C::IA) * 1024);
+      load_lds16(is_a ? ra : rw, dst, voff[i] + kb);
     }
-  };
-  auto store = [&](const StageRegs<FMT, BM, BN, RB, WMW, WNW>& r, uint8_t* st) {
-#pragma unroll
-    for (int i = 0; i < C::CA; ++i) *reinterpret_cast<v4i*>(st + l_off[i]) = r.a[i];
-#pragma unroll
-    for (int i = 0; i < C::CW; ++i) *reinterpret_cast<v4i*>(st + C::SA + l_off[i]) = r.w[i];
     if constexpr (T::kScaled) {
+      const uint32_t sk = s < nk ? (uint32_t)s * C::SBPR : kPastEnd;
 #pragma unroll
-      for (int j = 0; j < C::NS; ++j)
-        *reinterpret_cast<SW_t*>(st + C::SA + C::SW + C::SBPR * (tid + C::NT * j)) = r.s[j];
+      for (int i = 0; i < C::SPW; ++i) {
+        const int q = wave * C::SPW + i;
+        if (!C::kEven && q >= C::IS) break;
+        const bool is_a = q * 256 < BM * C::SBPR;
+        uint8_t* dst = st + C::SA + C::SW + q * 256;
+        load_lds4(is_a ? rsa : rsw, dst, soff[i] + sk);
+      }
     }
   };
 
@@ -227,7 +207,6 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
   // A stage in slices of 64 K (16 K for BF16): each slice's fragments are
   // read from LDS, then its MFMAs issue (the compiler interleaves the next
   // slice's reads with them).  Each row's scales come as one dword per two
@@ -301,65 +280,38 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
     }
   };
 
-  uint8_t* const lds0 = smem;
-  uint8_t* const lds1 = smem + C::STAGE;
-
-  // Step s (unrolled position J = s % U, register slot J % P): write stage
-  // s+1 from its slot into the other LDS buffer, refill that slot with stage
-  // s+1+P, compute stage s.
+  // Step s (unrolled position J = s % NSTG): load stage s + NSTG - 1 into
+  // the buffer freed by step s - 1, compute stage s, then wait for this
+  // wave's loads of stage s + 1 and for every wave.
+  constexpr int kAhead = (NSTG - 2) * C::DW;
   auto step = [&](auto Jc, int s) {
     constexpr int J = decltype(Jc)::value;
-    constexpr int Jn = (J + 1) % P;
-    uint8_t* cur = (J % 2) ? lds1 : lds0;
-    uint8_t* nxt = (J % 2) ? lds0 : lds1;
-    store(R[Jn], nxt);  // past the last stage this writes zeros nobody reads
-    // two waves per SIMD leave no registers to refill a one-slot ring
-    // before it is written out
-    if constexpr (C::NW > 4) __builtin_amdgcn_sched_barrier(0);
-    load(R[Jn], s + 1 + P);
-    // keep the refill ahead of the matrix work (the scheduler would sink it
-    // below, shortening the prefetch distance by a step)
+    issue(smem + ((J + NSTG - 1) % NSTG) * C::STAGE, s + NSTG - 1);
     __builtin_amdgcn_sched_barrier(0);
-    compute(cur);
-    lds_barrier();
+    compute(smem + J * C::STAGE);
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kAhead) : "memory");
   };
 
-  // prologue: fill the ring, publish stage 0
 #pragma unroll
-  for (int t = 0; t < P; ++t) {
-    load(R[t], t);
-    // issue order = slot order, so the loop's per-slot load-count waits hold
-    // on entry as well
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  store(R[0], lds0);
-  load(R[0], P);
-  __builtin_amdgcn_sched_barrier(0);
-  lds_barrier();
+  for (int t = 0; t < NSTG - 1; ++t) issue(smem + t * C::STAGE, t);
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kAhead) : "memory");
 
   int s = 0;
-  for (; s + U <= nk; s += U) {
+  for (; s + NSTG <= nk; s += NSTG) {
     step(std::integral_constant<int, 0>{}, s);
     step(std::integral_constant<int, 1>{}, s + 1);
-    if constexpr (U > 2) step(std::integral_constant<int, 2>{}, s + 2);
-    if constexpr (U > 3) step(std::integral_constant<int, 3>{}, s + 3);
-    if constexpr (U > 4) step(std::integral_constant<int, 4>{}, s + 4);
-    if constexpr (U > 5) step(std::integral_constant<int, 5>{}, s + 5);
+    if constexpr (NSTG > 2) step(std::integral_constant<int, 2>{}, s + 2);
+    if constexpr (NSTG > 3) step(std::integral_constant<int, 3>{}, s + 3);
   }
-  // the last nk % U steps keep their unrolled positions (slot and buffer)
   if (s < nk) step(std::integral_constant<int, 0>{}, s++);
-  if constexpr (U > 2) {
+  if constexpr (NSTG > 2) {
     if (s < nk) step(std::integral_constant<int, 1>{}, s++);
   }
-  if constexpr (U > 3) {
+  if constexpr (NSTG > 3) {
     if (s < nk) step(std::integral_constant<int, 2>{}, s++);
   }
-  if constexpr (U > 4) {
-    if (s < nk) step(std::integral_constant<int, 3>{}, s++);
-  }
-  if constexpr (U > 5) {
-    if (s < nk) step(std::integral_constant<int, 4>{}, s++);
-  }
+  // past-end loads may still be landing in LDS that the epilogue reuses
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 
   // Epilogue.  The W tile is the MFMA's first operand, so the accumulator
   // is the transposed tile: lane l, element r holds row m = l % 32 of the A
@@ -376,7 +328,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
   constexpr int RSTR = SC * EB + 16;                // strip row stride in bytes (16-byte aligned)
   constexpr int CPR = SC * EB / 16;                 // chunks per strip row
   constexpr int RPI = 64 / CPR;                     // strip rows per wave-wide read
-  static_assert(C::NW * 32 * RSTR <= 2 * C::STAGE, "epilogue strips fit in the stage buffers");
+  static_assert(C::NW * 32 * RSTR <= NSTG * C::STAGE, "epilogue strips fit in the stage buffers");
   uint8_t* const strip = smem + wave * 32 * RSTR;
   const int n_wave = n0 + wn * WN;
 #pragma unroll
@@ -478,11 +430,11 @@ bool gemm_pipe_supported(int fmt, int64_t M, int64_t N, int64_t K) {
   return 256 * ld < (int64_t)0x7FFFFFFF && M > 0 && N > 0;
 }
 
-template <int FMT, int EPI, int BM, int BN, int RB, int WMW, int WNW>
+template <int FMT, int EPI, int BM, int BN, int RB, int WMW, int WNW, int NSTG>
 static hipError_t launch_pipe_t(const void* a, const uint8_t* as, const void* w, const uint8_t* ws, int64_t M,
                                 int64_t N, int64_t K, void* y, hipStream_t stream) {
   const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
-  gemm_pipe_kernel<FMT, EPI, BM, BN, RB, WMW, WNW><<<tm * tn, 64 * WMW * WNW, 0, stream>>>(
+  gemm_pipe_kernel<FMT, EPI, BM, BN, RB, WMW, WNW, NSTG><<<tm * tn, 64 * WMW * WNW, 0, stream>>>(
       static_cast<const uint8_t*>(a), as, static_cast<const uint8_t*>(w), ws, (int)M, (int)N, (int)K, y, tm, tn);
   return hipGetLastError();
 }
@@ -490,10 +442,17 @@ static hipError_t launch_pipe_t(const void* a, const uint8_t* as, const void* w,
 template <int FMT, int EPI, int RB>
 static hipError_t launch_pipe_r(const void* a, const uint8_t* as, const void* w, const uint8_t* ws, int64_t M,
                                 int64_t N, int64_t K, void* y, hipStream_t stream) {
-  // 256 x 256 tiles when they fill the 256 CUs at least once, else 128 x 128
+  // 256 x 256 tiles (eight waves, 64-byte stages four deep or 128-byte ones
+  // double-buffered) when they fill the 256 CUs at least once.  Otherwise
+  // 128 x 128 tiles: three 128-byte stages when one workgroup per CU covers
+  // every tile, else two so that two workgroups share a CU; 64-byte stages
+  // always four deep.
   const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
-  if (big >= 256) return launch_pipe_t<FMT, EPI, 256, 256, RB, 2, 4>(a, as, w, ws, M, N, K, y, stream);
-  return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 2>(a, as, w, ws, M, N, K, y, stream);
+  if (big >= 256) return launch_pipe_t<FMT, EPI, 256, 256, RB, 2, 4, RB == 128 ? 2 : 4>(a, as, w, ws, M, N, K, y, stream);
+  const int64_t small = ((M + 127) / 128) * ((N + 127) / 128);
+  if (RB == 64) return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 2, 4>(a, as, w, ws, M, N, K, y, stream);
+  if (small <= 256) return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 2, 3>(a, as, w, ws, M, N, K, y, stream);
+  return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 2, 2>(a, as, w, ws, M, N, K, y, stream);
 }
 
 template <int FMT, int EPI>
