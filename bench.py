@@ -13,8 +13,10 @@ GFLOP, all seven linears) / wall time per step, in TFLOP/s, inputs resident
 in HBM.
 
 `roofline` covers the dominant kernel (the MXFP8 GEMM): algorithmic FLOP
-(2 M N K per launch) over its average launch time from HIP events recorded
-around every GEMM launch in the timed region.  `rows` measures the other
+(2 M N K per launch) over its average launch time, from HIP events around
+back-to-back launches of each of the step's four GEMMs on the same inputs,
+averaged over the four; `traffic` is the HBM bytes per launch from the
+committed counter summary (write it with --traffic-from).  `rows` measures the other
 steps of the path on their own workloads: single MXFP4 GEMM (128 x 1024 x
 1024), 4096^3 MXFP4 plain / ARC (K' = 4224) / BF16, quantization bandwidth,
 the recurrent prefill (8 steps, RAMP vs all-BF16) and the nibble GEMV
@@ -22,6 +24,7 @@ the recurrent prefill (8 steps, RAMP vs all-BF16) and the nibble GEMV
 oracle on a bounded sample of the main workload.
 
     python bench.py [--steps K] [--warmup W] [--no-rows] [--no-cpu-baseline]
+    python bench.py --traffic-from gpurun_out   # after the --pmc runs
 """
 
 import argparse
@@ -113,6 +116,61 @@ def time_calls(torch, fn, iters, warmup=3, before=None):
     return tm.total_ms() / iters
 
 
+COPY_BYTES = 256 << 20
+
+
+def write_traffic(pmc_dir):
+    """HBM bytes per launch of the main-line GEMM from FETCH_SIZE /
+    WRITE_SIZE counter runs (KiB per dispatch), each scaled by what the same
+    counter reads for a plain device copy of COPY_BYTES."""
+    import csv
+    from synthetic import workloads as W
+
+    def per_dispatch(run, counter):
+        path = os.path.join(pmc_dir, f"pmc_{run}_{counter}", "p_counter_collection.csv")
+        out = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Grid_Size"]))
+            out[key] = out.get(key, 0.0) + float(r["Counter_Value"]) * 1024  # KiB summed over instances
+        return out
+
+    scale = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        copies = [v for (d, name, g), v in per_dispatch("copy", counter).items() if "copy" in name.lower()]
+        copy_kib = sorted(copies)[len(copies) // 2]
+        scale[counter] = COPY_BYTES / copy_kib
+    grids = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        for (d, name, g), v in per_dispatch("main", counter).items():
+            if "gemm_pipe_kernel" not in name:
+                continue
+            e = grids.setdefault(g, {"grid_threads": g, "dispatches": 0, "FETCH_SIZE": 0.0, "WRITE_SIZE": 0.0})
+            e[counter] += v * scale[counter]
+            if counter == "FETCH_SIZE":
+                e["dispatches"] += 1
+    per_grid = []
+    for g, e in sorted(grids.items()):
+        n = e["dispatches"]
+        per_grid.append({"grid_threads": g, "dispatches": n, "read_bytes": round(e["FETCH_SIZE"] / n),
+                         "write_bytes": round(e["WRITE_SIZE"] / n)})
+    total = sum((e["read_bytes"] + e["write_bytes"]) * e["dispatches"] for e in per_grid)
+    nd = sum(e["dispatches"] for e in per_grid)
+    M = 4096
+    alg = [M * g["a"].shape[1] * 33 // 32 + g["w"].shape[0] * g["a"].shape[1] * 33 // 32 + M * g["w"].shape[0] * 2
+           for g in W.c2_layer(M=M)]
+    summary = {"kernel": "gemm_pipe_kernel<MXFP8, BF16 out>",
+               "workload": "qwen3-0.6b linear set of one layer, 4096 tokens, MXFP8, four GEMMs per step",
+               "gemm_source_sha256_16": source_hash(GEMM_SRCS),
+               "hbm_bytes_per_launch": round(total / nd),
+               "algorithmic_bytes_per_launch": round(sum(alg) / len(alg)),
+               "fetch_scale": scale["FETCH_SIZE"], "write_scale": scale["WRITE_SIZE"], "per_grid": per_grid}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(summary, f, indent=1)
+    print(json.dumps(summary, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,7 +180,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run plain 256 MiB device copies (the reference for HBM byte counters)")
+    ap.add_argument("--traffic-from", metavar="DIR",
+                    help="write the traffic summary from rocprofv3 --pmc CSV runs under DIR (pmc_main_FETCH_SIZE, "
+                         "pmc_main_WRITE_SIZE, pmc_copy_FETCH_SIZE, pmc_copy_WRITE_SIZE) and exit (no GPU needed)")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic(args.traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (no multi-GPU path is built).",
               file=sys.stderr)
@@ -165,14 +229,10 @@ def main():
                            y=torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
     flops_step = sum(2.0 * M * g["K"] * g["N"] for g in groups)
 
-    def step(ev=None):
-        for i, g in enumerate(groups):
+    def step():
+        for g in groups:
             L.rq_quantize(g["a"], M, g["K"], L.RQ_MXFP8, None, 0, L.RQ_APPEND_NONE, g["ac"], g["as_"])
-            if ev:
-                ev[i][0].record()
             L.rq_gemm(L.RQ_MXFP8, g["ac"], g["as_"], g["wc"], g["ws"], M, g["N"], g["K"], L.RQ_OUT_BF16, g["y"])
-            if ev:
-                ev[i][1].record()
 
     for _ in range(args.warmup):
         step()
@@ -184,15 +244,12 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    # the same steps again with events (made beforehand) around every GEMM
-    # launch, for the GEMM's average launch duration
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in groups]
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for ev in evs:
-        step(ev)
-    torch.cuda.synchronize()
-    gemm_ms = sum(s.elapsed_time(e) for ev in evs for s, e in ev) / (args.steps * len(groups))  # average launch
+    # the GEMM's average launch duration: each of the step's GEMMs launched
+    # back to back between one pair of events (events around every launch
+    # would add their own packets to the measured time), averaged over them
+    gemm_ms = sum(time_calls(torch, lambda g=g: L.rq_gemm(L.RQ_MXFP8, g["ac"], g["as_"], g["wc"], g["ws"], M, g["N"],
+                                                           g["K"], L.RQ_OUT_BF16, g["y"]), max(args.steps, 20))
+                  for g in groups) / len(groups)
     achieved = flops_step / len(groups) / (gemm_ms * 1e-3)
     log(f"main: {ms_step:.3f} ms/step, GEMM avg launch {gemm_ms * 1e3:.1f} us")
     value = flops_step / (ms_step * 1e-3) / 1e12

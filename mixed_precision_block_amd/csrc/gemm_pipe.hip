@@ -4,11 +4,13 @@
 // item 3: block scales applied inside the matrix core), organized for
 // throughput on large problems:
 //
-// * A pipeline stage holds one RB-byte chunk (RB = 128, or 64 where K does
-//   not divide) of every row of the A and W tiles: 2 RB elements of MXFP4,
-//   RB of MXFP8 or RB / 2 of BF16, so each stage carries the same
-//   matrix-core work whatever the format.  128-byte chunks are whole cache
-//   lines for the global loads.
+// * A pipeline stage holds one RB-byte chunk (RB = 128) of every row of the
+//   A and W tiles: 2 RB elements of MXFP4, RB of MXFP8 or RB / 2 of BF16, so
+//   each stage carries the same matrix-core work whatever the format.
+//   128-byte chunks are whole cache lines for the global loads.  When K is
+//   not a whole number of stages the last stage is partial: its loads run
+//   past the row (into the next row, or zeros past the buffer) and only its
+//   valid MFMA slices are computed.
 // * Operands go straight from global memory into LDS (gfx950's 16-byte
 //   buffer loads to LDS; scales by 4-byte ones), NSTG stages deep: while one
 //   stage feeds the MFMAs the next NSTG - 1 are in flight.  No registers
@@ -64,18 +66,12 @@ struct PipeTraits<3, RB> {  // BF16: RB / 2 K per stage in 16-deep slices
   static constexpr bool kScaled = false;
 };
 
-// Chunk swizzle of LDS row r.  64-byte rows: chunk bits (r1 ^ r3, r2 ^ r4);
-// 128-byte rows: chunk bits (r0 ^ r3, r2, r1).
+// Chunk swizzle of a 128-byte LDS row r: chunk bits (r0 ^ r3, r2, r1).
 template <int RB>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (RB == 64)
-    return ((r >> 1) ^ (r >> 3)) & 3;
-  else
-    return ((r ^ (r >> 3)) & 1) | ((r >> 1) & 2) | ((r << 1) & 4);
+  static_assert(RB == 128, "128-byte stage rows");
+  return ((r ^ (r >> 3)) & 1) | ((r >> 1) & 2) | ((r << 1) & 4);
 }
-
-// Publish LDS writes and wait for every wave (no wait on global loads).
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // One wave-wide direct load into LDS: lane l's 16 (4) bytes land at
 // lds + 16 l (4 l).
@@ -138,7 +134,9 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
 
   const uint32_t ld = FMT == 1 ? (uint32_t)K / 2 : (FMT == 2 ? (uint32_t)K : 2u * (uint32_t)K);  // row bytes
   const uint32_t ksb = (uint32_t)K / 32;
-  const int nk = K / T::kStepElems;
+  const int nk = (K + T::kStepElems - 1) / T::kStepElems;  // stages, the last one maybe partial
+  const int nfull = K / T::kStepElems;
+  const int tail_kk = (K - nfull * T::kStepElems) / (T::kStepElems / T::kKK);  // valid slices of a partial stage
 
   const uint32_t a_rows = (uint32_t)min(BM, M - m0), w_rows = (uint32_t)min(BN, N - n0);
   const __amdgpu_buffer_rsrc_t ra =
@@ -211,7 +209,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
   // read from LDS, then its MFMAs issue (the compiler interleaves the next
   // slice's reads with them).  Each row's scales come as one dword per two
   // slices; the lane's byte is extracted per slice.
-  auto compute = [&](const uint8_t* st) {
+  auto compute = [&](const uint8_t* st, int nkk) {
     constexpr int KK = T::kKK;
     constexpr int NQ = FMT == 2 ? 2 : 1;  // 16-byte chunks per lane per fragment
     const uint8_t* sc = st + C::SA + C::SW;
@@ -224,6 +222,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
     for (int j = 0; j < TN; ++j) zb[j] = swz<RB>(wn * C::WN + j * 32 + lrow);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
+      if (kk >= nkk) break;  // nkk == KK (folded) except in a partial last stage
       v4i fa[TM][NQ], fb[TN][NQ];
       // 16-byte chunk(s) of this slice for the lane's half
       const int c0 = FMT == 2 ? kk * 4 + half : kk * 2 + half;
@@ -288,7 +287,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
     constexpr int J = decltype(Jc)::value;
     issue(smem + ((J + NSTG - 1) % NSTG) * C::STAGE, s + NSTG - 1);
     __builtin_amdgcn_sched_barrier(0);
-    compute(smem + J * C::STAGE);
+    compute(smem + J * C::STAGE, T::kKK);
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kAhead) : "memory");
   };
 
@@ -297,19 +296,21 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kAhead) : "memory");
 
   int s = 0;
-  for (; s + NSTG <= nk; s += NSTG) {
+  for (; s + NSTG <= nfull; s += NSTG) {
     step(std::integral_constant<int, 0>{}, s);
     step(std::integral_constant<int, 1>{}, s + 1);
     if constexpr (NSTG > 2) step(std::integral_constant<int, 2>{}, s + 2);
     if constexpr (NSTG > 3) step(std::integral_constant<int, 3>{}, s + 3);
   }
-  if (s < nk) step(std::integral_constant<int, 0>{}, s++);
+  if (s < nfull) step(std::integral_constant<int, 0>{}, s++);
   if constexpr (NSTG > 2) {
-    if (s < nk) step(std::integral_constant<int, 1>{}, s++);
+    if (s < nfull) step(std::integral_constant<int, 1>{}, s++);
   }
   if constexpr (NSTG > 3) {
-    if (s < nk) step(std::integral_constant<int, 2>{}, s++);
+    if (s < nfull) step(std::integral_constant<int, 2>{}, s++);
   }
+  // a partial last stage: already loaded (the previous wait covered it)
+  if (tail_kk > 0) compute(smem + (nfull % NSTG) * C::STAGE, tail_kk);
   // past-end loads may still be landing in LDS that the epilogue reuses
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 
@@ -412,16 +413,13 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
   }
 }
 
-// The pipelined path applies when K is a whole number of 64-byte stages
-// (128-byte ones for MXFP8, whose scale rows must be whole dwords) and one
-// tile's operand rows fit a 32-bit buffer range.  128-byte stages are used
-// when K allows.
+// The pipelined path applies when K is a whole number of MFMA slices whose
+// stage scales are whole dwords in every row (K % 128 for MXFP4 and MXFP8,
+// any K % 32 for BF16) and one tile's operand rows fit a 32-bit buffer
+// range.
 static int pipe_row_bytes(int fmt, int64_t K) {
-  const int64_t e128 = fmt == 1 ? 256 : (fmt == 2 ? 128 : 64);
-  const int64_t e64 = fmt == 1 ? 128 : (fmt == 2 ? 0 : 32);
-  if (K % e128 == 0) return 128;
-  if (e64 && K % e64 == 0) return 64;
-  return 0;
+  const int64_t q = fmt == 3 ? 32 : 128;
+  return K % q == 0 ? 128 : 0;
 }
 
 bool gemm_pipe_supported(int fmt, int64_t M, int64_t N, int64_t K) {
@@ -442,15 +440,12 @@ static hipError_t launch_pipe_t(const void* a, const uint8_t* as, const void* w,
 template <int FMT, int EPI, int RB>
 static hipError_t launch_pipe_r(const void* a, const uint8_t* as, const void* w, const uint8_t* ws, int64_t M,
                                 int64_t N, int64_t K, void* y, hipStream_t stream) {
-  // 256 x 256 tiles (eight waves, 64-byte stages four deep or 128-byte ones
-  // double-buffered) when they fill the 256 CUs at least once.  Otherwise
-  // 128 x 128 tiles: three 128-byte stages when one workgroup per CU covers
-  // every tile, else two so that two workgroups share a CU; 64-byte stages
-  // always four deep.
+  // 256 x 256 tiles (eight waves, two stages) when they fill the 256 CUs at
+  // least once.  Otherwise 128 x 128 tiles: three stages when one workgroup
+  // per CU covers every tile, else two so that two workgroups share a CU.
   const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
-  if (big >= 256) return launch_pipe_t<FMT, EPI, 256, 256, RB, 2, 4, RB == 128 ? 2 : 4>(a, as, w, ws, M, N, K, y, stream);
+  if (big >= 256) return launch_pipe_t<FMT, EPI, 256, 256, RB, 2, 4, 2>(a, as, w, ws, M, N, K, y, stream);
   const int64_t small = ((M + 127) / 128) * ((N + 127) / 128);
-  if (RB == 64) return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 2, 4>(a, as, w, ws, M, N, K, y, stream);
   if (small <= 256) return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 2, 3>(a, as, w, ws, M, N, K, y, stream);
   return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 2, 2>(a, as, w, ws, M, N, K, y, stream);
 }
@@ -458,12 +453,7 @@ static hipError_t launch_pipe_r(const void* a, const uint8_t* as, const void* w,
 template <int FMT, int EPI>
 static hipError_t launch_pipe_e(const void* a, const uint8_t* as, const void* w, const uint8_t* ws, int64_t M,
                                 int64_t N, int64_t K, void* y, hipStream_t stream) {
-  if constexpr (FMT == 2) {
-    return launch_pipe_r<FMT, EPI, 128>(a, as, w, ws, M, N, K, y, stream);
-  } else {
-    if (pipe_row_bytes(FMT, K) == 128) return launch_pipe_r<FMT, EPI, 128>(a, as, w, ws, M, N, K, y, stream);
-    return launch_pipe_r<FMT, EPI, 64>(a, as, w, ws, M, N, K, y, stream);
-  }
+  return launch_pipe_r<FMT, EPI, 128>(a, as, w, ws, M, N, K, y, stream);
 }
 
 template <int FMT>

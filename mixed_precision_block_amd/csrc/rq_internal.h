@@ -22,8 +22,8 @@ enum Epilogue {
 hipError_t launch_gemm(int fmt, int epi, const void* a, const uint8_t* a_scales, const void* w,
                        const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y,
                        hipStream_t stream);
-// The general kernel (any K % 32 == 0) and the pipelined one (K a whole
-// number of 64-byte stages).
+// The general kernel (any K % 32 == 0) and the pipelined one (K % 128 == 0
+// for MXFP4 / MXFP8, K % 32 == 0 for BF16).
 hipError_t launch_gemm_basic(int fmt, int epi, const void* a, const uint8_t* a_scales, const void* w,
                              const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y,
                              hipStream_t stream);

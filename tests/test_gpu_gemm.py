@@ -102,11 +102,12 @@ def test_scale_association_every_block(fmt, ofmt, M, N, K):
 
 
 @pytest.mark.parametrize("fmt,ofmt", MX + [(L.RQ_BF16, None)])
-@pytest.mark.parametrize("M,N,K", [(4000, 4100, 384), (4096, 4096, 128), (3969, 4097, 1152)])
+@pytest.mark.parametrize("M,N,K", [(4000, 4100, 384), (4096, 4096, 128), (3969, 4097, 1152), (4096, 4096, 160)])
 def test_large_tiles_ragged_sampled(fmt, ofmt, M, N, K):
     """Shapes with at least 256 tiles of 256 x 256 (the large-tile path),
-    ragged in M and N, K of one stage, an odd number of stages and a long
-    tail; the oracle runs on sampled rows that include the last one."""
+    ragged in M and N, K of one stage, an odd number of stages, a long tail
+    and K ending in a partial stage (MXFP4 at 384 and 1152, BF16 at 160);
+    the oracle runs on sampled rows that include the last one."""
     rng = np.random.default_rng(M + 3 * N + K)
     a = F.f64_to_bf16(rng.standard_t(3, (M, K)))
     w = F.f64_to_bf16(rng.normal(0, 0.02, (N, K)))
