@@ -340,10 +340,21 @@ def measure_rows(torch, np, api, L, W, to_dev, dev):
 
     # ---- recurrent prefill, 4096 x 2048, FFN 5632, 8 steps
     rows.update(measure_ramp(torch, api, L, W, to_dev, dev, time_calls))
+    rows["recurrent_prefill_schedule_study"] = measure_ramp_study(torch, np, api, L, W, to_dev, dev, time_calls)
 
     # ---- nibble GEMV: weights drawn on the GPU with the same recipe
     rows.update(measure_gemv(torch, np, api, L, W, dev))
     return rows
+
+
+_C4 = {}
+
+
+def c4_block(W, tied=False):
+    """The recurrent block's inputs, generated once per run."""
+    if tied not in _C4:
+        _C4[tied] = W.c4_ramp(tied=tied)
+    return _C4[tied]
 
 
 def measure_ramp(torch, api, L, W, to_dev, dev, time_calls):
@@ -398,7 +409,7 @@ def measure_ramp(torch, api, L, W, to_dev, dev, time_calls):
         log(f"rows: RAMP {tag} {res}")
         return res, (h0, w1, w2, wsp, wsb, h)
 
-    res, (h0, w1, w2, wsp, wsb, h) = run_block(W.c4_ramp(), "random W", True)
+    res, (h0, w1, w2, wsp, wsb, h) = run_block(c4_block(W), "random W", True)
     res["ramp_speedup_vs_all_bf16"] = round(res["all_bf16"]["ms"] / res["ramp_steps1_6_mxfp4"]["ms"], 4)
     out["recurrent_prefill_4096x2048_ffn5632_r8"] = res
 
@@ -425,8 +436,73 @@ def measure_ramp(torch, api, L, W, to_dev, dev, time_calls):
     log(f"rows: RAMP T=32 K=24 MXFP8 {r32}")
     del h0, w1, w2, wsp, h, w1q8, w2q8, wsp8, finals
 
-    tied, _ = run_block(W.c4_ramp(tied=True), "tied W2 = -W1^T", False)
+    tied, _ = run_block(c4_block(W, True), "tied W2 = -W1^T", False)
     out["recurrent_prefill_tied_contractive_r8"] = tied
+    return out
+
+
+def measure_ramp_study(torch, np, api, L, W, to_dev, dev, time_calls):
+    """Fixed-budget schedule study of the 8-step recurrent prefill (MXFP4):
+    the switch point (steps 1..k quantized, BF16 after) for k = 0..8;
+    twenty seeded random schedules with six of eight steps quantized (the
+    RAMP budget) against RAMP's steps 1-6, on the random-weight and on the
+    tied, contractive block; and RAMP's speedup over all-BF16 as the
+    sequence grows from 128 to 4096 tokens."""
+    S, D, F = 4096, 2048, 5632
+    rng = np.random.default_rng(20261205)
+    masks = []
+    while len(masks) < 20:
+        m = int(sum(1 << int(b) for b in rng.choice(8, 6, replace=False)))
+        if m != 0x3F and m not in masks:
+            masks.append(m)
+    out = {"random_schedules": [f"0x{m:02X}" for m in masks]}
+    for tag, d in (("random_w", c4_block(W)), ("tied_contractive", c4_block(W, True))):
+        h0 = to_dev(d["h0"])
+        w1, w2 = to_dev(d["w1"]), to_dev(d["w2"])
+        w1q, w2q = api.quantize(w1, L.RQ_MXFP4), api.quantize(w2, L.RQ_MXFP4)
+        wsb = L.rq_recurrent_prefill_workspace_bytes(S, D, F, L.RQ_MXFP4)
+        wsp = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        h = torch.empty_like(h0)
+
+        def final(sched):
+            h.copy_(h0)
+            L.rq_recurrent_prefill(h, S, D, F, w1, w2, w1q[0], w1q[1], w2q[0], w2q[1], L.RQ_MXFP4, sched, 8, 1e-6,
+                                   wsp, wsb)
+            return h.view(torch.bfloat16).float().clone()
+
+        ref = final(0)
+
+        def err(sched):
+            return float((final(sched) - ref).norm() / ref.norm())
+
+        r = {"switch_point_err": [round(err((1 << k) - 1), 5) for k in range(9)]}
+        e_ramp = err(0x3F)
+        e_rand = sorted(err(m) for m in masks)
+        r["ramp_steps1_6_err"] = round(e_ramp, 5)
+        r["random_6_of_8_err_min_median_max"] = [round(e_rand[0], 5), round(e_rand[10], 5), round(e_rand[-1], 5)]
+        r["random_schedules_below_ramp"] = sum(e < e_ramp for e in e_rand)
+        out[tag] = r
+        del h0, w1, w2, w1q, w2q, wsp, h, ref
+    # sequence sweep on the random-weight block: the token-wise block's cost
+    # scales with S, the weight quantization is done once outside
+    d = c4_block(W)
+    w1, w2 = to_dev(d["w1"]), to_dev(d["w2"])
+    w1q, w2q = api.quantize(w1, L.RQ_MXFP4), api.quantize(w2, L.RQ_MXFP4)
+    sweep = {}
+    for s_tok in (128, 256, 512, 1024, 2048, 4096):
+        h0 = to_dev(d["h0"][:s_tok])
+        h = torch.empty_like(h0)
+        wsb = L.rq_recurrent_prefill_workspace_bytes(s_tok, D, F, L.RQ_MXFP4)
+        wsp = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+        t = {}
+        for name, sched in (("all_bf16", 0x00), ("ramp", 0x3F)):
+            t[name] = time_calls(torch, lambda sched=sched: L.rq_recurrent_prefill(
+                h, s_tok, D, F, w1, w2, w1q[0], w1q[1], w2q[0], w2q[1], L.RQ_MXFP4, sched, 8, 1e-6, wsp, wsb),
+                5, warmup=1, before=lambda: h.copy_(h0))
+        sweep[str(s_tok)] = {"all_bf16_ms": round(t["all_bf16"], 3), "ramp_ms": round(t["ramp"], 3),
+                             "speedup": round(t["all_bf16"] / t["ramp"], 3)}
+    out["sequence_sweep_r8"] = sweep
+    log(f"rows: RAMP schedule study {out}")
     return out
 
 
