@@ -23,8 +23,20 @@ Readings where the page leaves a step open:
   page's extra "significant precision gap" criterion has no threshold, so
   it is not applied.  Ties in amax go to the lower channel index; the order
   of idx is the order of the appended channels.
-* No channel reordering of the primary blocks (the page reorders before the
-  primary stage; here the primary stage keeps the original order).
+* Two arrangements are built.  augment_activations keeps the original
+  channel order for the primary blocks and appends the selected channels'
+  residuals (the gather form).  frontend follows the page's fused kernel
+  ("Kernel Implementatie": channel reorder, RMSNorm, primary and residual
+  quantization in one pass): channels are first permuted by descending
+  amax (ties to the lower index), so the S selected channels are the first
+  S positions, and the appended residual blocks are those positions'
+  residuals.  The "interleaved channel layout ready for the GEMM" is read
+  as this reordered [primary | residual] row, the layout the augmented GEMM
+  consumes; the weights take the same permutation and the duplicated first
+  S columns (frontend with append "copy").
+* RMSNorm in the front end is the one of the recurrent block: eps, no gain,
+  the normalized value rounded to BF16 before quantization.  The amax
+  ranking for the permutation is taken on the normalized activations.
 * The residual r = x - deq(Q(x)) is formed exactly; it is always a BF16
   value (checked), so keeping it in BF16 loses nothing.
 * Appended channels form their own blocks of 32 consecutive j (j indexes
@@ -38,6 +50,7 @@ import numpy as np
 from . import formats as F
 from . import quant as Q
 from . import gemm as G
+from . import ramp as R
 
 
 def select_outlier_channels(x_bits, S):
@@ -100,3 +113,38 @@ def arc_errors(a_bits, w_bits, idx, fmt=F.FMT_MXFP4):
     wc, ws = Q.quantize_mx(w_bits, fmt)
     y_plain = G.gemm_mx(ac, as_, wc, ws, fmt)
     return G.rel_frobenius(y_arc, ref), G.rel_frobenius(y_plain, ref)
+
+
+def reorder_permutation(x_bits):
+    """perm[j] = the channel placed at position j: all K channels by
+    descending max_m |x[m, k]|, ties -> lower k (so perm[:S] is the top-S
+    selection)."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    return select_outlier_channels(x_bits, x_bits.shape[1])
+
+
+def rmsnorm_bits(h_bits, eps=R.EPS):
+    """n = bf16(h / sqrt(mean(h^2) + eps)) per row, no gain."""
+    return F.f64_to_bf16(R.rmsnorm(F.bf16_to_f64(h_bits), eps))
+
+
+def frontend(h_bits, perm, S, fmt=F.FMT_MXFP4, append="residual", rmsnorm=True, eps=R.EPS):
+    """The fused front end, step by step:
+    1. n = rmsnorm_bits(h) (or h itself when rmsnorm is False);
+    2. x = n[:, perm] -- the outlier channels move to the first S positions;
+    3. primary: block quantization of x over K;
+    4. appended S channels: "residual" -> Q(x - deq(Q(x))) of positions
+       0..S-1 (activations), "copy" -> Q(x) of positions 0..S-1 (weights).
+    Returns codes [rows, K+S] (unpacked) and scales [rows, (K+S)/32]."""
+    h_bits = np.asarray(h_bits, dtype=np.uint16)
+    perm = np.asarray(perm, dtype=np.int64)
+    if sorted(perm.tolist()) != list(range(h_bits.shape[1])):
+        raise ValueError("perm must be a permutation of the K channels")
+    n = rmsnorm_bits(h_bits, eps) if rmsnorm else h_bits
+    x = n[:, perm]
+    first = np.arange(S)
+    if append == "residual":
+        return augment_activations(x, first, fmt)
+    if append == "copy":
+        return augment_weights(x, first, fmt)
+    raise ValueError(append)
