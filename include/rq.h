@@ -112,6 +112,46 @@ rq_status rq_select_channels(const uint16_t *amax_bf16, int64_t K, int64_t S,
                              int32_t *idx);
 
 /*
+ * rq_arc_frontend -- the fused ARC front end: channel reorder, RMSNorm,
+ * primary and residual quantization in one pass, producing the augmented
+ * row the GEMM consumes (ARCQuant page, technical summary, "Kernel
+ * Implementatie", with the stages of "Methodologie").
+ *   n = rmsnorm ? bf16(x / sqrt(mean(x^2) + eps)) : x   per row, no gain
+ *       (the RMSNorm of the recurrent block, RAMP page section 4.2; fp32
+ *       sum of squares, the same values as rq_rmsnorm)
+ *   p[j] = n[perm[j]]                    j < K (perm[j] outside [0, K) reads 0)
+ *   codes/scales[:, 0:K]   = Q(p)         primary blocks
+ *   codes/scales[:, K:K+S] = Q(p[:S] - deq(Q(p))[:S])   RQ_APPEND_RESIDUAL
+ *                          = Q(p[:S])                   RQ_APPEND_COPY
+ * With perm ordering the channels by descending calibration amax
+ * (rq_select_channels with S = K), p[:S] are the S outlier channels, so
+ * the residual blocks need no gather.  Activations take
+ * RQ_APPEND_RESIDUAL; the weights W' for the same perm take RQ_APPEND_COPY
+ * with rmsnorm = 0, and rq_gemm over K + S multiplies them.
+ * x_bf16 [rows x K] BF16; perm [K] int32 (device, 16-byte aligned);
+ * codes [rows x (K+S)] elements (FP4 packed two per byte), scales
+ * [rows x (K+S)/32] E8M0.  fmt RQ_MXFP4 / RQ_MXFP8.  append
+ * RQ_APPEND_NONE exactly when S == 0.  rmsnorm 0 or 1, eps finite >= 0.
+ * 0 < K <= 16384 (the row is staged in LDS), K % 32 == 0, 0 <= S <= K,
+ * S % 32 == 0.  x, perm, codes 16-byte aligned.
+ */
+rq_status rq_arc_frontend(const void *x_bf16, int64_t rows, int64_t K,
+                          const int32_t *perm, int64_t S, int fmt, int append,
+                          int rmsnorm, float eps, void *codes, uint8_t *scales,
+                          void *stream);
+
+/*
+ * rq_rmsnorm -- out = bf16(h / sqrt(mean(h^2) + eps)) per row, no gain: the
+ * normalization of the recurrent block (RAMP page, section 4.2; BF16 around
+ * the contractions), used inside rq_recurrent_prefill and for calibrating
+ * the ARC channel order on normalized activations.  fp32 sum of squares
+ * in a fixed order.  h_bf16, out_bf16 [rows x D] BF16, D % 8 == 0, 16-byte
+ * aligned; eps finite >= 0.
+ */
+rq_status rq_rmsnorm(const void *h_bf16, int64_t rows, int64_t D, float eps,
+                     void *out_bf16, void *stream);
+
+/*
  * rq_gemm -- Y[M x N] = A . W^T with FP32 accumulation.
  *
  * Defines: the unified block-scaled GEMM of the ARCQuant page (technical

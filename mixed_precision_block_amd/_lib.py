@@ -51,6 +51,8 @@ _SIGNATURES = {
     "rq_quantize": (_INT, [_P, _I64, _I64, _INT, _P, _I64, _INT, _P, _P, _P]),
     "rq_channel_amax": (_INT, [_P, _I64, _I64, _P, _P]),
     "rq_select_channels": (_INT, [_P, _I64, _I64, _P]),
+    "rq_arc_frontend": (_INT, [_P, _I64, _I64, _P, _I64, _INT, _INT, _INT, _F, _P, _P, _P]),
+    "rq_rmsnorm": (_INT, [_P, _I64, _I64, _F, _P, _P]),
     "rq_gemm": (_INT, [_INT, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _P, _P]),
     "rq_gemm_arc_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "rq_gemm_arc": (_INT, [_P, _I64, _I64, _P, _I64, _P, _P, _I64, _P, _SZ, _INT, _P, _P]),
@@ -126,6 +128,15 @@ def rq_channel_amax(x, rows, K, amax, stream=None):
 def rq_select_channels(amax_host, K, S, idx_host):
     """amax_host / idx_host: CPU tensors or host addresses."""
     _check("rq_select_channels", lib().rq_select_channels(_ptr(amax_host), K, S, _ptr(idx_host)))
+
+
+def rq_arc_frontend(x, rows, K, perm, S, fmt, append, rmsnorm, eps, codes, scales, stream=None):
+    _check("rq_arc_frontend", lib().rq_arc_frontend(_ptr(x), rows, K, _ptr(perm), S, fmt, append, rmsnorm, eps,
+                                                    _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def rq_rmsnorm(h, rows, D, eps, out, stream=None):
+    _check("rq_rmsnorm", lib().rq_rmsnorm(_ptr(h), rows, D, eps, _ptr(out), _stream(stream)))
 
 
 def rq_gemm(fmt, a, a_scales, w, w_scales, M, N, K, out, y, stream=None):

@@ -44,6 +44,33 @@ def select_channels(amax, S):
     return idx
 
 
+def arc_frontend(x, perm, S, fmt=L.RQ_MXFP4, append=L.RQ_APPEND_RESIDUAL, rmsnorm=True, eps=1e-6, stream=None):
+    """x [rows, K] BF16, perm [K] int32 on the device -> (codes, scales) of the
+    reordered, optionally normalized row with S appended channels."""
+    rows, K = x.shape
+    if S == 0:
+        append = L.RQ_APPEND_NONE
+    Kp = K + S
+    codes = _u8((rows, code_bytes(fmt, Kp)), x.device)
+    scales = _u8((rows, Kp // 32), x.device)
+    L.rq_arc_frontend(x, rows, K, perm, S, fmt, append, 1 if rmsnorm else 0, eps, codes, scales, stream)
+    return codes, scales
+
+
+def rmsnorm(h, eps=1e-6, stream=None):
+    rows, D = h.shape
+    out = torch.empty_like(h)
+    L.rq_rmsnorm(h, rows, D, eps, out, stream)
+    return out
+
+
+def reorder_permutation(x, stream=None):
+    """All channels by descending amax of x (ties to the lower index), as a
+    device int32 tensor."""
+    K = x.shape[1]
+    return select_channels(channel_amax(x, stream), K).to(x.device)
+
+
 def gemm(fmt, a, a_scales, w, w_scales, K, out=L.RQ_OUT_BF16, stream=None):
     M, N = a.shape[0], w.shape[0]
     dt = torch.float32 if out == L.RQ_OUT_F32 else torch.bfloat16

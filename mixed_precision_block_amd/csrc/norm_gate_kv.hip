@@ -7,34 +7,10 @@
 //    article, setup paragraph);
 //  * FP8 per-token-head-tile-128 KV quantize-on-write (Day-0 page, section
 //    III.3.3 with the section V listing's amax/448 scale).
-#include "rq_cvt.h"
-#include "rq_device.h"
+#include "rq_block.h"
 #include "rq_internal.h"
 
 namespace rq {
-
-__device__ __forceinline__ uint32_t quad_max_u(uint32_t m) {
-  m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));
-  m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false));
-  return m;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
-// Sum over a 256-thread block in a fixed order (lanes by butterfly, then
-// waves 0..3).
-__device__ __forceinline__ float block_sum(float v, float* sh) {
-  v = wave_sum(v);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) sh[wave] = v;
-  __syncthreads();
-  return ((sh[0] + sh[1]) + sh[2]) + sh[3];
-}
 
 // One workgroup per row.  FMT 3: BF16 output; FMT 1/2: MX codes + scales
 // (four consecutive threads own one 32-element block).
@@ -75,7 +51,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict
       uint32_t m = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) m = max(m, v[i] & 0x7FFFu);
-      m = quad_max_u(m);  // the quad is active together: chunks % 4 == 0
+      m = quad_max(m);  // the quad is active together: chunks % 4 == 0
       const uint32_t sb = (uint32_t)(mx_block_exp<Fm>(m) + 127);
       const uint4 pk = make_uint4(v[0] | v[1] << 16, v[2] | v[3] << 16, v[4] | v[5] << 16, v[6] | v[7] << 16);
       if constexpr (FMT == 1)

@@ -14,38 +14,10 @@
 // element encode is the hardware scaled conversion (rq_cvt.h), four
 // instructions per lane.  Loads and stores of a wave are contiguous (1 KiB
 // of BF16 in, 256 B / 512 B of codes out).  HBM-bound.
-#include "rq_cvt.h"
-#include "rq_device.h"
+#include "rq_block.h"
 #include "rq_internal.h"
 
 namespace rq {
-
-__device__ __forceinline__ uint32_t quad_max(uint32_t m) {
-  // quad_perm [1,0,3,2] then [2,3,0,1]
-  m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));
-  m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false));
-  return m;
-}
-
-// Encode 8 BF16 values (packed two per dword, element 2i in the low half of
-// dword i) with block scale byte sb and store them: FP4 -> one dword
-// (element 2j in the low nibble of byte j), FP8 -> two dwords.
-template <class Fmt>
-__device__ __forceinline__ void encode_store8(uint4 q, uint32_t sb, uint8_t* dst) {
-  const float scale = e8m0_to_f32(sb);
-  if constexpr (Fmt::kMantBits == 1)
-    *reinterpret_cast<uint32_t*>(dst) = cvt8_e2m1(q, scale);
-  else
-    *reinterpret_cast<uint2*>(dst) = cvt8_e4m3(q, scale);
-}
-
-__device__ __forceinline__ uint32_t amax8(uint4 q) {
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) m = max(m, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
-  return m;
-}
 
 // Rows are cut into segments of 64 chunks (512 elements); wave u of the
 // grid owns segment u % segs of row u / segs.
@@ -114,6 +86,89 @@ __global__ __launch_bounds__(256) void quant_append_kernel(const uint16_t* __res
   if ((c & 3) == 0) scales[row * lds + (K >> 5) + (c >> 2)] = (uint8_t)sb;
 }
 
+// ARCQuant fused front end (ARCQuant page, technical summary, "Kernel
+// Implementatie" with the stages of "Methodologie"): one workgroup per row.
+// The row is staged in LDS.  With kNorm its mean square is summed in fp32 in
+// the order of rmsnorm_kernel, and every element is scaled by
+// 1 / sqrt(ms + eps) and rounded to BF16 as it is gathered, so the
+// normalized values equal rmsnorm_kernel's.  Output position j takes
+// channel perm[j] (out-of-range entries read as 0).  Primary blocks cover
+// positions 0..K-1; the first S positions (the outlier channels after an
+// amax reorder) also fill appended block j / 32 + K / 32: the residual
+// against the primary stage (kResidual; exact, see quant_append_kernel) or
+// the value itself.
+template <class Fmt, bool kResidual, bool kNorm>
+__global__ __launch_bounds__(256) void arc_frontend_kernel(const uint16_t* __restrict__ x, int64_t K,
+                                                           const int32_t* __restrict__ perm, int64_t S, float eps,
+                                                           uint8_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ scales) {
+  extern __shared__ uint4 row_lds[];  // the row, K / 8 chunks of BF16
+  __shared__ float sh[4];
+  constexpr int kElemBytesNum = Fmt::kMantBits == 1 ? 1 : 2;  // bytes per 2 elements
+  const int64_t row = blockIdx.x;
+  const int chunks = (int)(K >> 3);
+  const int64_t ldc = (K + S) / 2 * kElemBytesNum, lds = (K + S) >> 5;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + row * K);
+  float ss = 0.0f;
+  for (int c = threadIdx.x; c < chunks; c += 256) {
+    const uint4 q = xr[c];
+    row_lds[c] = q;
+    if constexpr (kNorm) {
+      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = bf16_to_f32(w[i] & 0xFFFFu), b = bf16_to_f32(w[i] >> 16);
+        ss = fmaf(a, a, ss);
+        ss = fmaf(b, b, ss);
+      }
+    }
+  }
+  float inv = 1.0f;
+  if constexpr (kNorm)
+    inv = 1.0f / sqrtf(block_sum(ss, sh) / (float)K + eps);  // block_sum's barriers publish row_lds
+  else
+    __syncthreads();
+  const uint16_t* rh = reinterpret_cast<const uint16_t*>(row_lds);
+  const int s_chunks = (int)(S >> 3);
+  // chunks and s_chunks are multiples of 4 and the stride is 256, so the
+  // four lanes of a quad (one 32-block) take the same branches
+  for (int c = threadIdx.x; c < chunks; c += 256) {
+    const int4 p0 = reinterpret_cast<const int4*>(perm)[2 * c];
+    const int4 p1 = reinterpret_cast<const int4*>(perm)[2 * c + 1];
+    const int32_t p[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    uint32_t v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t b = (p[i] >= 0 && p[i] < K) ? (uint32_t)rh[p[i]] : 0u;
+      if constexpr (kNorm) b = f32_to_bf16(bf16_to_f32(b) * inv);
+      v[i] = b;
+    }
+    const uint4 q = pack8(v);
+    const uint32_t sb = (uint32_t)(mx_block_exp<Fmt>(quad_max(amax8(q))) + 127);
+    encode_store8<Fmt>(q, sb, codes + row * ldc + (int64_t)c * 4 * kElemBytesNum);
+    if ((c & 3) == 0) scales[row * lds + (c >> 2)] = (uint8_t)sb;
+    if (c < s_chunks) {
+      uint32_t r[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if constexpr (kResidual) {
+          const int ep = (int)sb - 127;
+          const uint32_t code = mx_encode<Fmt>(v[i], ep);
+          float dq = __builtin_ldexpf(mx_mag_value<Fmt>(code & ((1u << Fmt::kSignShift) - 1u)), ep);
+          if (code >> Fmt::kSignShift) dq = -dq;
+          r[i] = __builtin_bit_cast(uint32_t, bf16_to_f32(v[i]) - dq) >> 16;  // exact: a BF16 value
+        } else {
+          r[i] = v[i];
+        }
+      }
+      const uint4 q2 = pack8(r);
+      const uint32_t sb2 = (uint32_t)(mx_block_exp<Fmt>(quad_max(amax8(q2))) + 127);
+      encode_store8<Fmt>(q2, sb2, codes + row * ldc + (K + (int64_t)c * 8) / 2 * kElemBytesNum);
+      if ((c & 3) == 0) scales[row * lds + (K >> 5) + (c >> 2)] = (uint8_t)sb2;
+    }
+  }
+}
+
 // Column amax: a workgroup owns 64 channels; its four waves stride over the
 // rows (a wave reads 128 contiguous bytes per row), then combine in LDS.
 __global__ __launch_bounds__(256) void channel_amax_kernel(const uint16_t* __restrict__ x, int64_t rows,
@@ -162,6 +217,31 @@ hipError_t launch_quant_append(int fmt, int mode, const uint16_t* x, int64_t row
       quant_append_kernel<FmtE4M3, false><<<g, 256, 0, stream>>>(x, rows, K, idx, S, codes, scales, ldc, lds);
   }
   return hipGetLastError();
+}
+
+template <class Fmt>
+static hipError_t launch_frontend_f(int mode, bool norm, const uint16_t* x, int64_t rows, int64_t K,
+                                    const int32_t* perm, int64_t S, float eps, uint8_t* codes, uint8_t* scales,
+                                    hipStream_t stream) {
+  const size_t shm = (size_t)K * 2;
+  const unsigned g = (unsigned)rows;
+  if (mode == 1 && norm)
+    arc_frontend_kernel<Fmt, true, true><<<g, 256, shm, stream>>>(x, K, perm, S, eps, codes, scales);
+  else if (mode == 1)
+    arc_frontend_kernel<Fmt, true, false><<<g, 256, shm, stream>>>(x, K, perm, S, eps, codes, scales);
+  else if (norm)
+    arc_frontend_kernel<Fmt, false, true><<<g, 256, shm, stream>>>(x, K, perm, S, eps, codes, scales);
+  else
+    arc_frontend_kernel<Fmt, false, false><<<g, 256, shm, stream>>>(x, K, perm, S, eps, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_arc_frontend(int fmt, int mode, bool norm, const uint16_t* x, int64_t rows, int64_t K,
+                               const int32_t* perm, int64_t S, float eps, uint8_t* codes, uint8_t* scales,
+                               hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  if (fmt == 1) return launch_frontend_f<FmtE2M1>(mode, norm, x, rows, K, perm, S, eps, codes, scales, stream);
+  return launch_frontend_f<FmtE4M3>(mode, norm, x, rows, K, perm, S, eps, codes, scales, stream);
 }
 
 hipError_t launch_channel_amax(const uint16_t* x, int64_t rows, int64_t K, uint16_t* amax,

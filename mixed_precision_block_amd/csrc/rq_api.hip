@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <cmath>
 #include <utility>
 #include <vector>
 
@@ -124,6 +125,41 @@ rq_status rq_select_channels(const uint16_t* amax_bf16, int64_t K, int64_t S, in
   });
   std::copy(order.begin(), order.begin() + S, idx);
   return ok();
+}
+
+rq_status rq_arc_frontend(const void* x_bf16, int64_t rows, int64_t K, const int32_t* perm, int64_t S, int fmt,
+                          int append, int rmsnorm, float eps, void* codes, uint8_t* scales, void* stream) {
+  if (!x_bf16 || !perm || !codes || !scales) return fail(RQ_EINVAL, "rq_arc_frontend: null pointer");
+  if (fmt != RQ_MXFP4 && fmt != RQ_MXFP8) return fail(RQ_EINVAL, "rq_arc_frontend: fmt must be RQ_MXFP4 or RQ_MXFP8");
+  if (append != RQ_APPEND_NONE && append != RQ_APPEND_RESIDUAL && append != RQ_APPEND_COPY)
+    return fail(RQ_EINVAL, "rq_arc_frontend: unknown append mode %d", append);
+  if ((append == RQ_APPEND_NONE) != (S == 0))
+    return fail(RQ_EINVAL, "rq_arc_frontend: RQ_APPEND_NONE exactly when S == 0");
+  if (rmsnorm != 0 && rmsnorm != 1) return fail(RQ_EINVAL, "rq_arc_frontend: rmsnorm must be 0 or 1");
+  if (rmsnorm && !(eps >= 0.0f && eps < INFINITY)) return fail(RQ_EINVAL, "rq_arc_frontend: eps must be finite and >= 0");
+  if (rows < 0 || rows > kInt32Max || K <= 0 || K % 32 || K > 16384 || S < 0 || S % 32 || S > K)
+    return fail(RQ_ESHAPE, "rq_arc_frontend: need 0 <= rows < 2^31, 0 < K <= 16384, K %% 32 == 0, "
+                           "0 <= S <= K, S %% 32 == 0 (rows=%lld K=%lld S=%lld)",
+                (long long)rows, (long long)K, (long long)S);
+  if (!aligned16(x_bf16) || !aligned16(perm) || !aligned16(codes))
+    return fail(RQ_EALIGN, "rq_arc_frontend: x, perm and codes must be 16-byte aligned");
+  if (rq_status s = need_device(); s != RQ_OK) return s;
+  return hip_status(rq::launch_arc_frontend(fmt, append == RQ_APPEND_RESIDUAL ? 1 : (append == RQ_APPEND_COPY ? 2 : 0),
+                                            rmsnorm == 1, static_cast<const uint16_t*>(x_bf16), rows, K, perm, S,
+                                            eps, static_cast<uint8_t*>(codes), scales, as_stream(stream)),
+                    "rq_arc_frontend launch");
+}
+
+rq_status rq_rmsnorm(const void* h_bf16, int64_t rows, int64_t D, float eps, void* out_bf16, void* stream) {
+  if (!h_bf16 || !out_bf16) return fail(RQ_EINVAL, "rq_rmsnorm: null pointer");
+  if (!(eps >= 0.0f && eps < INFINITY)) return fail(RQ_EINVAL, "rq_rmsnorm: eps must be finite and >= 0");
+  if (rows < 0 || rows > kInt32Max || D <= 0 || D % 8)
+    return fail(RQ_ESHAPE, "rq_rmsnorm: need 0 <= rows < 2^31, D > 0, D %% 8 == 0");
+  if (!aligned16(h_bf16) || !aligned16(out_bf16)) return fail(RQ_EALIGN, "rq_rmsnorm: h and out must be 16-byte aligned");
+  if (rq_status s = need_device(); s != RQ_OK) return s;
+  return hip_status(rq::launch_rmsnorm(RQ_BF16, static_cast<const uint16_t*>(h_bf16), rows, D, eps, out_bf16, nullptr,
+                                       as_stream(stream)),
+                    "rq_rmsnorm launch");
 }
 
 rq_status rq_gemm(int fmt, const void* a, const uint8_t* a_scales, const void* w, const uint8_t* w_scales,

@@ -42,6 +42,13 @@ hipError_t launch_quant_rows(int fmt, const uint16_t* x, int64_t rows, int64_t K
 hipError_t launch_quant_append(int fmt, int mode, const uint16_t* x, int64_t rows, int64_t K,
                                const int32_t* idx, int64_t S, uint8_t* codes, uint8_t* scales,
                                int64_t ldc_bytes, int64_t lds_bytes, hipStream_t stream);
+// Fused front end: optional RMSNorm (eps, no gain), reorder by perm,
+// primary block quantization over K, and for positions 0..S-1 an appended
+// block (mode 1 residual, 2 copy; S == 0 for none).  K <= 16384 (the row
+// is staged in LDS).
+hipError_t launch_arc_frontend(int fmt, int mode, bool norm, const uint16_t* x, int64_t rows, int64_t K,
+                               const int32_t* perm, int64_t S, float eps, uint8_t* codes, uint8_t* scales,
+                               hipStream_t stream);
 hipError_t launch_channel_amax(const uint16_t* x, int64_t rows, int64_t K, uint16_t* amax,
                                hipStream_t stream);
 

@@ -172,3 +172,32 @@ def test_gemv_group_plan_and_grouped_validation():
     lowonly[4] = None
     lowonly[5] = L.RQ_LOW
     assert status_of(rq.rq_gemv_nibble_escalate_grouped, *lowonly) in (L.RQ_OK, L.RQ_ENODEV)
+
+
+def test_arc_frontend_and_rmsnorm_validation():
+    R, C = L.RQ_APPEND_RESIDUAL, L.RQ_APPEND_COPY
+    ok = [A16, 4, 4096, A16, 128, L.RQ_MXFP4, R, 1, 1e-6, A16, A16]
+    cases = [
+        (0, None, L.RQ_EINVAL), (3, None, L.RQ_EINVAL), (9, None, L.RQ_EINVAL),
+        (5, L.RQ_BF16, L.RQ_EINVAL), (6, 7, L.RQ_EINVAL), (6, L.RQ_APPEND_NONE, L.RQ_EINVAL),
+        (7, 2, L.RQ_EINVAL), (8, -1.0, L.RQ_EINVAL), (8, float("inf"), L.RQ_EINVAL),
+        (2, 4100, L.RQ_ESHAPE), (2, 16416, L.RQ_ESHAPE), (4, 48, L.RQ_ESHAPE), (4, 4128, L.RQ_ESHAPE),
+        (1, -1, L.RQ_ESHAPE), (0, A16 + 2, L.RQ_EALIGN), (3, A16 + 4, L.RQ_EALIGN), (9, A16 + 8, L.RQ_EALIGN),
+    ]
+    for i, v, want in cases:
+        a = list(ok)
+        a[i] = v
+        assert status_of(rq.rq_arc_frontend, *a) == want, (i, v)
+    none = list(ok)
+    none[4], none[6] = 0, L.RQ_APPEND_NONE
+    copy_no_norm = list(ok)
+    copy_no_norm[6], copy_no_norm[7], copy_no_norm[8] = C, 0, float("nan")  # eps unused without RMSNorm
+    for a in (ok, none, copy_no_norm):
+        assert status_of(rq.rq_arc_frontend, *a) in (L.RQ_OK, L.RQ_ENODEV)
+    r = [A16, 4, 64, 1e-6, A16]
+    for i, v, want in [(0, None, L.RQ_EINVAL), (4, None, L.RQ_EINVAL), (3, -1.0, L.RQ_EINVAL),
+                       (2, 12, L.RQ_ESHAPE), (2, 0, L.RQ_ESHAPE), (0, A16 + 2, L.RQ_EALIGN)]:
+        a = list(r)
+        a[i] = v
+        assert status_of(rq.rq_rmsnorm, *a) == want, (i, v)
+    assert status_of(rq.rq_rmsnorm, *r) in (L.RQ_OK, L.RQ_ENODEV)
