@@ -336,6 +336,7 @@ def measure_rows(torch, np, api, L, W, to_dev, dev):
                                         "frac_hbm": round(qbytes / (ms_q * 1e-3) / PEAK["hbm"], 4)}
     log(f"rows: 4096^3 plain {ms_plain * 1e3:.1f} us, ARC {ms_arc * 1e3:.1f} us, BF16 {ms_bf * 1e3:.1f} us, "
         f"quant {ms_q * 1e3:.1f} us")
+    rows["arc_front_end_4096x4096_s128"] = measure_front_end(torch, api, L, a, w, qc, qs, dev, time_calls)
     del a, w, pc, ps, qc, qs, y, w_aug, wsp
 
     # ---- recurrent prefill, 4096 x 2048, FFN 5632, 8 steps
@@ -345,6 +346,66 @@ def measure_rows(torch, np, api, L, W, to_dev, dev):
     # ---- nibble GEMV: weights drawn on the GPU with the same recipe
     rows.update(measure_gemv(torch, np, api, L, W, dev))
     return rows
+
+
+def measure_front_end(torch, api, L, a, w, qc, qs, dev, time_calls):
+    """The ARC fused front end on config 3's activations read as the hidden
+    state before RMSNorm: channel order calibrated on the normalized rows;
+    the fused pass (RMSNorm + reorder + primary + residual) against RMSNorm
+    followed by the gather-form quantize, alone and with the GEMM over
+    K + S; errors of fused ARC, gather ARC and plain MXFP4 against the BF16
+    product of the normalized rows."""
+    n, S = a.shape[0], 128
+    Kp = n + S
+    nb = torch.empty_like(a)
+    L.rq_rmsnorm(a, n, n, 1e-6, nb)
+    perm = api.reorder_permutation(nb)
+    idx = perm[:S].contiguous()
+    fc = torch.empty((n, Kp // 2), dtype=torch.uint8, device=dev)
+    fs = torch.empty((n, Kp // 32), dtype=torch.uint8, device=dev)
+    gc, gs = torch.empty_like(fc), torch.empty_like(fs)
+    wf = api.arc_frontend(w, perm, S, append=L.RQ_APPEND_COPY, rmsnorm=False)
+    wg = api.quantize(w, L.RQ_MXFP4, idx, L.RQ_APPEND_COPY)
+    y = torch.empty((n, n), dtype=torch.float32, device=dev)
+
+    def fused():
+        L.rq_arc_frontend(a, n, n, perm, S, L.RQ_MXFP4, L.RQ_APPEND_RESIDUAL, 1, 1e-6, fc, fs)
+
+    def unfused():
+        L.rq_rmsnorm(a, n, n, 1e-6, nb)
+        L.rq_quantize(nb, n, n, L.RQ_MXFP4, idx, S, L.RQ_APPEND_RESIDUAL, gc, gs)
+
+    def fused_gemm():
+        fused()
+        L.rq_gemm(L.RQ_MXFP4, fc, fs, wf[0], wf[1], n, n, Kp, L.RQ_OUT_BF16, y)
+
+    ms_f = time_calls(torch, fused, 50)
+    ms_u = time_calls(torch, unfused, 50)
+    ms_fg = time_calls(torch, fused_gemm, 50)
+    ref = torch.empty((n, n), dtype=torch.float32, device=dev)
+    L.rq_gemm(L.RQ_BF16, nb, None, w, None, n, n, n, L.RQ_OUT_F32, ref)
+
+    def rel():
+        return round(float((y - ref).norm() / ref.norm()), 5)
+
+    fused()
+    L.rq_gemm(L.RQ_MXFP4, fc, fs, wf[0], wf[1], n, n, Kp, L.RQ_OUT_F32, y)
+    e_fused = rel()
+    unfused()
+    L.rq_gemm(L.RQ_MXFP4, gc, gs, wg[0], wg[1], n, n, Kp, L.RQ_OUT_F32, y)
+    e_gather = rel()
+    pa = api.quantize(nb, L.RQ_MXFP4)
+    L.rq_gemm(L.RQ_MXFP4, pa[0], pa[1], qc, qs, n, n, n, L.RQ_OUT_F32, y)
+    e_plain = rel()
+    nbytes = n * n * 2 + n * Kp // 2 + n * Kp // 32 + 4 * n
+    out = {"us_fused_front_end": round(ms_f * 1e3, 2), "gb_s": round(nbytes / (ms_f * 1e-3) / 1e9, 1),
+           "frac_hbm": round(nbytes / (ms_f * 1e-3) / PEAK["hbm"], 4), "bytes": nbytes,
+           "us_unfused_rmsnorm_then_quantize_gather": round(ms_u * 1e3, 2),
+           "us_fused_front_end_plus_gemm_kprime4224": round(ms_fg * 1e3, 1),
+           "rel_err_vs_bf16_fused_arc": e_fused, "rel_err_vs_bf16_gather_arc": e_gather,
+           "rel_err_vs_bf16_plain_mxfp4": e_plain}
+    log(f"rows: ARC front end {out}")
+    return out
 
 
 _C4 = {}
