@@ -379,9 +379,20 @@ def measure_front_end(torch, api, L, a, w, qc, qs, dev, time_calls):
         fused()
         L.rq_gemm(L.RQ_MXFP4, fc, fs, wf[0], wf[1], n, n, Kp, L.RQ_OUT_BF16, y)
 
+    # the same pass without ARC (identity order, no appended channels): the
+    # plain normalize-and-quantize front end, then the GEMM over K
+    ident = torch.arange(n, dtype=torch.int32, device=dev)
+    pc = torch.empty((n, n // 2), dtype=torch.uint8, device=dev)
+    pcs = torch.empty((n, n // 32), dtype=torch.uint8, device=dev)
+
+    def plain_gemm():
+        L.rq_arc_frontend(a, n, n, ident, 0, L.RQ_MXFP4, L.RQ_APPEND_NONE, 1, 1e-6, pc, pcs)
+        L.rq_gemm(L.RQ_MXFP4, pc, pcs, qc, qs, n, n, n, L.RQ_OUT_BF16, y)
+
     ms_f = time_calls(torch, fused, 50)
     ms_u = time_calls(torch, unfused, 50)
     ms_fg = time_calls(torch, fused_gemm, 50)
+    ms_pg = time_calls(torch, plain_gemm, 50)
     ref = torch.empty((n, n), dtype=torch.float32, device=dev)
     L.rq_gemm(L.RQ_BF16, nb, None, w, None, n, n, n, L.RQ_OUT_F32, ref)
 
@@ -402,6 +413,8 @@ def measure_front_end(torch, api, L, a, w, qc, qs, dev, time_calls):
            "frac_hbm": round(nbytes / (ms_f * 1e-3) / PEAK["hbm"], 4), "bytes": nbytes,
            "us_unfused_rmsnorm_then_quantize_gather": round(ms_u * 1e3, 2),
            "us_fused_front_end_plus_gemm_kprime4224": round(ms_fg * 1e3, 1),
+           "us_plain_front_end_plus_gemm_k4096": round(ms_pg * 1e3, 1),
+           "arc_overhead_vs_plain": round(ms_fg / ms_pg - 1, 4),
            "rel_err_vs_bf16_fused_arc": e_fused, "rel_err_vs_bf16_gather_arc": e_gather,
            "rel_err_vs_bf16_plain_mxfp4": e_plain}
     log(f"rows: ARC front end {out}")

@@ -14,6 +14,8 @@
 // element encode is the hardware scaled conversion (rq_cvt.h), four
 // instructions per lane.  Loads and stores of a wave are contiguous (1 KiB
 // of BF16 in, 256 B / 512 B of codes out).  HBM-bound.
+#include <algorithm>
+
 #include "rq_block.h"
 #include "rq_internal.h"
 
@@ -87,84 +89,116 @@ __global__ __launch_bounds__(256) void quant_append_kernel(const uint16_t* __res
 }
 
 // ARCQuant fused front end (ARCQuant page, technical summary, "Kernel
-// Implementatie" with the stages of "Methodologie"): one workgroup per row.
-// The row is staged in LDS.  With kNorm its mean square is summed in fp32 in
-// the order of rmsnorm_kernel, and every element is scaled by
-// 1 / sqrt(ms + eps) and rounded to BF16 as it is gathered, so the
-// normalized values equal rmsnorm_kernel's.  Output position j takes
+// Implementatie" with the stages of "Methodologie").  A workgroup owns
+// rows_per_wg consecutive rows and keeps its threads' perm entries in
+// registers across them; thread t owns chunks c = t + 256 i (i < CPT) of
+// every row.  Each row is staged in LDS; with kNorm its mean square is
+// summed in fp32 in the order of rmsnorm_kernel, and every element is
+// scaled by 1 / sqrt(ms + eps) and rounded to BF16 as it is gathered, so
+// the normalized values equal rmsnorm_kernel's.  The next row's loads are
+// issued before the current row is gathered.  Output position j takes
 // channel perm[j] (out-of-range entries read as 0).  Primary blocks cover
 // positions 0..K-1; the first S positions (the outlier channels after an
 // amax reorder) also fill appended block j / 32 + K / 32: the residual
 // against the primary stage (kResidual; exact, see quant_append_kernel) or
 // the value itself.
-template <class Fmt, bool kResidual, bool kNorm>
-__global__ __launch_bounds__(256) void arc_frontend_kernel(const uint16_t* __restrict__ x, int64_t K,
+template <class Fmt, bool kResidual, bool kNorm, int CPT>
+__global__ __launch_bounds__(256) void arc_frontend_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t K,
                                                            const int32_t* __restrict__ perm, int64_t S, float eps,
-                                                           uint8_t* __restrict__ codes,
-                                                           uint8_t* __restrict__ scales) {
-  extern __shared__ uint4 row_lds[];  // the row, K / 8 chunks of BF16
+                                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                           int rows_per_wg) {
+  extern __shared__ uint4 row_lds[];  // one row, K / 8 chunks of BF16
   __shared__ float sh[4];
   constexpr int kElemBytesNum = Fmt::kMantBits == 1 ? 1 : 2;  // bytes per 2 elements
-  const int64_t row = blockIdx.x;
-  const int chunks = (int)(K >> 3);
+  const int chunks = (int)(K >> 3), s_chunks = (int)(S >> 3);
   const int64_t ldc = (K + S) / 2 * kElemBytesNum, lds = (K + S) >> 5;
-  const uint4* xr = reinterpret_cast<const uint4*>(x + row * K);
-  float ss = 0.0f;
-  for (int c = threadIdx.x; c < chunks; c += 256) {
-    const uint4 q = xr[c];
-    row_lds[c] = q;
-    if constexpr (kNorm) {
-      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  const int64_t r0 = (int64_t)blockIdx.x * rows_per_wg;
+  const int64_t r1 = min(rows, r0 + rows_per_wg);
+  int32_t p[CPT][8];
+  uint4 q[CPT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float a = bf16_to_f32(w[i] & 0xFFFFu), b = bf16_to_f32(w[i] >> 16);
-        ss = fmaf(a, a, ss);
-        ss = fmaf(b, b, ss);
-      }
+  for (int i = 0; i < CPT; ++i) {
+    const int c = (int)threadIdx.x + 256 * i;
+    int4 p0 = make_int4(-1, -1, -1, -1), p1 = p0;
+    if (c < chunks) {
+      p0 = reinterpret_cast<const int4*>(perm)[2 * c];
+      p1 = reinterpret_cast<const int4*>(perm)[2 * c + 1];
     }
+    p[i][0] = p0.x, p[i][1] = p0.y, p[i][2] = p0.z, p[i][3] = p0.w;
+    p[i][4] = p1.x, p[i][5] = p1.y, p[i][6] = p1.z, p[i][7] = p1.w;
   }
-  float inv = 1.0f;
-  if constexpr (kNorm)
-    inv = 1.0f / sqrtf(block_sum(ss, sh) / (float)K + eps);  // block_sum's barriers publish row_lds
-  else
-    __syncthreads();
-  const uint16_t* rh = reinterpret_cast<const uint16_t*>(row_lds);
-  const int s_chunks = (int)(S >> 3);
-  // chunks and s_chunks are multiples of 4 and the stride is 256, so the
-  // four lanes of a quad (one 32-block) take the same branches
-  for (int c = threadIdx.x; c < chunks; c += 256) {
-    const int4 p0 = reinterpret_cast<const int4*>(perm)[2 * c];
-    const int4 p1 = reinterpret_cast<const int4*>(perm)[2 * c + 1];
-    const int32_t p[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-    uint32_t v[8];
+  auto load_row = [&](int64_t r) {
+    const uint4* xr = reinterpret_cast<const uint4*>(x + r * K);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t b = (p[i] >= 0 && p[i] < K) ? (uint32_t)rh[p[i]] : 0u;
-      if constexpr (kNorm) b = f32_to_bf16(bf16_to_f32(b) * inv);
-      v[i] = b;
+    for (int i = 0; i < CPT; ++i) {
+      const int c = (int)threadIdx.x + 256 * i;
+      q[i] = c < chunks ? xr[c] : make_uint4(0, 0, 0, 0);
     }
-    const uint4 q = pack8(v);
-    const uint32_t sb = (uint32_t)(mx_block_exp<Fmt>(quad_max(amax8(q))) + 127);
-    encode_store8<Fmt>(q, sb, codes + row * ldc + (int64_t)c * 4 * kElemBytesNum);
-    if ((c & 3) == 0) scales[row * lds + (c >> 2)] = (uint8_t)sb;
-    if (c < s_chunks) {
-      uint32_t r[8];
+  };
+  if (r0 < r1) load_row(r0);
+  const uint16_t* rh = reinterpret_cast<const uint16_t*>(row_lds);
+  for (int64_t row = r0; row < r1; ++row) {
+    __syncthreads();  // the previous row's gathers are done with row_lds
+    float ss = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if constexpr (kResidual) {
-          const int ep = (int)sb - 127;
-          const uint32_t code = mx_encode<Fmt>(v[i], ep);
-          float dq = __builtin_ldexpf(mx_mag_value<Fmt>(code & ((1u << Fmt::kSignShift) - 1u)), ep);
-          if (code >> Fmt::kSignShift) dq = -dq;
-          r[i] = __builtin_bit_cast(uint32_t, bf16_to_f32(v[i]) - dq) >> 16;  // exact: a BF16 value
-        } else {
-          r[i] = v[i];
+    for (int i = 0; i < CPT; ++i) {
+      const int c = (int)threadIdx.x + 256 * i;
+      if (c >= chunks) break;
+      row_lds[c] = q[i];
+      if constexpr (kNorm) {
+        const uint32_t w[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a = bf16_to_f32(w[e] & 0xFFFFu), b = bf16_to_f32(w[e] >> 16);
+          ss = fmaf(a, a, ss);
+          ss = fmaf(b, b, ss);
         }
       }
-      const uint4 q2 = pack8(r);
-      const uint32_t sb2 = (uint32_t)(mx_block_exp<Fmt>(quad_max(amax8(q2))) + 127);
-      encode_store8<Fmt>(q2, sb2, codes + row * ldc + (K + (int64_t)c * 8) / 2 * kElemBytesNum);
-      if ((c & 3) == 0) scales[row * lds + (K >> 5) + (c >> 2)] = (uint8_t)sb2;
+    }
+    float inv = 1.0f;
+    if constexpr (kNorm)
+      inv = 1.0f / sqrtf(block_sum(ss, sh) / (float)K + eps);  // block_sum's barriers publish row_lds
+    else
+      __syncthreads();
+    if (row + 1 < r1) load_row(row + 1);
+    // chunks and s_chunks are multiples of 4, so the four lanes of a quad
+    // (one 32-block) take the same branches
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = (int)threadIdx.x + 256 * i;
+      if (c >= chunks) break;
+      uint32_t v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint32_t b = (p[i][e] >= 0 && p[i][e] < K) ? (uint32_t)rh[p[i][e]] : 0u;
+        if constexpr (kNorm) b = f32_to_bf16(bf16_to_f32(b) * inv);
+        v[e] = b;
+      }
+      const uint4 qv = pack8(v);
+      const uint32_t sb = (uint32_t)(mx_block_exp<Fmt>(quad_max(amax8(qv))) + 127);
+      const uint2 cv = encode8<Fmt>(qv, sb);
+      store8<Fmt>(cv, codes + row * ldc + (int64_t)c * 4 * kElemBytesNum);
+      if ((c & 3) == 0) scales[row * lds + (c >> 2)] = (uint8_t)sb;
+      if (c < s_chunks) {
+        uint32_t r[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if constexpr (kResidual) {
+            // the primary stage's value from its own code (the hardware
+            // conversion's codes are the integer encoder's)
+            const uint32_t code = code_at<Fmt>(cv, e);
+            float dq = __builtin_ldexpf(mx_mag_value<Fmt>(code & ((1u << Fmt::kSignShift) - 1u)), (int)sb - 127);
+            if (code >> Fmt::kSignShift) dq = -dq;
+            r[e] = __builtin_bit_cast(uint32_t, bf16_to_f32(v[e]) - dq) >> 16;  // exact: a BF16 value
+          } else {
+            r[e] = v[e];
+          }
+        }
+        const uint4 q2 = pack8(r);
+        const uint32_t sb2 = (uint32_t)(mx_block_exp<Fmt>(quad_max(amax8(q2))) + 127);
+        encode_store8<Fmt>(q2, sb2, codes + row * ldc + (K + (int64_t)c * 8) / 2 * kElemBytesNum);
+        if ((c & 3) == 0) scales[row * lds + (K >> 5) + (c >> 2)] = (uint8_t)sb2;
+      }
     }
   }
 }
@@ -219,21 +253,35 @@ hipError_t launch_quant_append(int fmt, int mode, const uint16_t* x, int64_t row
   return hipGetLastError();
 }
 
+template <class Fmt, int CPT>
+static hipError_t launch_frontend_c(int mode, bool norm, const uint16_t* x, int64_t rows, int64_t K,
+                                    const int32_t* perm, int64_t S, float eps, uint8_t* codes, uint8_t* scales,
+                                    hipStream_t stream) {
+  // about 2048 workgroups, each over a run of rows (its perm entries stay
+  // in registers)
+  const int rpw = (int)std::max<int64_t>(1, rows / 2048);
+  const unsigned g = (unsigned)((rows + rpw - 1) / rpw);
+  const size_t shm = (size_t)K * 2;
+  if (mode == 1 && norm)
+    arc_frontend_kernel<Fmt, true, true, CPT><<<g, 256, shm, stream>>>(x, rows, K, perm, S, eps, codes, scales, rpw);
+  else if (mode == 1)
+    arc_frontend_kernel<Fmt, true, false, CPT><<<g, 256, shm, stream>>>(x, rows, K, perm, S, eps, codes, scales, rpw);
+  else if (norm)
+    arc_frontend_kernel<Fmt, false, true, CPT><<<g, 256, shm, stream>>>(x, rows, K, perm, S, eps, codes, scales, rpw);
+  else
+    arc_frontend_kernel<Fmt, false, false, CPT><<<g, 256, shm, stream>>>(x, rows, K, perm, S, eps, codes, scales, rpw);
+  return hipGetLastError();
+}
+
 template <class Fmt>
 static hipError_t launch_frontend_f(int mode, bool norm, const uint16_t* x, int64_t rows, int64_t K,
                                     const int32_t* perm, int64_t S, float eps, uint8_t* codes, uint8_t* scales,
                                     hipStream_t stream) {
-  const size_t shm = (size_t)K * 2;
-  const unsigned g = (unsigned)rows;
-  if (mode == 1 && norm)
-    arc_frontend_kernel<Fmt, true, true><<<g, 256, shm, stream>>>(x, K, perm, S, eps, codes, scales);
-  else if (mode == 1)
-    arc_frontend_kernel<Fmt, true, false><<<g, 256, shm, stream>>>(x, K, perm, S, eps, codes, scales);
-  else if (norm)
-    arc_frontend_kernel<Fmt, false, true><<<g, 256, shm, stream>>>(x, K, perm, S, eps, codes, scales);
-  else
-    arc_frontend_kernel<Fmt, false, false><<<g, 256, shm, stream>>>(x, K, perm, S, eps, codes, scales);
-  return hipGetLastError();
+  // chunks per thread: K / 8 chunks over 256 threads
+  if (K <= 2048) return launch_frontend_c<Fmt, 1>(mode, norm, x, rows, K, perm, S, eps, codes, scales, stream);
+  if (K <= 4096) return launch_frontend_c<Fmt, 2>(mode, norm, x, rows, K, perm, S, eps, codes, scales, stream);
+  if (K <= 8192) return launch_frontend_c<Fmt, 4>(mode, norm, x, rows, K, perm, S, eps, codes, scales, stream);
+  return launch_frontend_c<Fmt, 8>(mode, norm, x, rows, K, perm, S, eps, codes, scales, stream);
 }
 
 hipError_t launch_arc_frontend(int fmt, int mode, bool norm, const uint16_t* x, int64_t rows, int64_t K,

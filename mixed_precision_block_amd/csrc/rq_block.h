@@ -49,15 +49,39 @@ __device__ __forceinline__ uint4 pack8(const uint32_t v[8]) {
   return make_uint4(v[0] | v[1] << 16, v[2] | v[3] << 16, v[4] | v[5] << 16, v[6] | v[7] << 16);
 }
 
+// Codes of 8 BF16 values under block scale byte sb: FP4 -> .x (element k
+// in nibble k), FP8 -> .x, .y (element k in byte k).
+template <class Fmt>
+__device__ __forceinline__ uint2 encode8(uint4 q, uint32_t sb) {
+  const float scale = e8m0_to_f32(sb);
+  if constexpr (Fmt::kMantBits == 1)
+    return make_uint2(cvt8_e2m1(q, scale), 0u);
+  else
+    return cvt8_e4m3(q, scale);
+}
+
+// Code of element k of an encode8 result.
+template <class Fmt>
+__device__ __forceinline__ uint32_t code_at(uint2 c, int k) {
+  if constexpr (Fmt::kMantBits == 1)
+    return (c.x >> (4 * k)) & 0xFu;
+  else
+    return ((k < 4 ? c.x : c.y) >> (8 * (k & 3))) & 0xFFu;
+}
+
+template <class Fmt>
+__device__ __forceinline__ void store8(uint2 c, uint8_t* dst) {
+  if constexpr (Fmt::kMantBits == 1)
+    *reinterpret_cast<uint32_t*>(dst) = c.x;
+  else
+    *reinterpret_cast<uint2*>(dst) = c;
+}
+
 // Encode 8 BF16 values with block scale byte sb and store them: FP4 -> one
 // dword (element 2j in the low nibble of byte j), FP8 -> two dwords.
 template <class Fmt>
 __device__ __forceinline__ void encode_store8(uint4 q, uint32_t sb, uint8_t* dst) {
-  const float scale = e8m0_to_f32(sb);
-  if constexpr (Fmt::kMantBits == 1)
-    *reinterpret_cast<uint32_t*>(dst) = cvt8_e2m1(q, scale);
-  else
-    *reinterpret_cast<uint2*>(dst) = cvt8_e4m3(q, scale);
+  store8<Fmt>(encode8<Fmt>(q, sb), dst);
 }
 
 }  // namespace rq

@@ -52,8 +52,11 @@ def expect(h_bits, perm, S, ofmt, mode, rmsnorm, eps=1e-6):
 
 @pytest.mark.parametrize("fmt,ofmt", FMTS)
 @pytest.mark.parametrize("append,mode", MODES)
-@pytest.mark.parametrize("rows,K,S", [(37, 4096, 128), (5, 96, 32), (3, 64, 64)])
+@pytest.mark.parametrize("rows,K,S", [(37, 4096, 128), (5, 96, 32), (3, 64, 64), (3, 16384, 256), (4, 8192, 32),
+                                      (2501, 128, 32)])
 def test_without_rmsnorm_bit_exact(fmt, ofmt, append, mode, rows, K, S):
+    """Every row length class (one to eight chunks per thread), several rows
+    per workgroup with a ragged last one (2501 rows), S from one block to K."""
     rng = np.random.default_rng(rows + K + S)
     h = outlier_rows(rng, rows, K)
     for perm in (A.reorder_permutation(h), rng.permutation(K)):
@@ -64,6 +67,24 @@ def test_without_rmsnorm_bit_exact(fmt, ofmt, append, mode, rows, K, S):
     pc, ps = Q.quantize_mx(h, ofmt)
     assert np.array_equal(c, Q.storage_codes(pc, ofmt)) and np.array_equal(s, ps)
     log(f"front end without RMSNorm fmt={ofmt} {mode} rows={rows} K={K} S={S}: bit-exact")
+
+
+@pytest.mark.parametrize("fmt,ofmt", FMTS)
+@pytest.mark.parametrize("append,mode", MODES)
+def test_without_rmsnorm_extreme_block_exponents(fmt, ofmt, append, mode):
+    """Every 32-channel group scaled by 2^u, u uniform over the BF16 range
+    (subnormal to near the largest finite value), so primary blocks and
+    residuals cover the clamped and subnormal scale bytes."""
+    rng = np.random.default_rng(25)
+    K = 1024
+    x = rng.standard_normal((16, K)) * np.repeat(2.0 ** rng.integers(-140, 120, (16, K // 32)), 32, axis=1)
+    h = F.f64_to_bf16(x)
+    # move whole groups (and shuffle within each), so blocks keep one scale
+    perm = (rng.permutation(K // 32)[:, None] * 32 + rng.permutation(32)[None, :]).ravel()
+    c, s = gpu_frontend(h, perm, 256, fmt, append, False)
+    ec, es = expect(h, perm, 256, ofmt, mode, False)
+    assert es.min() <= 2 and es.max() >= 230  # the scale range is covered
+    assert np.array_equal(s, es) and np.array_equal(c, ec)
 
 
 @pytest.mark.parametrize("fmt,ofmt", FMTS)
