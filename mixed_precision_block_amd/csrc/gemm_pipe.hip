@@ -91,16 +91,16 @@ struct DmaCfg {
   static constexpr int CPR = RB / 16;                 // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;                // rows per wave-wide 16-byte DMA (1 KB)
   static constexpr int IA = BM / RPI, IW = BN / RPI;  // DMAs per stage of the A / W tile
-  static constexpr int DPW = (IA + IW + NW - 1) / NW; // operand DMAs per wave per stage (the last waves may have fewer)
+  static constexpr int DPW = (IA + IW) / NW;          // operand DMAs per wave per stage
   static constexpr int SA = BM * RB, SW = BN * RB;
   static constexpr int SBPR = T::kSBPR;
   static constexpr int SS = (BM + BN) * SBPR;
   static constexpr int IS = SS / 256;                 // dword DMAs of the stage's scales (0 for BF16)
-  static constexpr int SPW = (IS + NW - 1) / NW;
-  static constexpr bool kEven = (IA + IW) % NW == 0 && IS % NW == 0;
+  static constexpr int SPW = IS / NW;
   static constexpr int DW = DPW + SPW;                // DMAs per wave per stage
   static constexpr int STAGE = SA + SW + SS;
-  static_assert(kEven || NSTG == 2, "deeper rings count each wave's loads: even splits only");
+  // every wave issues the same loads per stage, so the load-count waits are exact
+  static_assert((IA + IW) % NW == 0 && IS % NW == 0, "loads split evenly over the waves");
   static_assert(SS % 256 == 0, "whole scale DMAs");
   static_assert((BM * SBPR) % 256 == 0, "a scale DMA stays on one side");
   static_assert(NSTG * STAGE <= 160 * 1024, "stages fit the LDS");
@@ -180,7 +180,6 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
 #pragma unroll
     for (int i = 0; i < C::DPW; ++i) {
       const int q = wave * C::DPW + i;
-      if (!C::kEven && q >= C::IA + C::IW) break;
       const bool is_a = q < C::IA;
       uint8_t* dst = st + (is_a ? q * 1024 : C::SA + (q - C::IA) * 1024);
       load_lds16(is_a ? ra : rw, dst, voff[i] + kb);
@@ -190,7 +189,6 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
 #pragma unroll
       for (int i = 0; i < C::SPW; ++i) {
         const int q = wave * C::SPW + i;
-        if (!C::kEven && q >= C::IS) break;
         const bool is_a = q * 256 < BM * C::SBPR;
         uint8_t* dst = st + C::SA + C::SW + q * 256;
         load_lds4(is_a ? rsa : rsw, dst, soff[i] + sk);
@@ -319,12 +317,15 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
   // tile and column n = 8 (r / 4) + 4 half + r % 4 of the W tile, i.e. four
   // consecutive columns of one output row per group r / 4.  Results go
   // through a per-wave LDS strip of 32 rows (BF16: the quadrant's full
-  // width; FP32: half of it per pass), so every global store is a 16-byte
-  // chunk of a row.
+  // width; FP32: half of it per pass where the quadrant is two or more MFMA
+  // tiles wide), so every global store is a 16-byte chunk of a row.
   constexpr int WN = C::WN;                         // columns of a wave's quadrant
   constexpr int EB = EPI == kEpiStoreF32 ? 4 : 2;   // output element bytes
-  constexpr int SC = WN * 2 / EB;                   // strip columns per pass
-  constexpr int NP = WN / SC;                       // passes per strip
+  // FP32 strips take two half-width passes when the quadrant has an even
+  // number of 32-column MFMA tiles, else one full-width pass
+  constexpr int NP = (EB == 4 && TN % 2 == 0) ? 2 : 1;  // passes per strip
+  constexpr int SC = WN / NP;                           // strip columns per pass
+  static_assert(TN % NP == 0 && SC % 32 == 0, "whole MFMA tiles per pass");
   constexpr int EPC = 16 / EB;                      // elements per 16-byte chunk
   constexpr int RSTR = SC * EB + 16;                // strip row stride in bytes (16-byte aligned)
   constexpr int CPR = SC * EB / 16;                 // chunks per strip row
@@ -442,10 +443,15 @@ static hipError_t launch_pipe_r(const void* a, const uint8_t* as, const void* w,
                                 int64_t N, int64_t K, void* y, hipStream_t stream) {
   // 256 x 256 tiles (eight waves, two stages) when they fill the 256 CUs at
   // least once.  Otherwise 128 x 128 tiles: three stages when one workgroup
-  // per CU covers every tile, else two so that two workgroups share a CU.
+  // per CU covers every tile (MXFP8 on four waves of 64 x 64, MXFP4 and BF16
+  // on eight of 64 x 32: the faster layout of each, measured), else two so
+  // that two workgroups share a CU.
   const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
   if (big >= 256) return launch_pipe_t<FMT, EPI, 256, 256, RB, 2, 4, 2>(a, as, w, ws, M, N, K, y, stream);
   const int64_t small = ((M + 127) / 128) * ((N + 127) / 128);
+  if constexpr (FMT != 2) {
+    if (small <= 256) return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 4, 3>(a, as, w, ws, M, N, K, y, stream);
+  }
   if (small <= 256) return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 2, 3>(a, as, w, ws, M, N, K, y, stream);
   return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 2, 2>(a, as, w, ws, M, N, K, y, stream);
 }
