@@ -180,6 +180,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run plain 256 MiB device copies (the reference for HBM byte counters)")
+    ap.add_argument("--only", choices=["square", "gemv"],
+                    help="run only one group of rows (4096^3 GEMMs and the ARC front end, or the nibble GEMV) "
+                         "and print them; for profiling runs")
     ap.add_argument("--traffic-from", metavar="DIR",
                     help="write the traffic summary from rocprofv3 --pmc CSV runs under DIR (pmc_main_FETCH_SIZE, "
                          "pmc_main_WRITE_SIZE, pmc_copy_FETCH_SIZE, pmc_copy_WRITE_SIZE) and exit (no GPU needed)")
@@ -204,6 +207,14 @@ def main():
         sys.exit(1)
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.only:
+        to_dev_only = (lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev))
+        if args.only == "square":
+            out = measure_square(torch, api, L, W, to_dev_only, dev)
+        else:
+            out = measure_gemv(torch, np, api, L, W, dev)
+        print(json.dumps(out), flush=True)
+        return
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -305,7 +316,26 @@ def measure_rows(torch, np, api, L, W, to_dev, dev):
                                                "frac_mxfp4_peak": round(tflops(f, ms) * 1e12 / PEAK["mxfp4"], 5)}
     log(f"rows: config-1 {ms * 1e3:.1f} us")
 
-    # ---- 4096^3: plain MXFP4, ARC (K' = 4224), BF16; quantization bandwidth
+    # ---- 4096^3: plain MXFP4, ARC (K' = 4224), BF16; quantization bandwidth; ARC front end
+    rows.update(measure_square(torch, api, L, W, to_dev, dev))
+
+    # ---- recurrent prefill, 4096 x 2048, FFN 5632, 8 steps
+    rows.update(measure_ramp(torch, api, L, W, to_dev, dev, time_calls))
+    rows["recurrent_prefill_schedule_study"] = measure_ramp_study(torch, np, api, L, W, to_dev, dev, time_calls)
+
+    # ---- nibble GEMV: weights drawn on the GPU with the same recipe
+    rows.update(measure_gemv(torch, np, api, L, W, dev))
+    return rows
+
+
+def measure_square(torch, api, L, W, to_dev, dev):
+    """Config 3 at 4096^3: plain MXFP4, ARC (K' = 4224) and BF16 GEMMs, the
+    MXFP4 quantization bandwidth and the ARC fused front end."""
+    rows = {}
+
+    def tflops(flop, ms):
+        return flop / (ms * 1e-3) / 1e12
+
     d = W.c3_arc()
     a = to_dev(d["a"])
     w = to_dev(d["w"])
@@ -339,12 +369,6 @@ def measure_rows(torch, np, api, L, W, to_dev, dev):
     rows["arc_front_end_4096x4096_s128"] = measure_front_end(torch, api, L, a, w, qc, qs, dev, time_calls)
     del a, w, pc, ps, qc, qs, y, w_aug, wsp
 
-    # ---- recurrent prefill, 4096 x 2048, FFN 5632, 8 steps
-    rows.update(measure_ramp(torch, api, L, W, to_dev, dev, time_calls))
-    rows["recurrent_prefill_schedule_study"] = measure_ramp_study(torch, np, api, L, W, to_dev, dev, time_calls)
-
-    # ---- nibble GEMV: weights drawn on the GPU with the same recipe
-    rows.update(measure_gemv(torch, np, api, L, W, dev))
     return rows
 
 
