@@ -654,6 +654,18 @@ def measure_gemv(torch, np, api, L, W, dev):
     out["gemv_lm_head_low_pass_b16"] = {"us": round(ms * 1e3, 2), "gb_s": round(gb, 1),
                                         "frac_hbm": round(gb * 1e9 / PEAK["hbm"], 4),
                                         "bytes": low_bytes(N, K)}
+    nf_lm = int(flags.sum().item())
+
+    def lm_esc():
+        c = copies[it[0] % 4]
+        it[0] += 1
+        L.rq_gemv_nibble_escalate(xs[K], B, K, N, c[0], c[1], c[2], flags, L.RQ_ESCALATE, wsp, wsb, ys[N])
+
+    ms = time_calls(torch, lm_esc, 40)
+    gb = esc_bytes(N, K, nf_lm) / (ms * 1e-3) / 1e9
+    out["gemv_lm_head_escalation_2_of_16"] = {"us": round(ms * 1e3, 2), "gb_s": round(gb, 1),
+                                              "frac_hbm": round(gb * 1e9 / PEAK["hbm"], 4),
+                                              "bytes": esc_bytes(N, K, nf_lm)}
     del copies
 
     def sweep(phase):

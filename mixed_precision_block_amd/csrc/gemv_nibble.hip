@@ -158,10 +158,20 @@ __device__ __forceinline__ void gemv_tile(const uint16_t* __restrict__ x, int B,
       if (kFull && t >= nt) continue;  // wave-uniform; the low pass computes every slot
       uint32_t xq[16];
       if constexpr (kFull) {
-        // the few flagged tokens: x straight through the scalar cache
-        const uint32_t* xt = reinterpret_cast<const uint32_t*>(x) + ((size_t)tok[t] * K + 32 * (size_t)b) / 2;
+        if (xs != nullptr) {
+          // the flagged tokens' x of this slice, staged in LDS by the workgroup
+          const int kc = (b1 - b0) * 4;
 #pragma unroll
-        for (int p = 0; p < 16; ++p) xq[p] = xt[p];
+          for (int i = 0; i < 4; ++i) {
+            const uint4 v = xs[t * kc + (b - b0) * 4 + i];
+            xq[4 * i] = v.x, xq[4 * i + 1] = v.y, xq[4 * i + 2] = v.z, xq[4 * i + 3] = v.w;
+          }
+        } else {
+          // the few flagged tokens: x straight through the scalar cache
+          const uint32_t* xt = reinterpret_cast<const uint32_t*>(x) + ((size_t)tok[t] * K + 32 * (size_t)b) / 2;
+#pragma unroll
+          for (int p = 0; p < 16; ++p) xq[p] = xt[p];
+        }
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -226,17 +236,121 @@ __device__ __forceinline__ int flagged_group(const uint8_t* __restrict__ flags, 
   return nt;
 }
 
+// LDS budget for staging the flagged tokens' x in the escalation: up to
+// kXStageElems elements per token of a workgroup's K range.
+constexpr int kXStageElems = 4096;
+
+// Stage x[tok[t]][32 b0, 32 b1) for t < nt into xst (4 (b1 - b0) 16-byte
+// chunks per token).  Every thread of the workgroup calls it.
+__device__ __forceinline__ void stage_x(uint4* xst, const uint16_t* __restrict__ x, int K, const int* tok, int nt,
+                                        int b0, int b1) {
+  const int kc = (b1 - b0) * 4;
+  for (int i = threadIdx.x; i < nt * kc; i += 256) {
+    const int t = i / kc, c = i - t * kc;
+    xst[t * kc + c] = reinterpret_cast<const uint4*>(x + (size_t)tok[t] * K + (size_t)b0 * 32)[c];
+  }
+  __syncthreads();
+}
+
+// Escalation of one 64-row tile by one wave (lane = row), over all of K.
+// The sum is kept as four partials over the blocks b = w mod 4, combined
+// as ((p0 + p1) + p2) + p3 -- the order of the four-wave tile (gemv_tile
+// with one slice) -- so both give the same bits.  The planes of the next
+// two blocks are in flight; x comes through the scalar cache.
+__device__ __forceinline__ void escalate_wave_tile(const uint16_t* __restrict__ x, int K, int N,
+                                                   const uint8_t* __restrict__ hi, const uint8_t* __restrict__ lo,
+                                                   const uint16_t* __restrict__ sc, const int* tok, int nt,
+                                                   uint16_t* __restrict__ y, int tile) {
+  constexpr int PF = 2;
+  const int lane = threadIdx.x & 63;
+  const int nb = K >> 5;
+  const size_t tbase = (size_t)tile * nb * 64 + lane;
+  const uint4* hp = reinterpret_cast<const uint4*>(hi) + tbase;
+  const uint4* lp = reinterpret_cast<const uint4*>(lo) + tbase;
+  const uint16_t* sp = sc + tbase;
+  float acc[4][kEscTokens];
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+#pragma unroll
+    for (int t = 0; t < kEscTokens; ++t) acc[w][t] = 0.0f;
+  uint4 ph[PF], pl[PF];
+  uint16_t ps[PF];
+#pragma unroll
+  for (int f = 0; f < PF; ++f) {
+    const int bb = f < nb ? f : nb - 1;
+    ph[f] = hp[(size_t)bb * 64], pl[f] = lp[(size_t)bb * 64], ps[f] = sp[(size_t)bb * 64];
+  }
+  // four blocks per turn so that the partial index is static
+  for (int b4 = 0; b4 < nb; b4 += 4) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int b = b4 + w;
+      if (b >= nb) break;
+      const uint4 dh = ph[0], dl = pl[0];
+      const float s = f16_to_f32(ps[0]);
+#pragma unroll
+      for (int f = 0; f + 1 < PF; ++f) ph[f] = ph[f + 1], pl[f] = pl[f + 1], ps[f] = ps[f + 1];
+      const int bn = b + PF < nb ? b + PF : b;  // the last blocks reload themselves
+      ph[PF - 1] = hp[(size_t)bn * 64], pl[PF - 1] = lp[(size_t)bn * 64], ps[PF - 1] = sp[(size_t)bn * 64];
+      bf16x2 wp[16];
+      unpack_full(dh, dl, wp);
+#pragma unroll
+      for (int t = 0; t < kEscTokens; ++t) {
+        if (t >= nt) continue;
+        const uint32_t* xt = reinterpret_cast<const uint32_t*>(x) + ((size_t)tok[t] * K + 32 * (size_t)b) / 2;
+        float blk = 0.0f;
+#pragma unroll
+        for (int p = 0; p < 16; ++p) blk = __builtin_amdgcn_fdot2_f32_bf16(wp[p], as_bf16x2(xt[p]), blk, false);
+        acc[w][t] = fmaf(blk, s, acc[w][t]);
+      }
+    }
+  }
+  const int n = tile * 64 + lane;
+#pragma unroll
+  for (int t = 0; t < kEscTokens; ++t) {
+    const float v = ((acc[0][t] + acc[1][t]) + acc[2][t]) + acc[3][t];
+    if (t < nt && n < N) y[(size_t)tok[t] * N + n] = (uint16_t)f32_to_bf16(v);
+  }
+}
+
+// Escalation with one wave per tile (large N, unsplit): four tiles per
+// workgroup, no cross-wave reduction.
+__global__ __launch_bounds__(256) void gemv_escalate_wave_kernel(const uint16_t* __restrict__ x, int B, int K, int N,
+                                                                 const uint8_t* __restrict__ hi,
+                                                                 const uint8_t* __restrict__ lo,
+                                                                 const uint16_t* __restrict__ sc,
+                                                                 const uint8_t* __restrict__ flags,
+                                                                 uint16_t* __restrict__ y) {
+  int tok[kEscTokens];
+  const int nt = flagged_group(flags, B, blockIdx.z, tok);
+  if (nt == 0) return;
+  const int tile = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  if (tile >= (N + 63) / 64) return;
+  escalate_wave_tile(x, K, N, hi, lo, sc, tok, nt, y, tile);
+}
+
 __global__ __launch_bounds__(256) void gemv_escalate_kernel(const uint16_t* __restrict__ x, int B, int K, int N,
                                                             const uint8_t* __restrict__ hi,
                                                             const uint8_t* __restrict__ lo,
                                                             const uint16_t* __restrict__ sc,
                                                             const uint8_t* __restrict__ flags,
-                                                            uint16_t* __restrict__ y, float* __restrict__ ws) {
+                                                            uint16_t* __restrict__ y, float* __restrict__ ws,
+                                                            int staged) {
+  extern __shared__ uint4 xst[];  // the flagged tokens' x of this slice, when staged
   __shared__ float red[4][kEscTokens][64];
   int tok[kEscTokens];
   const int nt = flagged_group(flags, B, blockIdx.z, tok);
   if (nt == 0) return;  // nothing (more) flagged: no weight traffic
-  gemv_tile<kEscTokens, true>(x, B, K, N, hi, lo, sc, tok, nt, y, ws, red, nullptr, blockIdx.x, blockIdx.y,
+  uint4* xs = nullptr;
+  if (staged) {
+    const int nb = K >> 5, per = (nb + (int)gridDim.y - 1) / (int)gridDim.y;
+    const int b0 = (int)blockIdx.y * per, b1 = min(nb, b0 + per);
+    if (b0 < b1) {
+      stage_x(xst, x, K, tok, nt, b0, b1);
+      xs = xst;
+    }
+  }
+  gemv_tile<kEscTokens, true>(x, B, K, N, hi, lo, sc, tok, nt, y, ws, red, xs, blockIdx.x, blockIdx.y,
                               gridDim.y);
 }
 
@@ -295,6 +409,8 @@ __global__ __launch_bounds__(256) void gemv_escalate_grouped_kernel(const rq_gem
   const int64_t tile = (int64_t)blockIdx.x - p->tile_start;
   // problems without a low plane take no escalation
   if (p->w_lo == nullptr || tile < 0 || tile >= (p->N + 63) / 64) return;
+  // four waves per tile: the sweep's 7750 tiles as one wave each would be a
+  // single round whose K = 3072 tiles set the end
   gemv_tile<kEscTokens, true>(static_cast<const uint16_t*>(p->x_bf16), B, (int)p->K, (int)p->N, p->w_hi, p->w_lo,
                               p->scales_tiled, tok, nt, static_cast<uint16_t*>(p->y_bf16), nullptr, red, nullptr,
                               (int)tile, 0, 1);
@@ -401,8 +517,20 @@ hipError_t launch_gemv_escalate(const uint16_t* x, int64_t B, int64_t K, int64_t
   const int b = (int)B, k = (int)K, n = (int)N;
   float* w = static_cast<float*>(ws);
   // up to four groups of four flagged tokens
-  const dim3 grid3(tiles, ns, (unsigned)((B + kEscTokens - 1) / kEscTokens));
-  gemv_escalate_kernel<<<grid3, 256, 0, stream>>>(x, b, k, n, hi, lo, scales, flags, y, w);
+  const unsigned groups = (unsigned)((B + kEscTokens - 1) / kEscTokens);
+  if (ns == 1 && tiles >= 2048) {
+    // enough tiles for one wave each: no cross-wave reduction
+    gemv_escalate_wave_kernel<<<dim3((tiles + 3) / 4, 1, groups), 256, 0, stream>>>(x, b, k, n, hi, lo, scales,
+                                                                                     flags, y);
+    return hipGetLastError();
+  }
+  // four waves per tile; the flagged tokens' x of the slice staged in LDS
+  // when it fits the budget
+  const int64_t nb = K / 32, per = (nb + ns - 1) / ns;
+  const int staged = per * 32 <= kXStageElems ? 1 : 0;
+  const size_t shm = staged ? (size_t)kEscTokens * per * 32 * 2 : 0;
+  const dim3 grid3(tiles, ns, groups);
+  gemv_escalate_kernel<<<grid3, 256, shm, stream>>>(x, b, k, n, hi, lo, scales, flags, y, w, staged);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && ns > 1) e = launch_reduce(w, ns, B, N, flags, y, stream);
   return e;
