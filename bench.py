@@ -89,24 +89,42 @@ class Timer:
         return sum(s.elapsed_time(e) for s, e in self.pairs)
 
 
-def time_calls(torch, fn, iters, warmup=3, before=None):
-    """Mean per-call milliseconds of fn().  Without `before`, one pair of
-    events brackets the back-to-back calls (the host issues faster than the
-    GPU runs them, so this is device time); with it, events bracket each
-    call and the untimed `before` work runs in between."""
+def time_calls(torch, fn, iters, warmup=10, before=None, batches=5, graph=False):
+    """Per-call milliseconds of fn().  Without `before`: the median over
+    `batches` batches of iters back-to-back calls, each batch bracketed by
+    one pair of events.  Eager calls are device time only while the host
+    issues them faster than the GPU runs them (about 7 us per library call
+    from Python); for shorter kernels graph=True captures the iters calls
+    once in a HIP graph and times its replays.  With `before`: events
+    bracket each call, the untimed `before` work runs in between, and the
+    mean is returned."""
     for _ in range(warmup):
         if before:
             before()
         fn()
     if before is None:
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(iters):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / iters
+        if graph:
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(iters):
+                    fn()
+            g.replay()
+            run = g.replay
+        else:
+            def run():
+                for _ in range(iters):
+                    fn()
+        per = []
+        for _ in range(batches):
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run()
+            e1.record()
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / iters)
+        return sorted(per)[len(per) // 2]
     tm = Timer(torch)
     for _ in range(iters):
         before()
@@ -258,9 +276,23 @@ def main():
     # the GEMM's average launch duration: each of the step's GEMMs launched
     # back to back between one pair of events (events around every launch
     # would add their own packets to the measured time), averaged over them
-    gemm_ms = sum(time_calls(torch, lambda g=g: L.rq_gemm(L.RQ_MXFP8, g["ac"], g["as_"], g["wc"], g["ws"], M, g["N"],
-                                                           g["K"], L.RQ_OUT_BF16, g["y"]), max(args.steps, 20))
-                  for g in groups) / len(groups)
+    per_gemm, per_quant = {}, {}
+    for g in groups:
+        ms_g = time_calls(torch, lambda g=g: L.rq_gemm(L.RQ_MXFP8, g["ac"], g["as_"], g["wc"], g["ws"], M, g["N"],
+                                                      g["K"], L.RQ_OUT_BF16, g["y"]), max(args.steps, 20),
+                          graph=True)
+        f_g = 2.0 * M * g["N"] * g["K"]
+        per_gemm[f"{g['name']} {M}x{g['N']}x{g['K']}"] = {
+            "us": round(ms_g * 1e3, 2), "tflops": round(f_g / (ms_g * 1e-3) / 1e12, 1),
+            "frac_mxfp8_peak": round(f_g / (ms_g * 1e-3) / PEAK["mxfp8"], 4)}
+        ms_q = time_calls(torch, lambda g=g: L.rq_quantize(g["a"], M, g["K"], L.RQ_MXFP8, None, 0,
+                                                          L.RQ_APPEND_NONE, g["ac"], g["as_"]), max(args.steps, 20),
+                          graph=True)
+        qb = M * g["K"] * (2 + 1) + M * g["K"] // 32
+        per_quant[f"{g['name']} input {M}x{g['K']}"] = {
+            "us": round(ms_q * 1e3, 2), "gb_s": round(qb / (ms_q * 1e-3) / 1e9, 1),
+            "frac_hbm": round(qb / (ms_q * 1e-3) / PEAK["hbm"], 4)}
+    gemm_ms = sum(v["us"] for v in per_gemm.values()) / 1e3 / len(groups)
     achieved = flops_step / len(groups) / (gemm_ms * 1e-3)
     log(f"main: {ms_step:.3f} ms/step, GEMM avg launch {gemm_ms * 1e3:.1f} us")
     value = flops_step / (ms_step * 1e-3) / 1e12
@@ -288,7 +320,8 @@ def main():
                                "gate_up, 128x128 for o and down)",
                      "achieved": round(achieved / 1e12, 2), "peak": PEAK["mxfp8"] / 1e12, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK["mxfp8"], 4), "traffic": traffic,
-                     "avg_launch_us": round(gemm_ms * 1e3, 2)},
+                     "avg_launch_us": round(gemm_ms * 1e3, 2), "per_gemm": per_gemm},
+        "quantize_per_input": per_quant,
     }
     for g in groups:
         del g["ac"], g["as_"], g["y"], g["a"]
@@ -310,10 +343,18 @@ def measure_rows(torch, np, api, L, W, to_dev, dev):
     ac, as_ = api.quantize(to_dev(d["a"]), L.RQ_MXFP4)
     wc, ws = api.quantize(to_dev(d["w"]), L.RQ_MXFP4)
     y = torch.empty((128, 1024), dtype=torch.bfloat16, device=dev)
-    ms = time_calls(torch, lambda: L.rq_gemm(L.RQ_MXFP4, ac, as_, wc, ws, 128, 1024, 1024, 0, y), 200)
+    ms = time_calls(torch, lambda: L.rq_gemm(L.RQ_MXFP4, ac, as_, wc, ws, 128, 1024, 1024, 0, y), 200, graph=True)
     f = 2.0 * 128 * 1024 * 1024
     rows["single_mxfp4_gemm_128x1024x1024"] = {"us": round(ms * 1e3, 2), "tflops": round(tflops(f, ms), 2),
                                                "frac_mxfp4_peak": round(tflops(f, ms) * 1e12 / PEAK["mxfp4"], 5)}
+    a1, w1 = to_dev(d["a"]), to_dev(d["w"])
+    for name, x1, r1 in (("a_128x1024", a1, 128), ("w_1024x1024", w1, 1024)):
+        c1, s1 = api.quantize(x1, L.RQ_MXFP4)
+        ms_q = time_calls(torch, lambda: L.rq_quantize(x1, r1, 1024, L.RQ_MXFP4, None, 0, 0, c1, s1), 100,
+                          graph=True)
+        qb = r1 * 1024 * 2 + r1 * 512 + r1 * 32
+        rows[f"single_mxfp4_quantize_{name}"] = {"us": round(ms_q * 1e3, 2),
+                                                 "gb_s": round(qb / (ms_q * 1e-3) / 1e9, 1), "bytes": qb}
     log(f"rows: config-1 {ms * 1e3:.1f} us")
 
     # ---- 4096^3: plain MXFP4, ARC (K' = 4224), BF16; quantization bandwidth; ARC front end
@@ -345,7 +386,7 @@ def measure_square(torch, api, L, W, to_dev, dev):
     qc, qs = api.quantize(w, L.RQ_MXFP4)
     y = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
     ms_plain = time_calls(torch, lambda: L.rq_gemm(L.RQ_MXFP4, pc, ps, qc, qs, n, n, n, 0, y), 50)
-    ms_q = time_calls(torch, lambda: L.rq_quantize(a, n, n, L.RQ_MXFP4, None, 0, 0, pc, ps), 50)
+    ms_q = time_calls(torch, lambda: L.rq_quantize(a, n, n, L.RQ_MXFP4, None, 0, 0, pc, ps), 50, graph=True)
     idx = api.select_channels(api.channel_amax(a), 128).to(dev)
     w_aug = api.quantize(w, L.RQ_MXFP4, idx, L.RQ_APPEND_COPY)
     ws_bytes = L.rq_gemm_arc_workspace_bytes(n, n, 128)
@@ -413,8 +454,8 @@ def measure_front_end(torch, api, L, a, w, qc, qs, dev, time_calls):
         L.rq_arc_frontend(a, n, n, ident, 0, L.RQ_MXFP4, L.RQ_APPEND_NONE, 1, 1e-6, pc, pcs)
         L.rq_gemm(L.RQ_MXFP4, pc, pcs, qc, qs, n, n, n, L.RQ_OUT_BF16, y)
 
-    ms_f = time_calls(torch, fused, 50)
-    ms_u = time_calls(torch, unfused, 50)
+    ms_f = time_calls(torch, fused, 50, graph=True)
+    ms_u = time_calls(torch, unfused, 50, graph=True)
     ms_fg = time_calls(torch, fused_gemm, 50)
     ms_pg = time_calls(torch, plain_gemm, 50)
     ref = torch.empty((n, n), dtype=torch.float32, device=dev)
@@ -749,7 +790,45 @@ def cpu_baseline(np, W):
     dt = (time.perf_counter() - t0) / n
     return {"value": round(flop / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{rows} of 4096 rows of each of the 4 layer inputs (quantize + float64 GEMM against the "
-                      f"stacked weights + BF16 rounding), {n} repetitions, {dt:.3f} s each"}
+                      f"stacked weights + BF16 rounding), {n} repetitions, {dt:.3f} s each",
+            "rows": cpu_rows(np, W)}
+
+
+def cpu_rows(np, W):
+    """The oracle's other steps on bounded samples (a baseline only): MXFP4
+    quantization, one decode GEMV with escalation, one RAMP step; each the
+    median of three timed runs after one warm-up."""
+    from oracle import formats as F
+    from oracle import quant as Q
+    from oracle import gemv as V
+    from oracle import ramp as R
+
+    def med3(fn):
+        fn()
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return sorted(ts)[1]
+
+    out = {}
+    a = W.c3_arc(M=256, N=32)["a"]
+    t = med3(lambda: Q.quantize_mx(a, F.FMT_MXFP4))
+    qb = a.size * 2 + a.size // 2 + a.size // 32
+    out["quantize_mxfp4_256x4096"] = {"s": round(t, 4), "gb_s": round(qb / t / 1e9, 4)}
+    d = W.c5_linear(0)
+    flags = d["flags"]
+    t = med3(lambda: V.gemv_nibble_escalate(d["x"], d["w"], d["scales"], flags))
+    wb = d["w"].size
+    out[f"gemv_nibble_escalate_{d['name']}_{d['w'].shape[0]}x{d['w'].shape[1]}_b16"] = {
+        "s": round(t, 4), "gb_s_of_int8_weights": round(wb / t / 1e9, 4)}
+    c4 = W.c4_ramp(S=64)
+    w1d = R.quantize_weights(c4["w1"], F.FMT_MXFP4)
+    w2d = R.quantize_weights(c4["w2"], F.FMT_MXFP4)
+    t = med3(lambda: R.ramp_step(c4["h0"], c4["w1"], c4["w2"], True, F.FMT_MXFP4, w1d, w2d))
+    out["ramp_step_mxfp4_64_of_4096_rows"] = {"s": round(t, 4), "s_per_step_at_4096_rows": round(t * 64, 2)}
+    return out
 
 
 if __name__ == "__main__":
