@@ -374,7 +374,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
         if constexpr (EPI == kEpiStoreF32) {
           float* yrow = reinterpret_cast<float*>(Y) + (int64_t)m * N;
           if (whole) {
-            *reinterpret_cast<uint4*>(yrow + n) = v;
+            __builtin_nontemporal_store(__builtin_bit_cast(v4i, v), reinterpret_cast<v4i*>(yrow + n));
           } else {
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
             for (int e = 0; e < 4; ++e)
@@ -403,7 +403,9 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
             }
           }
           if (whole) {
-            *reinterpret_cast<uint4*>(yrow + n) = uint4{w[0], w[1], w[2], w[3]};
+            // streaming store: the output is not read again by this kernel
+            __builtin_nontemporal_store(v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]},
+                                        reinterpret_cast<v4i*>(yrow + n));
           } else {
             for (int e = 0; e < 8; ++e)
               if (n + e < N) yrow[n + e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
