@@ -8,6 +8,9 @@
  * are asynchronous on that stream: they validate their arguments on the
  * host, enqueue kernels and return.  On a validation error nothing is
  * enqueued.  Device faults surface at the caller's next synchronization.
+ * A tensor with no elements (one of its extents is 0) is never read or
+ * written, and its pointer may be NULL; a call whose work is empty
+ * validates its other arguments and enqueues nothing.
  * No call allocates device memory; calls that need scratch space take a
  * caller-provided workspace whose size a *_workspace_bytes() helper gives.
  * The library keeps no per-call state and is thread-safe (the last-error

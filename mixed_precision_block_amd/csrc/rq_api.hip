@@ -32,6 +32,10 @@ rq_status ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// A tensor with no elements is never dereferenced, so its pointer may be
+// NULL (torch hands out NULL for empty tensors).
+bool have(const void* p, bool empty) { return p != nullptr || empty; }
+
 // Device presence, checked after argument validation so that bad arguments
 // are reported the same way with or without a GPU.
 rq_status need_device() {
@@ -81,7 +85,8 @@ const char* rq_last_error(void) { return g_err; }
 
 rq_status rq_quantize(const void* x_bf16, int64_t rows, int64_t K, int fmt, const int32_t* idx, int64_t S,
                       int append, void* codes, uint8_t* scales, void* stream) {
-  if (!x_bf16 || !codes || !scales) return fail(RQ_EINVAL, "rq_quantize: null tensor pointer");
+  if (!have(x_bf16, rows == 0) || !have(codes, rows == 0) || !have(scales, rows == 0))
+    return fail(RQ_EINVAL, "rq_quantize: null tensor pointer");
   if (fmt != RQ_MXFP4 && fmt != RQ_MXFP8) return fail(RQ_EINVAL, "rq_quantize: fmt must be RQ_MXFP4 or RQ_MXFP8");
   if (append != RQ_APPEND_NONE && append != RQ_APPEND_RESIDUAL && append != RQ_APPEND_COPY)
     return fail(RQ_EINVAL, "rq_quantize: unknown append mode %d", append);
@@ -106,7 +111,7 @@ rq_status rq_quantize(const void* x_bf16, int64_t rows, int64_t K, int fmt, cons
 }
 
 rq_status rq_channel_amax(const void* x_bf16, int64_t rows, int64_t K, uint16_t* amax_bf16, void* stream) {
-  if (!x_bf16 || !amax_bf16) return fail(RQ_EINVAL, "rq_channel_amax: null pointer");
+  if (!have(x_bf16, rows == 0) || !amax_bf16) return fail(RQ_EINVAL, "rq_channel_amax: null pointer");
   if (rows < 0 || K <= 0) return fail(RQ_ESHAPE, "rq_channel_amax: need rows >= 0, K > 0");
   if (rq_status s = need_device(); s != RQ_OK) return s;
   return hip_status(rq::launch_channel_amax(static_cast<const uint16_t*>(x_bf16), rows, K, amax_bf16,
@@ -129,7 +134,8 @@ rq_status rq_select_channels(const uint16_t* amax_bf16, int64_t K, int64_t S, in
 
 rq_status rq_arc_frontend(const void* x_bf16, int64_t rows, int64_t K, const int32_t* perm, int64_t S, int fmt,
                           int append, int rmsnorm, float eps, void* codes, uint8_t* scales, void* stream) {
-  if (!x_bf16 || !perm || !codes || !scales) return fail(RQ_EINVAL, "rq_arc_frontend: null pointer");
+  if (!have(x_bf16, rows == 0) || !perm || !have(codes, rows == 0) || !have(scales, rows == 0))
+    return fail(RQ_EINVAL, "rq_arc_frontend: null pointer");
   if (fmt != RQ_MXFP4 && fmt != RQ_MXFP8) return fail(RQ_EINVAL, "rq_arc_frontend: fmt must be RQ_MXFP4 or RQ_MXFP8");
   if (append != RQ_APPEND_NONE && append != RQ_APPEND_RESIDUAL && append != RQ_APPEND_COPY)
     return fail(RQ_EINVAL, "rq_arc_frontend: unknown append mode %d", append);
@@ -151,7 +157,7 @@ rq_status rq_arc_frontend(const void* x_bf16, int64_t rows, int64_t K, const int
 }
 
 rq_status rq_rmsnorm(const void* h_bf16, int64_t rows, int64_t D, float eps, void* out_bf16, void* stream) {
-  if (!h_bf16 || !out_bf16) return fail(RQ_EINVAL, "rq_rmsnorm: null pointer");
+  if (!have(h_bf16, rows == 0) || !have(out_bf16, rows == 0)) return fail(RQ_EINVAL, "rq_rmsnorm: null pointer");
   if (!(eps >= 0.0f && eps < INFINITY)) return fail(RQ_EINVAL, "rq_rmsnorm: eps must be finite and >= 0");
   if (rows < 0 || rows > kInt32Max || D <= 0 || D % 8)
     return fail(RQ_ESHAPE, "rq_rmsnorm: need 0 <= rows < 2^31, D > 0, D %% 8 == 0");
@@ -164,10 +170,12 @@ rq_status rq_rmsnorm(const void* h_bf16, int64_t rows, int64_t D, float eps, voi
 
 rq_status rq_gemm(int fmt, const void* a, const uint8_t* a_scales, const void* w, const uint8_t* w_scales,
                   int64_t M, int64_t N, int64_t K, int out, void* y, void* stream) {
-  if (!a || !w || !y) return fail(RQ_EINVAL, "rq_gemm: null tensor pointer");
+  if (!have(a, M == 0) || !have(w, N == 0) || !have(y, M == 0 || N == 0))
+    return fail(RQ_EINVAL, "rq_gemm: null tensor pointer");
   if (fmt != RQ_MXFP4 && fmt != RQ_MXFP8 && fmt != RQ_BF16) return fail(RQ_EINVAL, "rq_gemm: unknown fmt %d", fmt);
   if (fmt == RQ_BF16 && (a_scales || w_scales)) return fail(RQ_EINVAL, "rq_gemm: RQ_BF16 takes no scales");
-  if (fmt != RQ_BF16 && (!a_scales || !w_scales)) return fail(RQ_EINVAL, "rq_gemm: MX formats need scales");
+  if (fmt != RQ_BF16 && (!have(a_scales, M == 0) || !have(w_scales, N == 0)))
+    return fail(RQ_EINVAL, "rq_gemm: MX formats need scales");
   if (out != RQ_OUT_BF16 && out != RQ_OUT_F32) return fail(RQ_EINVAL, "rq_gemm: unknown out %d", out);
   if (M < 0 || N < 0 || K <= 0 || K % 32 || M > kInt32Max || N > kInt32Max || K > kInt32Max)
     return fail(RQ_ESHAPE, "rq_gemm: need 0 <= M, N < 2^31 and 0 < K < 2^31 with K %% 32 == 0");
@@ -187,7 +195,9 @@ size_t rq_gemm_arc_workspace_bytes(int64_t M, int64_t K, int64_t S) {
 rq_status rq_gemm_arc(const void* a_bf16, int64_t M, int64_t K, const int32_t* idx, int64_t S, const void* w_aug,
                       const uint8_t* w_aug_scales, int64_t N, void* workspace, size_t ws_bytes, int out, void* y,
                       void* stream) {
-  if (!a_bf16 || !idx || !w_aug || !w_aug_scales || !workspace || !y) return fail(RQ_EINVAL, "rq_gemm_arc: null pointer");
+  if (!have(a_bf16, M == 0) || !idx || !have(w_aug, N == 0) || !have(w_aug_scales, N == 0) ||
+      !have(workspace, M == 0) || !have(y, M == 0 || N == 0))
+    return fail(RQ_EINVAL, "rq_gemm_arc: null pointer");
   if (out != RQ_OUT_BF16 && out != RQ_OUT_F32) return fail(RQ_EINVAL, "rq_gemm_arc: unknown out %d", out);
   if (M < 0 || N < 0 || K <= 0 || K % 32 || S <= 0 || S % 32 || M > kInt32Max || N > kInt32Max ||
       K + S > kInt32Max)
@@ -226,7 +236,8 @@ rq_status rq_recurrent_prefill(void* h_bf16, int64_t S, int64_t D, int64_t F, co
                                const void* w2_bf16, const void* w1_q, const uint8_t* w1_s, const void* w2_q,
                                const uint8_t* w2_s, int fmt, uint64_t schedule, int steps, float eps,
                                void* workspace, size_t ws_bytes, void* stream) {
-  if (!h_bf16 || !workspace) return fail(RQ_EINVAL, "rq_recurrent_prefill: null h or workspace");
+  if (!have(h_bf16, S == 0) || !have(workspace, S == 0))
+    return fail(RQ_EINVAL, "rq_recurrent_prefill: null h or workspace");
   if (fmt != RQ_MXFP4 && fmt != RQ_MXFP8) return fail(RQ_EINVAL, "rq_recurrent_prefill: fmt must be MXFP4 or MXFP8");
   if (steps < 1 || steps > 64) return fail(RQ_ESHAPE, "rq_recurrent_prefill: steps must be in [1, 64]");
   const uint64_t used = steps == 64 ? ~0ull : ((1ull << steps) - 1);
@@ -285,7 +296,9 @@ size_t rq_nibble_scale_bytes(int64_t N, int64_t K) {
 
 rq_status rq_pack_nibble_planes(const int8_t* w, const uint16_t* scales_f16, int64_t N, int64_t K, uint8_t* hi,
                                 uint8_t* lo, uint16_t* scales_tiled, void* stream) {
-  if (!w || !scales_f16 || !hi || !lo || !scales_tiled) return fail(RQ_EINVAL, "rq_pack_nibble_planes: null pointer");
+  if (!have(w, N == 0) || !have(scales_f16, N == 0) || !have(hi, N == 0) || !have(lo, N == 0) ||
+      !have(scales_tiled, N == 0))
+    return fail(RQ_EINVAL, "rq_pack_nibble_planes: null pointer");
   if (N < 0 || K <= 0 || K % 32 || N > kInt32Max || K > kInt32Max)
     return fail(RQ_ESHAPE, "rq_pack_nibble_planes: need K > 0, K %% 32 == 0");
   if (!aligned16(hi) || !aligned16(lo)) return fail(RQ_EALIGN, "rq_pack_nibble_planes: planes must be 16-byte aligned");
@@ -302,10 +315,11 @@ size_t rq_gemv_workspace_bytes(int64_t B, int64_t N, int64_t K) {
 rq_status rq_gemv_nibble_escalate(const void* x_bf16, int64_t B, int64_t K, int64_t N, const uint8_t* w_hi,
                                   const uint8_t* w_lo, const uint16_t* scales_tiled, const uint8_t* flags, int phase,
                                   void* workspace, size_t ws_bytes, void* y_bf16, void* stream) {
-  if (!x_bf16 || !w_hi || !scales_tiled || !y_bf16) return fail(RQ_EINVAL, "rq_gemv_nibble_escalate: null pointer");
+  if (!x_bf16 || !have(w_hi, N == 0) || !have(scales_tiled, N == 0) || !have(y_bf16, N == 0))
+    return fail(RQ_EINVAL, "rq_gemv_nibble_escalate: null pointer");
   if (phase != RQ_LOW && phase != RQ_ESCALATE && phase != RQ_BOTH)
     return fail(RQ_EINVAL, "rq_gemv_nibble_escalate: unknown phase %d", phase);
-  if ((phase & RQ_ESCALATE) && (!w_lo || !flags))
+  if ((phase & RQ_ESCALATE) && (!have(w_lo, N == 0) || !flags))
     return fail(RQ_EINVAL, "rq_gemv_nibble_escalate: escalation needs w_lo and flags");
   if (B < 1 || B > 16) return fail(RQ_ESHAPE, "rq_gemv_nibble_escalate: B must be in [1, 16]");
   if (N < 0 || K <= 0 || K % 32 || N > kInt32Max || K > kInt32Max)
@@ -384,7 +398,9 @@ rq_status rq_escalation_gate(const void* logits_bf16, int64_t B, int64_t V, floa
 
 rq_status rq_kv_quantize(const void* x_bf16, int64_t T, int64_t H, int64_t D, uint8_t* codes, float* scales,
                          void* stream) {
-  if (!x_bf16 || !codes || !scales) return fail(RQ_EINVAL, "rq_kv_quantize: null pointer");
+  const bool kv_empty = T == 0 || H == 0;
+  if (!have(x_bf16, kv_empty) || !have(codes, kv_empty) || !have(scales, kv_empty))
+    return fail(RQ_EINVAL, "rq_kv_quantize: null pointer");
   if (T < 0 || H < 0 || D <= 0 || D % 128) return fail(RQ_ESHAPE, "rq_kv_quantize: need D > 0, D %% 128 == 0");
   if (!aligned16(x_bf16) || !aligned16(codes)) return fail(RQ_EALIGN, "rq_kv_quantize: x and codes must be 16-byte aligned");
   if (rq_status s = need_device(); s != RQ_OK) return s;

@@ -201,3 +201,37 @@ def test_arc_frontend_and_rmsnorm_validation():
         a[i] = v
         assert status_of(rq.rq_rmsnorm, *a) == want, (i, v)
     assert status_of(rq.rq_rmsnorm, *r) in (L.RQ_OK, L.RQ_ENODEV)
+
+
+def test_empty_tensors_may_be_null_and_nothing_else():
+    """A zero extent makes a tensor's pointer optional (torch gives empty
+    tensors a NULL data pointer); the same NULL with work to do is EINVAL."""
+    passed = (L.RQ_OK, L.RQ_ENODEV)
+    # rows == 0: x, codes, scales may be NULL
+    assert status_of(rq.rq_quantize, None, 0, 64, L.RQ_MXFP4, None, 0, 0, None, None) in passed
+    assert status_of(rq.rq_quantize, None, 1, 64, L.RQ_MXFP4, None, 0, 0, None, None) == L.RQ_EINVAL
+    # ... but the arguments are still validated
+    assert status_of(rq.rq_quantize, None, 0, 48, L.RQ_MXFP4, None, 0, 0, None, None) == L.RQ_ESHAPE
+    assert status_of(rq.rq_arc_frontend, None, 0, 64, A16, 32, L.RQ_MXFP4, L.RQ_APPEND_RESIDUAL, 1, 1e-6,
+                     None, None) in passed
+    assert status_of(rq.rq_arc_frontend, None, 0, 64, None, 32, L.RQ_MXFP4, L.RQ_APPEND_RESIDUAL, 1, 1e-6,
+                     None, None) == L.RQ_EINVAL  # perm has K entries
+    assert status_of(rq.rq_rmsnorm, None, 0, 64, 1e-6, None) in passed
+    assert status_of(rq.rq_channel_amax, None, 0, 64, A16) in passed
+    # GEMM: M == 0 frees a, a_scales and y; N == 0 frees w, w_scales and y
+    assert status_of(rq.rq_gemm, L.RQ_MXFP4, None, None, A16, A16, 0, 4, 64, 0, None) in passed
+    assert status_of(rq.rq_gemm, L.RQ_MXFP4, A16, A16, None, None, 4, 0, 64, 0, None) in passed
+    assert status_of(rq.rq_gemm, L.RQ_MXFP4, None, None, A16, A16, 4, 4, 64, 0, A16) == L.RQ_EINVAL
+    assert status_of(rq.rq_gemm, L.RQ_MXFP4, A16, A16, None, A16, 0, 4, 64, 0, None) == L.RQ_EINVAL
+    assert status_of(rq.rq_gemm_arc, None, 0, 128, A16, 32, A16, A16, 16, None, 0, 0, None) in passed
+    ws = rq.rq_recurrent_prefill_workspace_bytes(0, 128, 256, L.RQ_MXFP4)
+    assert ws == 0
+    assert status_of(rq.rq_recurrent_prefill, None, 0, 128, 256, A16, A16, A16, A16, A16, A16, L.RQ_MXFP4, 3, 4,
+                     1e-6, None, 0) in passed
+    assert status_of(rq.rq_pack_nibble_planes, None, None, 0, 64, None, None, None) in passed
+    assert status_of(rq.rq_gemv_nibble_escalate, A16, 4, 64, 0, None, None, None, A16, L.RQ_BOTH, None, 0,
+                     None) in passed
+    assert status_of(rq.rq_gemv_nibble_escalate, None, 4, 64, 0, None, None, None, A16, L.RQ_BOTH, None, 0,
+                     None) == L.RQ_EINVAL  # x [B, K] is not empty
+    assert status_of(rq.rq_kv_quantize, None, 0, 2, 128, None, None) in passed
+    assert status_of(rq.rq_kv_quantize, None, 3, 2, 128, None, None) == L.RQ_EINVAL
