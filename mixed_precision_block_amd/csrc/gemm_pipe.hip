@@ -73,6 +73,13 @@ __device__ __forceinline__ int swz(int r) {
   return ((r ^ (r >> 3)) & 1) | ((r >> 1) & 2) | ((r << 1) & 4);
 }
 
+// Two floats to packed BF16 (lo in bits 15:0) by the hardware conversion:
+// round to nearest even, the same result as f32_to_bf16 for finite values.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, (bf16x2){(__bf16)lo, (__bf16)hi});
+}
+
 // One wave-wide direct load into LDS: lane l's 16 (4) bytes land at
 // lds + 16 l (4 l).
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
@@ -348,17 +355,16 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
             *reinterpret_cast<float4*>(dst) =
                 float4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
           } else {
-            uint32_t b[4];
+            uint32_t b[2];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              uint32_t v = f32_to_bf16(acc[i][j][4 * g + t]);
+            for (int t = 0; t < 2; ++t) {
+              b[t] = pack_bf16(acc[i][j][4 * g + 2 * t], acc[i][j][4 * g + 2 * t + 1]);
               if constexpr (EPI == kEpiSiluBf16) {
-                const float z = bf16_to_f32(v);
-                v = f32_to_bf16(z / (1.0f + expf(-z)));
+                const float z0 = bf16_to_f32(b[t] & 0xFFFFu), z1 = bf16_to_f32(b[t] >> 16);
+                b[t] = pack_bf16(z0 / (1.0f + expf(-z0)), z1 / (1.0f + expf(-z1)));
               }
-              b[t] = v;
             }
-            *reinterpret_cast<uint2*>(dst) = uint2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+            *reinterpret_cast<uint2*>(dst) = uint2{b[0], b[1]};
           }
         }
       }
@@ -397,9 +403,8 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const uint32_t lo = f32_to_bf16(bf16_to_f32(h[e] & 0xFFFFu) + bf16_to_f32(w[e] & 0xFFFFu));
-              const uint32_t hi = f32_to_bf16(bf16_to_f32(h[e] >> 16) + bf16_to_f32(w[e] >> 16));
-              w[e] = lo | (hi << 16);
+              w[e] = pack_bf16(bf16_to_f32(h[e] & 0xFFFFu) + bf16_to_f32(w[e] & 0xFFFFu),
+                               bf16_to_f32(h[e] >> 16) + bf16_to_f32(w[e] >> 16));
             }
           }
           if (whole) {
