@@ -215,17 +215,20 @@ __global__ __launch_bounds__(256) void gemv_low_kernel(const uint16_t* __restric
                        gridDim.y);
 }
 
-// Escalation: workgroup z takes the flagged tokens of rank 4z .. 4z + 3
-// (ranks in token order); groups past the last flagged token exit at once.
+// Escalation: a workgroup takes the flagged tokens in groups of four (in
+// token order), one group after another; with none flagged it exits.
 constexpr int kEscTokens = 4;
 
-// The flagged tokens of rank 4 z .. 4 z + 3 (wave-uniform); returns their
-// count, 0 when none is left for this group.
-__device__ __forceinline__ int flagged_group(const uint8_t* __restrict__ flags, int B, int z, int tok[kEscTokens]) {
+// Bit t set for each flagged token t < B (wave-uniform).
+__device__ __forceinline__ uint32_t flag_mask(const uint8_t* __restrict__ flags, int B) {
   uint32_t fmask = 0;
   for (int t = 0; t < B; ++t) fmask |= (flags[t] != 0 ? 1u : 0u) << t;
-  fmask = __builtin_amdgcn_readfirstlane(fmask);
-  for (int r = 0; r < kEscTokens * z; ++r) fmask &= fmask - 1u;  // drop earlier groups
+  return __builtin_amdgcn_readfirstlane(fmask);
+}
+
+// Takes the next (up to) four flagged tokens off fmask into tok; returns
+// their count, 0 when none is left.
+__device__ __forceinline__ int next_group(uint32_t& fmask, int tok[kEscTokens]) {
   int nt = 0;
 #pragma unroll
   for (int t = 0; t < kEscTokens; ++t) {
@@ -321,12 +324,11 @@ __global__ __launch_bounds__(256) void gemv_escalate_wave_kernel(const uint16_t*
                                                                  const uint16_t* __restrict__ sc,
                                                                  const uint8_t* __restrict__ flags,
                                                                  uint16_t* __restrict__ y) {
-  int tok[kEscTokens];
-  const int nt = flagged_group(flags, B, blockIdx.z, tok);
-  if (nt == 0) return;
   const int tile = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   if (tile >= (N + 63) / 64) return;
-  escalate_wave_tile(x, K, N, hi, lo, sc, tok, nt, y, tile);
+  uint32_t fmask = flag_mask(flags, B);
+  int tok[kEscTokens];
+  for (int nt; (nt = next_group(fmask, tok)) > 0;) escalate_wave_tile(x, K, N, hi, lo, sc, tok, nt, y, tile);
 }
 
 __global__ __launch_bounds__(256) void gemv_escalate_kernel(const uint16_t* __restrict__ x, int B, int K, int N,
@@ -338,20 +340,22 @@ __global__ __launch_bounds__(256) void gemv_escalate_kernel(const uint16_t* __re
                                                             int staged) {
   extern __shared__ uint4 xst[];  // the flagged tokens' x of this slice, when staged
   __shared__ float red[4][kEscTokens][64];
+  uint32_t fmask = flag_mask(flags, B);
   int tok[kEscTokens];
-  const int nt = flagged_group(flags, B, blockIdx.z, tok);
-  if (nt == 0) return;  // nothing (more) flagged: no weight traffic
-  uint4* xs = nullptr;
-  if (staged) {
-    const int nb = K >> 5, per = (nb + (int)gridDim.y - 1) / (int)gridDim.y;
-    const int b0 = (int)blockIdx.y * per, b1 = min(nb, b0 + per);
-    if (b0 < b1) {
-      stage_x(xst, x, K, tok, nt, b0, b1);
-      xs = xst;
+  for (int nt; (nt = next_group(fmask, tok)) > 0;) {  // nothing (more) flagged: no weight traffic
+    uint4* xs = nullptr;
+    if (staged) {
+      const int nb = K >> 5, per = (nb + (int)gridDim.y - 1) / (int)gridDim.y;
+      const int b0 = (int)blockIdx.y * per, b1 = min(nb, b0 + per);
+      if (b0 < b1) {
+        stage_x(xst, x, K, tok, nt, b0, b1);
+        xs = xst;
+      }
     }
+    gemv_tile<kEscTokens, true>(x, B, K, N, hi, lo, sc, tok, nt, y, ws, red, xs, blockIdx.x, blockIdx.y,
+                                gridDim.y);
+    __syncthreads();  // the next group reuses red and xst
   }
-  gemv_tile<kEscTokens, true>(x, B, K, N, hi, lo, sc, tok, nt, y, ws, red, xs, blockIdx.x, blockIdx.y,
-                              gridDim.y);
 }
 
 // y[t][n] = BF16(sum over slices of ws[slice][t][n]) in slice order, for
@@ -402,18 +406,21 @@ __global__ __launch_bounds__(256) void gemv_escalate_grouped_kernel(const rq_gem
                                                                     int count, int B,
                                                                     const uint8_t* __restrict__ flags) {
   __shared__ float red[4][kEscTokens][64];
-  int tok[kEscTokens];
-  const int nt = flagged_group(flags, B, blockIdx.z, tok);
-  if (nt == 0) return;
+  uint32_t fmask = flag_mask(flags, B);
+  if (fmask == 0) return;
   const rq_gemv_problem* p = find_problem(probs, count, blockIdx.x);
   const int64_t tile = (int64_t)blockIdx.x - p->tile_start;
   // problems without a low plane take no escalation
   if (p->w_lo == nullptr || tile < 0 || tile >= (p->N + 63) / 64) return;
   // four waves per tile: the sweep's 7750 tiles as one wave each would be a
   // single round whose K = 3072 tiles set the end
-  gemv_tile<kEscTokens, true>(static_cast<const uint16_t*>(p->x_bf16), B, (int)p->K, (int)p->N, p->w_hi, p->w_lo,
-                              p->scales_tiled, tok, nt, static_cast<uint16_t*>(p->y_bf16), nullptr, red, nullptr,
-                              (int)tile, 0, 1);
+  int tok[kEscTokens];
+  for (int nt; (nt = next_group(fmask, tok)) > 0;) {
+    gemv_tile<kEscTokens, true>(static_cast<const uint16_t*>(p->x_bf16), B, (int)p->K, (int)p->N, p->w_hi,
+                                p->w_lo, p->scales_tiled, tok, nt, static_cast<uint16_t*>(p->y_bf16), nullptr, red,
+                                nullptr, (int)tile, 0, 1);
+    __syncthreads();  // the next group reuses red
+  }
 }
 
 // One thread per (padded row, 32-block): 32 int8 weights -> one 16-byte
@@ -516,12 +523,9 @@ hipError_t launch_gemv_escalate(const uint16_t* x, int64_t B, int64_t K, int64_t
   const int ns = slices_for(B, N, K, ws_bytes);
   const int b = (int)B, k = (int)K, n = (int)N;
   float* w = static_cast<float*>(ws);
-  // up to four groups of four flagged tokens
-  const unsigned groups = (unsigned)((B + kEscTokens - 1) / kEscTokens);
   if (ns == 1 && tiles >= 2048) {
     // enough tiles for one wave each: no cross-wave reduction
-    gemv_escalate_wave_kernel<<<dim3((tiles + 3) / 4, 1, groups), 256, 0, stream>>>(x, b, k, n, hi, lo, scales,
-                                                                                     flags, y);
+    gemv_escalate_wave_kernel<<<(tiles + 3) / 4, 256, 0, stream>>>(x, b, k, n, hi, lo, scales, flags, y);
     return hipGetLastError();
   }
   // four waves per tile; the flagged tokens' x of the slice staged in LDS
@@ -529,7 +533,7 @@ hipError_t launch_gemv_escalate(const uint16_t* x, int64_t B, int64_t K, int64_t
   const int64_t nb = K / 32, per = (nb + ns - 1) / ns;
   const int staged = per * 32 <= kXStageElems ? 1 : 0;
   const size_t shm = staged ? (size_t)kEscTokens * per * 32 * 2 : 0;
-  const dim3 grid3(tiles, ns, groups);
+  const dim3 grid3(tiles, ns);
   gemv_escalate_kernel<<<grid3, 256, shm, stream>>>(x, b, k, n, hi, lo, scales, flags, y, w, staged);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && ns > 1) e = launch_reduce(w, ns, B, N, flags, y, stream);
@@ -552,8 +556,7 @@ hipError_t launch_gemv_grouped(const rq_gemv_problem* probs, int count, int64_t 
     if (e != hipSuccess) return e;
   }
   if (phase & 2) {
-    const dim3 grid((unsigned)total_tiles, 1, (unsigned)((B + kEscTokens - 1) / kEscTokens));
-    gemv_escalate_grouped_kernel<<<grid, 256, 0, stream>>>(probs, count, b, flags);
+    gemv_escalate_grouped_kernel<<<(unsigned)total_tiles, 256, 0, stream>>>(probs, count, b, flags);
     return hipGetLastError();
   }
   return hipSuccess;
