@@ -73,13 +73,6 @@ __device__ __forceinline__ int swz(int r) {
   return ((r ^ (r >> 3)) & 1) | ((r >> 1) & 2) | ((r << 1) & 4);
 }
 
-// Two floats to packed BF16 (lo in bits 15:0) by the hardware conversion:
-// round to nearest even, the same result as f32_to_bf16 for finite values.
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, (bf16x2){(__bf16)lo, (__bf16)hi});
-}
-
 // One wave-wide direct load into LDS: lane l's 16 (4) bytes land at
 // lds + 16 l (4 l).
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {

@@ -37,23 +37,16 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict
   for (int c = threadIdx.x; c < chunks; c += 256) {
     const uint4 q = *reinterpret_cast<const uint4*>(hr + c * 8);
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-    uint32_t v[8];
+    uint32_t pw[4];  // the normalized pairs, BF16
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = f32_to_bf16(bf16_to_f32(w[i] & 0xFFFFu) * inv);
-      v[2 * i + 1] = f32_to_bf16(bf16_to_f32(w[i] >> 16) * inv);
-    }
+    for (int i = 0; i < 4; ++i) pw[i] = pack_bf16(bf16_to_f32(w[i] & 0xFFFFu) * inv, bf16_to_f32(w[i] >> 16) * inv);
+    const uint4 pk = make_uint4(pw[0], pw[1], pw[2], pw[3]);
     if constexpr (FMT == 3) {
-      *reinterpret_cast<uint4*>(out + (row * D + c * 8) * 2) =
-          make_uint4(v[0] | v[1] << 16, v[2] | v[3] << 16, v[4] | v[5] << 16, v[6] | v[7] << 16);
+      *reinterpret_cast<uint4*>(out + (row * D + c * 8) * 2) = pk;
     } else {
       using Fm = typename std::conditional<FMT == 1, FmtE2M1, FmtE4M3>::type;
-      uint32_t m = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) m = max(m, v[i] & 0x7FFFu);
-      m = quad_max(m);  // the quad is active together: chunks % 4 == 0
+      const uint32_t m = quad_max(amax8(pk));  // the quad is active together: chunks % 4 == 0
       const uint32_t sb = (uint32_t)(mx_block_exp<Fm>(m) + 127);
-      const uint4 pk = make_uint4(v[0] | v[1] << 16, v[2] | v[3] << 16, v[4] | v[5] << 16, v[6] | v[7] << 16);
       if constexpr (FMT == 1)
         *reinterpret_cast<uint32_t*>(out + row * (D / 2) + c * 4) = cvt8_e2m1(pk, e8m0_to_f32(sb));
       else

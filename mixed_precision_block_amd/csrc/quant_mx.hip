@@ -180,12 +180,19 @@ __global__ __launch_bounds__(256) void arc_frontend_kernel(const uint16_t* __res
       if (c >= chunks) break;
       uint32_t v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t b = (p[i][e] >= 0 && p[i][e] < K) ? (uint32_t)rh[p[i][e]] : 0u;
-        if constexpr (kNorm) b = f32_to_bf16(bf16_to_f32(b) * inv);
-        v[e] = b;
+      for (int e = 0; e < 8; ++e) v[e] = (p[i][e] >= 0 && p[i][e] < K) ? (uint32_t)rh[p[i][e]] : 0u;
+      uint4 qv;
+      if constexpr (kNorm) {
+        qv = make_uint4(pack_bf16(bf16_to_f32(v[0]) * inv, bf16_to_f32(v[1]) * inv),
+                        pack_bf16(bf16_to_f32(v[2]) * inv, bf16_to_f32(v[3]) * inv),
+                        pack_bf16(bf16_to_f32(v[4]) * inv, bf16_to_f32(v[5]) * inv),
+                        pack_bf16(bf16_to_f32(v[6]) * inv, bf16_to_f32(v[7]) * inv));
+        const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (qw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+      } else {
+        qv = pack8(v);
       }
-      const uint4 qv = pack8(v);
       const uint32_t sb = (uint32_t)(mx_block_exp<Fmt>(quad_max(amax8(qv))) + 127);
       const uint2 cv = encode8<Fmt>(qv, sb);
       store8<Fmt>(cv, codes + row * ldc + (int64_t)c * 4 * kElemBytesNum);

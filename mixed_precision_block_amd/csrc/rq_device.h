@@ -47,6 +47,14 @@ RQ_HD uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
+// Two floats to packed BF16 (lo in bits 15:0) by the hardware conversion
+// (v_cvt_pk_bf16_f32): round to nearest even, the same bits as f32_to_bf16
+// for finite values.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, (bf16x2_t){(__bf16)lo, (__bf16)hi});
+}
+
 // Block exponent from the 15-bit magnitude bits of the block amax.
 template <class Fmt>
 RQ_HD int mx_block_exp(uint32_t amax_bits) {
