@@ -680,6 +680,15 @@ def measure_gemv(torch, np, api, L, W, dev):
     def esc_bytes(N, K, nf):
         return N * K + N * K // 32 * 2 + nf * K * 2 + nf * N * 2
 
+    # with the FP32 carry: the low pass also writes every row's FP32 sum; the
+    # escalation reads the lo plane, the scales, the flagged rows' x and
+    # carry, and writes their y
+    def low_carry_bytes(N, K):
+        return low_bytes(N, K) + B * N * 4
+
+    def esc_lo_bytes(N, K, nf):
+        return N * K // 2 + N * K // 32 * 2 + nf * K * 2 + nf * N * 2 + nf * N * 4
+
     # LM head alone, low pass; four rotating copies so the 256 MB MALL does not serve it
     N, K, p = planes[-1]
     copies = [p] + [tuple(t.clone() for t in p) for _ in range(3)]
@@ -688,7 +697,7 @@ def measure_gemv(torch, np, api, L, W, dev):
     def lm_low():
         c = copies[it[0] % 4]
         it[0] += 1
-        L.rq_gemv_nibble_escalate(xs[K], B, K, N, c[0], c[1], c[2], None, L.RQ_LOW, wsp, wsb, ys[N])
+        L.rq_gemv_nibble_escalate(xs[K], B, K, N, c[0], c[1], c[2], None, L.RQ_LOW, wsp, wsb, None, ys[N])
 
     ms = time_calls(torch, lm_low, 40)
     gb = low_bytes(N, K) / (ms * 1e-3) / 1e9
@@ -700,18 +709,41 @@ def measure_gemv(torch, np, api, L, W, dev):
     def lm_esc():
         c = copies[it[0] % 4]
         it[0] += 1
-        L.rq_gemv_nibble_escalate(xs[K], B, K, N, c[0], c[1], c[2], flags, L.RQ_ESCALATE, wsp, wsb, ys[N])
+        L.rq_gemv_nibble_escalate(xs[K], B, K, N, c[0], c[1], c[2], flags, L.RQ_ESCALATE, wsp, wsb, None, ys[N])
 
     ms = time_calls(torch, lm_esc, 40)
     gb = esc_bytes(N, K, nf_lm) / (ms * 1e-3) / 1e9
     out["gemv_lm_head_escalation_2_of_16"] = {"us": round(ms * 1e3, 2), "gb_s": round(gb, 1),
                                               "frac_hbm": round(gb * 1e9 / PEAK["hbm"], 4),
                                               "bytes": esc_bytes(N, K, nf_lm)}
-    del copies
+    # the same two passes through the FP32 carry (the copies hold the same
+    # weights, so one carry serves them all)
+    carry = torch.empty((B, N), dtype=torch.float32, device=dev)
+
+    def lm_low_carry():
+        c = copies[it[0] % 4]
+        it[0] += 1
+        L.rq_gemv_nibble_escalate(xs[K], B, K, N, c[0], c[1], c[2], None, L.RQ_LOW, wsp, wsb, carry, ys[N])
+
+    def lm_esc_lo():
+        c = copies[it[0] % 4]
+        it[0] += 1
+        L.rq_gemv_nibble_escalate(xs[K], B, K, N, None, c[1], c[2], flags, L.RQ_ESCALATE, wsp, wsb, carry, ys[N])
+
+    ms = time_calls(torch, lm_low_carry, 40)
+    out["gemv_lm_head_low_pass_b16_with_carry"] = {
+        "us": round(ms * 1e3, 2), "gb_s": round(low_carry_bytes(N, K) / (ms * 1e-3) / 1e9, 1),
+        "frac_hbm": round(low_carry_bytes(N, K) / (ms * 1e-3) / PEAK["hbm"], 4), "bytes": low_carry_bytes(N, K)}
+    ms = time_calls(torch, lm_esc_lo, 40)
+    out["gemv_lm_head_escalation_2_of_16_lo_plane_from_carry"] = {
+        "us": round(ms * 1e3, 2), "gb_s": round(esc_lo_bytes(N, K, nf_lm) / (ms * 1e-3) / 1e9, 1),
+        "frac_hbm": round(esc_lo_bytes(N, K, nf_lm) / (ms * 1e-3) / PEAK["hbm"], 4),
+        "bytes": esc_lo_bytes(N, K, nf_lm)}
+    del copies, carry
 
     def sweep(phase):
         for N, K, (hi, lo, st) in planes:
-            L.rq_gemv_nibble_escalate(xs[K], B, K, N, hi, lo, st, flags, phase, wsp, wsb, ys[N])
+            L.rq_gemv_nibble_escalate(xs[K], B, K, N, hi, lo, st, flags, phase, wsp, wsb, None, ys[N])
 
     tot_low = sum(low_bytes(N, K) for N, K, _ in planes)
     nf = int(flags.sum().item())
@@ -737,7 +769,7 @@ def measure_gemv(torch, np, api, L, W, dev):
         "frac_hbm": round(tot_esc / (ms_esc_g * 1e-3) / PEAK["hbm"], 4), "bytes": tot_esc}
     del graphs
     # the same sweeps as one grouped launch per phase (a problem table in
-    # device memory; no split-K: the 197 problems give 7302 row tiles)
+    # device memory; no split-K: the 197 problems give 7750 row tiles)
     gys = [torch.empty((B, N), dtype=torch.bfloat16, device=dev) for N, _, _ in planes]
     table = api.gemv_group([(xs[K], p, y) for (N, K, p), y in zip(planes, gys)], dev)
     ms_low_grp = time_calls(torch, lambda: api.gemv_nibble_escalate_grouped(table, B, None, L.RQ_LOW), 10)
@@ -749,7 +781,21 @@ def measure_gemv(torch, np, api, L, W, dev):
     out["gemv_full_sweep_escalation_2_of_16_grouped"] = {
         "us": round(ms_esc_grp * 1e3, 1), "gb_s": round(tot_esc / (ms_esc_grp * 1e-3) / 1e9, 1),
         "frac_hbm": round(tot_esc / (ms_esc_grp * 1e-3) / PEAK["hbm"], 4), "bytes": tot_esc}
-    del table, gys
+    del table
+    # grouped, through the FP32 carries: the escalation reads only the lo planes
+    carries = [torch.empty((B, N), dtype=torch.float32, device=dev) for N, _, _ in planes]
+    table = api.gemv_group([(xs[K], p, y, c) for (N, K, p), y, c in zip(planes, gys, carries)], dev)
+    tot_low_c = sum(low_carry_bytes(N, K) for N, K, _ in planes)
+    tot_esc_lo = sum(esc_lo_bytes(N, K, nf) for N, K, _ in planes)
+    ms_low_c = time_calls(torch, lambda: api.gemv_nibble_escalate_grouped(table, B, None, L.RQ_LOW), 10)
+    ms_esc_lo = time_calls(torch, lambda: api.gemv_nibble_escalate_grouped(table, B, flags, L.RQ_ESCALATE), 10)
+    out["gemv_full_sweep_197_linears_low_pass_b16_grouped_with_carry"] = {
+        "us": round(ms_low_c * 1e3, 1), "gb_s": round(tot_low_c / (ms_low_c * 1e-3) / 1e9, 1),
+        "frac_hbm": round(tot_low_c / (ms_low_c * 1e-3) / PEAK["hbm"], 4), "bytes": tot_low_c}
+    out["gemv_full_sweep_escalation_2_of_16_grouped_lo_plane_from_carry"] = {
+        "us": round(ms_esc_lo * 1e3, 1), "gb_s": round(tot_esc_lo / (ms_esc_lo * 1e-3) / 1e9, 1),
+        "frac_hbm": round(tot_esc_lo / (ms_esc_lo * 1e-3) / PEAK["hbm"], 4), "bytes": tot_esc_lo}
+    del table, gys, carries
     out["gemv_full_sweep_197_linears_low_pass_b16"] = {
         "us": round(ms_low * 1e3, 1), "gb_s": round(tot_low / (ms_low * 1e-3) / 1e9, 1),
         "frac_hbm": round(tot_low / (ms_low * 1e-3) / PEAK["hbm"], 4), "bytes": tot_low,

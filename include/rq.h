@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define RQ_ABI_VERSION 1
+#define RQ_ABI_VERSION 2
 
 typedef enum {
   RQ_OK = 0,
@@ -256,6 +256,14 @@ rq_status rq_pack_nibble_planes(const int8_t *w, const uint16_t *scales_f16,
  * tiles split K over more workgroups; NULL / smaller runs them unsplit.
  * The result is the same bits either way only up to FP32 summation
  * order; a given (shape, workspace) choice is deterministic.
+ * y_f32: optional FP32 carry [B x N] (caller-owned, 4-byte aligned, NULL
+ * for none).  RQ_LOW with it also stores every row's unrounded FP32 sum.
+ * RQ_ESCALATE with it takes those sums as the hi part -- they must come
+ * from an RQ_LOW on the same x, planes, shape and workspace choice, with
+ * this y_f32 -- and reads only the lo plane (half the bytes):
+ * y[t,n] = BF16(y_f32[t,n] + sum_b s[n,b] sum_k lo[n,k] x[t,k]), exact
+ * in real arithmetic because w = 16*hi + lo; w_hi may then be NULL for
+ * RQ_ESCALATE alone.  The flagged rows of y_f32 are left unchanged.
  */
 size_t rq_gemv_workspace_bytes(int64_t B, int64_t N, int64_t K);
 rq_status rq_gemv_nibble_escalate(const void *x_bf16, int64_t B, int64_t K,
@@ -264,7 +272,7 @@ rq_status rq_gemv_nibble_escalate(const void *x_bf16, int64_t B, int64_t K,
                                   const uint16_t *scales_tiled,
                                   const uint8_t *flags, int phase,
                                   void *workspace, size_t ws_bytes,
-                                  void *y_bf16, void *stream);
+                                  float *y_f32, void *y_bf16, void *stream);
 
 /*
  * Grouped decode GEMV: one launch over many independent problems (the same
@@ -273,7 +281,8 @@ rq_status rq_gemv_nibble_escalate(const void *x_bf16, int64_t B, int64_t K,
  *
  * rq_gemv_problem: one problem; pointers as for rq_gemv_nibble_escalate
  * (every x holds the same B tokens; w_lo may be NULL, and such a problem
- * then takes only the low pass: the escalation skips it).  tile_start is
+ * then takes only the low pass: the escalation skips it; y_f32 is the
+ * optional carry, with the same meaning per problem).  tile_start is
  * filled by rq_gemv_group_plan.
  *
  * rq_gemv_group_plan (host): validates every entry (non-NULL x, w_hi,
@@ -296,6 +305,7 @@ typedef struct rq_gemv_problem {
   const uint8_t *w_lo;          /* lo plane, or NULL for RQ_LOW only */
   const uint16_t *scales_tiled; /* tiled FP16 scales */
   void *y_bf16;                 /* [B x N] BF16 */
+  float *y_f32;                 /* optional FP32 carry [B x N], or NULL */
   int64_t N, K;
   int64_t tile_start;           /* set by rq_gemv_group_plan */
 } rq_gemv_problem;

@@ -32,8 +32,8 @@ class RQError(RuntimeError):
 class RqGemvProblem(ctypes.Structure):
     """rq_gemv_problem: one problem of a grouped GEMV launch (include/rq.h)."""
     _fields_ = [("x_bf16", ctypes.c_void_p), ("w_hi", ctypes.c_void_p), ("w_lo", ctypes.c_void_p),
-                ("scales_tiled", ctypes.c_void_p), ("y_bf16", ctypes.c_void_p), ("N", ctypes.c_int64),
-                ("K", ctypes.c_int64), ("tile_start", ctypes.c_int64)]
+                ("scales_tiled", ctypes.c_void_p), ("y_bf16", ctypes.c_void_p), ("y_f32", ctypes.c_void_p),
+                ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("tile_start", ctypes.c_int64)]
 
 
 _P = ctypes.c_void_p
@@ -63,7 +63,7 @@ _SIGNATURES = {
     "rq_nibble_scale_bytes": (_SZ, [_I64, _I64]),
     "rq_pack_nibble_planes": (_INT, [_P, _P, _I64, _I64, _P, _P, _P, _P]),
     "rq_gemv_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
-    "rq_gemv_nibble_escalate": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _INT, _P, _SZ, _P, _P]),
+    "rq_gemv_nibble_escalate": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _INT, _P, _SZ, _P, _P, _P]),
     "rq_gemv_group_plan": (_I64, [ctypes.POINTER(RqGemvProblem), _INT]),
     "rq_gemv_nibble_escalate_grouped": (_INT, [_P, _INT, _I64, _I64, _P, _INT, _P]),
     "rq_escalation_gate": (_INT, [_P, _I64, _I64, _F, _F, _P, _P, _P]),
@@ -71,6 +71,9 @@ _SIGNATURES = {
 }
 
 _lib = None
+
+# The RQ_ABI_VERSION these signatures and RqGemvProblem follow (include/rq.h).
+ABI_VERSION = 2
 
 
 def lib():
@@ -85,6 +88,9 @@ def lib():
             fn = getattr(handle, name)
             fn.restype = res
             fn.argtypes = args
+        if handle.rq_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"librq.so has ABI version {handle.rq_abi_version()}, this binding expects "
+                               f"{ABI_VERSION}; rebuild it with `python -m mixed_precision_block_amd.build`")
         _lib = handle
     return _lib
 
@@ -182,11 +188,11 @@ def rq_gemv_workspace_bytes(B, N, K):
     return lib().rq_gemv_workspace_bytes(B, N, K)
 
 
-def rq_gemv_nibble_escalate(x, B, K, N, w_hi, w_lo, scales_tiled, flags, phase, workspace, ws_bytes, y,
+def rq_gemv_nibble_escalate(x, B, K, N, w_hi, w_lo, scales_tiled, flags, phase, workspace, ws_bytes, y_f32, y,
                             stream=None):
     _check("rq_gemv_nibble_escalate",
            lib().rq_gemv_nibble_escalate(_ptr(x), B, K, N, _ptr(w_hi), _ptr(w_lo), _ptr(scales_tiled), _ptr(flags),
-                                         phase, _ptr(workspace), ws_bytes, _ptr(y), _stream(stream)))
+                                         phase, _ptr(workspace), ws_bytes, _ptr(y_f32), _ptr(y), _stream(stream)))
 
 
 def rq_gemv_group_plan(problems):

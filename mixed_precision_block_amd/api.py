@@ -117,27 +117,33 @@ def pack_nibble_planes(w, scales_f16, stream=None):
     return hi, lo, st
 
 
-def gemv_nibble_escalate(x, N, planes, flags=None, phase=L.RQ_BOTH, y=None, stream=None, split=True):
-    """split=False runs every shape unsplit (no workspace)."""
+def gemv_nibble_escalate(x, N, planes, flags=None, phase=L.RQ_BOTH, y=None, stream=None, split=True, carry=None):
+    """split=False runs every shape unsplit (no workspace).  carry: an FP32
+    [B x N] tensor the low pass fills and a later escalation starts from
+    (reading only the lo plane); the same split choice on both calls."""
     B, K = x.shape
     hi, lo, st = planes
     if y is None:
         y = torch.empty((B, N), dtype=torch.bfloat16, device=x.device)
     wsb = L.rq_gemv_workspace_bytes(B, N, K) if split else 0
     ws = _u8((wsb,), x.device) if wsb else None
-    L.rq_gemv_nibble_escalate(x, B, K, N, hi, lo, st, flags, phase, ws, wsb, y, stream)
+    L.rq_gemv_nibble_escalate(x, B, K, N, hi, lo, st, flags, phase, ws, wsb, carry, y, stream)
     return y
 
 
 def gemv_group(problems, device="cuda"):
-    """Plan a grouped GEMV: problems is a list of (x, planes, y) with x [B x K]
-    BF16, planes from pack_nibble_planes, y [B x N].  Returns (table on the
+    """Plan a grouped GEMV: problems is a list of (x, planes, y) or (x,
+    planes, y, carry) with x [B x K] BF16, planes from pack_nibble_planes,
+    y [B x N] and the optional FP32 carry [B x N].  Returns (table on the
     device, count, total tiles) for gemv_nibble_escalate_grouped; the table
     refers to the tensors, which must outlive it."""
     arr = (L.RqGemvProblem * len(problems))()
-    for i, (x, (hi, lo, st), y) in enumerate(problems):
+    for i, prob in enumerate(problems):
+        x, (hi, lo, st), y = prob[:3]
+        carry = prob[3] if len(prob) > 3 else None
         arr[i] = L.RqGemvProblem(x.data_ptr(), hi.data_ptr(), lo.data_ptr() if lo is not None else None,
-                                 st.data_ptr(), y.data_ptr(), y.shape[1], x.shape[1], 0)
+                                 st.data_ptr(), y.data_ptr(), carry.data_ptr() if carry is not None else None,
+                                 y.shape[1], x.shape[1], 0)
     total = L.rq_gemv_group_plan(arr)
     host = torch.frombuffer(bytearray(bytes(arr)), dtype=torch.uint8)
     return host.to(device), len(problems), total

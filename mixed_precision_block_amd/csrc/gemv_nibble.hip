@@ -17,10 +17,15 @@
 // 32-blocks of K; per block each lane turns its 16 bytes into 16 exact BF16
 // pairs once and reuses them for every token (low pass: the block's x for
 // all tokens is one coalesced 1 KiB load per wave, broadcast through LDS;
-// escalation: the few flagged tokens' x come through the scalar cache, the
-// address being wave-uniform).  FP32 block partials are scaled by
+// escalation: the few flagged tokens' x are copied to LDS by the workgroup
+// where they fit, else come through the scalar cache, the address being
+// wave-uniform).  FP32 block partials are scaled by
 // the block's FP16 scale and accumulated; the four waves' sums are added in
 // a fixed order through LDS.
+//
+// Carry: the low pass can also keep its FP32 sums in a caller buffer.  As
+// w = 16 hi + lo, an escalation that starts from those sums needs only the
+// lo plane: y = sum_b s sum_k 16 hi x + sum_b s sum_k lo x.
 #include "../../include/rq.h"
 #include "rq_device.h"
 #include "rq_internal.h"
@@ -70,6 +75,14 @@ __device__ __forceinline__ void unpack_hi16(const uint4 d, bf16x2 wp[16]) {
   for (int q = 0; q < 4; ++q) pairs_from_bytes((dq[q] << 4) & 0xF0F0F0F0u, dq[q] & 0xF0F0F0F0u, wp + 4 * q);
 }
 
+// lo (0..15) for the 16 pairs of a lo-plane chunk: each nibble in the low
+// half of its byte.
+__device__ __forceinline__ void unpack_lo16(const uint4 d, bf16x2 wp[16]) {
+  const uint32_t dq[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) pairs_from_bytes(dq[q] & 0x0F0F0F0Fu, (dq[q] >> 4) & 0x0F0F0F0Fu, wp + 4 * q);
+}
+
 // Full 8-bit weights: byte (hi << 4 | lo) of a nibble position is the
 // int8 weight.
 __device__ __forceinline__ void unpack_full(const uint4 dh, const uint4 dl, bf16x2 wp[16]) {
@@ -81,22 +94,28 @@ __device__ __forceinline__ void unpack_full(const uint4 dh, const uint4 dl, bf16
                      (h[q] & 0xF0F0F0F0u) | ((l[q] >> 4) & 0x0F0F0F0Fu), wp + 4 * q);
 }
 
-// Both passes share one loop: a workgroup owns 64 rows and the K-blocks
+// Planes a pass reads: the low pass the hi plane; the escalation both, or
+// only lo when it starts from the low pass's FP32 carry.
+enum Planes { kHi = 0, kHiLo = 1, kLo = 2 };
+
+// Every pass shares one loop: a workgroup owns 64 rows and the K-blocks
 // [b0, b1) of its slice (grid y splits K when there are too few row tiles
 // to fill the chip); wave w takes blocks b0 + w, b0 + w + 4, ...  The
 // workgroup computes TB accumulator slots; slot t is token tok[t] for
 // t < nt.  The four waves' sums meet in LDS in a fixed order; with one
-// slice the workgroup writes BF16 outputs, otherwise FP32 partials to
+// slice the workgroup writes BF16 outputs (kHi: also the FP32 carry yf
+// when given; kLo: adds the carry first), otherwise FP32 partials to
 // ws[slice][token][row] (16 token rows per slice) that gemv_reduce_kernel
 // adds in slice order.
 constexpr int kWsTokens = 16;
 
-template <int TB, bool kFull>
+template <int TB, int kP>
 __device__ __forceinline__ void gemv_tile(const uint16_t* __restrict__ x, int B, int K, int N,
                                           const uint8_t* __restrict__ hi, const uint8_t* __restrict__ lo,
                                           const uint16_t* __restrict__ sc, const int* tok, int nt,
-                                          uint16_t* __restrict__ y, float* __restrict__ ws, float (*red)[TB][64],
-                                          uint4* xs, int tile, int slice, int nslice) {
+                                          uint16_t* __restrict__ y, float* __restrict__ yf, float* __restrict__ ws,
+                                          float (*red)[TB][64], uint4* xs, int tile, int slice, int nslice) {
+  constexpr bool kFull = kP != kHi;  // an escalation pass: flagged tokens only
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nb = K >> 5;
@@ -123,7 +142,7 @@ __device__ __forceinline__ void gemv_tile(const uint16_t* __restrict__ x, int B,
   uint4 nh = make_uint4(0, 0, 0, 0), nl = make_uint4(0, 0, 0, 0);
   uint16_t ns = 0;
   if (kFull && b < b1) {
-    nh = hp[(size_t)b * 64];
+    if constexpr (kP != kLo) nh = hp[(size_t)b * 64];
     nl = lp[(size_t)b * 64];
     ns = sp[(size_t)b * 64];
   }
@@ -134,7 +153,7 @@ __device__ __forceinline__ void gemv_tile(const uint16_t* __restrict__ x, int B,
       dh = nh, dl = nl;
       s = f16_to_f32(ns);
       const int bn = b + 4 < b1 ? b + 4 : b;  // the last block reloads itself
-      nh = hp[(size_t)bn * 64];
+      if constexpr (kP != kLo) nh = hp[(size_t)bn * 64];
       nl = lp[(size_t)bn * 64];
       ns = sp[(size_t)bn * 64];
     } else {
@@ -149,8 +168,10 @@ __device__ __forceinline__ void gemv_tile(const uint16_t* __restrict__ x, int B,
       xv = xg[(size_t)bn * 4];
     }
     bf16x2 wp[16];
-    if constexpr (kFull)
+    if constexpr (kP == kHiLo)
       unpack_full(dh, dl, wp);
+    else if constexpr (kP == kLo)
+      unpack_lo16(dl, wp);
     else
       unpack_hi16(dh, wp);
 #pragma unroll
@@ -192,9 +213,14 @@ __device__ __forceinline__ void gemv_tile(const uint16_t* __restrict__ x, int B,
     const int t = o >> 6, l = o & 63;
     const int n = tile * 64 + l;
     if (t >= nt) continue;
-    const float v = ((red[0][t][l] + red[1][t][l]) + red[2][t][l]) + red[3][t][l];
+    float v = ((red[0][t][l] + red[1][t][l]) + red[2][t][l]) + red[3][t][l];
     if (nslice == 1) {
-      if (n < N) y[(size_t)tok[t] * N + n] = (uint16_t)f32_to_bf16(v);
+      if (n < N) {
+        const size_t o = (size_t)tok[t] * N + n;
+        if constexpr (kP == kLo) v = yf[o] + v;
+        if (kP == kHi && yf != nullptr) yf[o] = v;
+        y[o] = (uint16_t)f32_to_bf16(v);
+      }
     } else {
       ws[((size_t)slice * kWsTokens + tok[t]) * ((size_t)((N + 63) / 64) * 64) + n] = v;
     }
@@ -205,14 +231,14 @@ template <int TB>
 __global__ __launch_bounds__(256) void gemv_low_kernel(const uint16_t* __restrict__ x, int B, int K, int N,
                                                        const uint8_t* __restrict__ hi,
                                                        const uint16_t* __restrict__ sc, uint16_t* __restrict__ y,
-                                                       float* __restrict__ ws) {
+                                                       float* __restrict__ yf, float* __restrict__ ws) {
   __shared__ float red[4][TB][64];
   __shared__ uint4 xs[4 * 64];
   int tok[TB];
 #pragma unroll
   for (int t = 0; t < TB; ++t) tok[t] = t;
-  gemv_tile<TB, false>(x, B, K, N, hi, nullptr, sc, tok, B < TB ? B : TB, y, ws, red, xs, blockIdx.x, blockIdx.y,
-                       gridDim.y);
+  gemv_tile<TB, kHi>(x, B, K, N, hi, nullptr, sc, tok, B < TB ? B : TB, y, yf, ws, red, xs, blockIdx.x, blockIdx.y,
+                     gridDim.y);
 }
 
 // Escalation: a workgroup takes the flagged tokens in groups of four (in
@@ -259,11 +285,16 @@ __device__ __forceinline__ void stage_x(uint4* xst, const uint16_t* __restrict__
 // The sum is kept as four partials over the blocks b = w mod 4, combined
 // as ((p0 + p1) + p2) + p3 -- the order of the four-wave tile (gemv_tile
 // with one slice) -- so both give the same bits.  The planes of the next
-// two blocks are in flight; x comes through the scalar cache.
+// two blocks are in flight; x comes through the scalar cache (a workgroup
+// copy of x in LDS made this kernel slower: every workgroup of its single
+// round then waits for the copy before streaming weights).  kP is kHiLo,
+// or kLo starting from the carry yf.
+template <int kP>
 __device__ __forceinline__ void escalate_wave_tile(const uint16_t* __restrict__ x, int K, int N,
                                                    const uint8_t* __restrict__ hi, const uint8_t* __restrict__ lo,
                                                    const uint16_t* __restrict__ sc, const int* tok, int nt,
-                                                   uint16_t* __restrict__ y, int tile) {
+                                                   uint16_t* __restrict__ y, const float* __restrict__ yf,
+                                                   int tile) {
   constexpr int PF = 2;
   const int lane = threadIdx.x & 63;
   const int nb = K >> 5;
@@ -281,7 +312,9 @@ __device__ __forceinline__ void escalate_wave_tile(const uint16_t* __restrict__ 
 #pragma unroll
   for (int f = 0; f < PF; ++f) {
     const int bb = f < nb ? f : nb - 1;
-    ph[f] = hp[(size_t)bb * 64], pl[f] = lp[(size_t)bb * 64], ps[f] = sp[(size_t)bb * 64];
+    ph[f] = make_uint4(0, 0, 0, 0);
+    if constexpr (kP != kLo) ph[f] = hp[(size_t)bb * 64];  // kLo: w_hi may be NULL
+    pl[f] = lp[(size_t)bb * 64], ps[f] = sp[(size_t)bb * 64];
   }
   // four blocks per turn so that the partial index is static
   for (int b4 = 0; b4 < nb; b4 += 4) {
@@ -294,9 +327,13 @@ __device__ __forceinline__ void escalate_wave_tile(const uint16_t* __restrict__ 
 #pragma unroll
       for (int f = 0; f + 1 < PF; ++f) ph[f] = ph[f + 1], pl[f] = pl[f + 1], ps[f] = ps[f + 1];
       const int bn = b + PF < nb ? b + PF : b;  // the last blocks reload themselves
-      ph[PF - 1] = hp[(size_t)bn * 64], pl[PF - 1] = lp[(size_t)bn * 64], ps[PF - 1] = sp[(size_t)bn * 64];
+      if constexpr (kP != kLo) ph[PF - 1] = hp[(size_t)bn * 64];
+      pl[PF - 1] = lp[(size_t)bn * 64], ps[PF - 1] = sp[(size_t)bn * 64];
       bf16x2 wp[16];
-      unpack_full(dh, dl, wp);
+      if constexpr (kP == kLo)
+        unpack_lo16(dl, wp);
+      else
+        unpack_full(dh, dl, wp);
 #pragma unroll
       for (int t = 0; t < kEscTokens; ++t) {
         if (t >= nt) continue;
@@ -311,33 +348,40 @@ __device__ __forceinline__ void escalate_wave_tile(const uint16_t* __restrict__ 
   const int n = tile * 64 + lane;
 #pragma unroll
   for (int t = 0; t < kEscTokens; ++t) {
-    const float v = ((acc[0][t] + acc[1][t]) + acc[2][t]) + acc[3][t];
-    if (t < nt && n < N) y[(size_t)tok[t] * N + n] = (uint16_t)f32_to_bf16(v);
+    float v = ((acc[0][t] + acc[1][t]) + acc[2][t]) + acc[3][t];
+    if (t < nt && n < N) {
+      const size_t o = (size_t)tok[t] * N + n;
+      if constexpr (kP == kLo) v = yf[o] + v;
+      y[o] = (uint16_t)f32_to_bf16(v);
+    }
   }
 }
 
 // Escalation with one wave per tile (large N, unsplit): four tiles per
 // workgroup, no cross-wave reduction.
+template <int kP>
 __global__ __launch_bounds__(256) void gemv_escalate_wave_kernel(const uint16_t* __restrict__ x, int B, int K, int N,
                                                                  const uint8_t* __restrict__ hi,
                                                                  const uint8_t* __restrict__ lo,
                                                                  const uint16_t* __restrict__ sc,
                                                                  const uint8_t* __restrict__ flags,
-                                                                 uint16_t* __restrict__ y) {
+                                                                 uint16_t* __restrict__ y,
+                                                                 const float* __restrict__ yf) {
   const int tile = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   if (tile >= (N + 63) / 64) return;
   uint32_t fmask = flag_mask(flags, B);
   int tok[kEscTokens];
-  for (int nt; (nt = next_group(fmask, tok)) > 0;) escalate_wave_tile(x, K, N, hi, lo, sc, tok, nt, y, tile);
+  for (int nt; (nt = next_group(fmask, tok)) > 0;) escalate_wave_tile<kP>(x, K, N, hi, lo, sc, tok, nt, y, yf, tile);
 }
 
+template <int kP>
 __global__ __launch_bounds__(256) void gemv_escalate_kernel(const uint16_t* __restrict__ x, int B, int K, int N,
                                                             const uint8_t* __restrict__ hi,
                                                             const uint8_t* __restrict__ lo,
                                                             const uint16_t* __restrict__ sc,
                                                             const uint8_t* __restrict__ flags,
-                                                            uint16_t* __restrict__ y, float* __restrict__ ws,
-                                                            int staged) {
+                                                            uint16_t* __restrict__ y, float* __restrict__ yf,
+                                                            float* __restrict__ ws, int staged) {
   extern __shared__ uint4 xst[];  // the flagged tokens' x of this slice, when staged
   __shared__ float red[4][kEscTokens][64];
   uint32_t fmask = flag_mask(flags, B);
@@ -352,23 +396,26 @@ __global__ __launch_bounds__(256) void gemv_escalate_kernel(const uint16_t* __re
         xs = xst;
       }
     }
-    gemv_tile<kEscTokens, true>(x, B, K, N, hi, lo, sc, tok, nt, y, ws, red, xs, blockIdx.x, blockIdx.y,
-                                gridDim.y);
+    gemv_tile<kEscTokens, kP>(x, B, K, N, hi, lo, sc, tok, nt, y, yf, ws, red, xs, blockIdx.x, blockIdx.y,
+                              gridDim.y);
     __syncthreads();  // the next group reuses red and xst
   }
 }
 
 // y[t][n] = BF16(sum over slices of ws[slice][t][n]) in slice order, for
-// every token (flags == nullptr) or the flagged ones.
+// every token (flags == nullptr) or the flagged ones.  carry_in (a lo-only
+// escalation) is added first; carry_out (a low pass) keeps the FP32 sum.
 __global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restrict__ ws, int nslice, int B, int N,
                                                           int Np, const uint8_t* __restrict__ flags,
-                                                          uint16_t* __restrict__ y) {
+                                                          const float* __restrict__ carry_in,
+                                                          float* __restrict__ carry_out, uint16_t* __restrict__ y) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (int64_t)B * N) return;
   const int t = (int)(i / N), n = (int)(i - (int64_t)t * N);
   if (flags && !flags[t]) return;
-  float v = 0.0f;
+  float v = carry_in ? carry_in[i] : 0.0f;
   for (int sl = 0; sl < nslice; ++sl) v += ws[((size_t)sl * kWsTokens + t) * Np + n];
+  if (carry_out) carry_out[i] = v;
   y[i] = (uint16_t)f32_to_bf16(v);
 }
 
@@ -397,15 +444,20 @@ __global__ __launch_bounds__(256) void gemv_low_grouped_kernel(const rq_gemv_pro
   int tok[TB];
 #pragma unroll
   for (int t = 0; t < TB; ++t) tok[t] = t;
-  gemv_tile<TB, false>(static_cast<const uint16_t*>(p->x_bf16), B, (int)p->K, (int)p->N, p->w_hi, nullptr,
-                       p->scales_tiled, tok, B < TB ? B : TB, static_cast<uint16_t*>(p->y_bf16), nullptr, red, xs,
-                       (int)tile, 0, 1);
+  gemv_tile<TB, kHi>(static_cast<const uint16_t*>(p->x_bf16), B, (int)p->K, (int)p->N, p->w_hi, nullptr,
+                     p->scales_tiled, tok, B < TB ? B : TB, static_cast<uint16_t*>(p->y_bf16), p->y_f32, nullptr,
+                     red, xs, (int)tile, 0, 1);
 }
+
+// LDS for the grouped escalation's copy of the flagged tokens' x: problems
+// with K up to this are staged, longer ones read x through the scalar cache.
+constexpr int kGroupStageElems = 2048;
 
 __global__ __launch_bounds__(256) void gemv_escalate_grouped_kernel(const rq_gemv_problem* __restrict__ probs,
                                                                     int count, int B,
                                                                     const uint8_t* __restrict__ flags) {
   __shared__ float red[4][kEscTokens][64];
+  __shared__ uint4 xst[kEscTokens * kGroupStageElems / 8];
   uint32_t fmask = flag_mask(flags, B);
   if (fmask == 0) return;
   const rq_gemv_problem* p = find_problem(probs, count, blockIdx.x);
@@ -414,12 +466,21 @@ __global__ __launch_bounds__(256) void gemv_escalate_grouped_kernel(const rq_gem
   if (p->w_lo == nullptr || tile < 0 || tile >= (p->N + 63) / 64) return;
   // four waves per tile: the sweep's 7750 tiles as one wave each would be a
   // single round whose K = 3072 tiles set the end
+  // with a carry, the low pass's FP32 sums plus the lo plane alone
+  const uint16_t* x = static_cast<const uint16_t*>(p->x_bf16);
+  const int K = (int)p->K;
+  const bool staged = K <= kGroupStageElems;
   int tok[kEscTokens];
   for (int nt; (nt = next_group(fmask, tok)) > 0;) {
-    gemv_tile<kEscTokens, true>(static_cast<const uint16_t*>(p->x_bf16), B, (int)p->K, (int)p->N, p->w_hi,
-                                p->w_lo, p->scales_tiled, tok, nt, static_cast<uint16_t*>(p->y_bf16), nullptr, red,
-                                nullptr, (int)tile, 0, 1);
-    __syncthreads();  // the next group reuses red
+    if (staged) stage_x(xst, x, K, tok, nt, 0, K >> 5);
+    uint4* xs = staged ? xst : nullptr;
+    if (p->y_f32 != nullptr)
+      gemv_tile<kEscTokens, kLo>(x, B, K, (int)p->N, p->w_hi, p->w_lo, p->scales_tiled, tok, nt,
+                                 static_cast<uint16_t*>(p->y_bf16), p->y_f32, nullptr, red, xs, (int)tile, 0, 1);
+    else
+      gemv_tile<kEscTokens, kHiLo>(x, B, K, (int)p->N, p->w_hi, p->w_lo, p->scales_tiled, tok, nt,
+                                   static_cast<uint16_t*>(p->y_bf16), nullptr, nullptr, red, xs, (int)tile, 0, 1);
+    __syncthreads();  // the next group reuses red and xst
   }
 }
 
@@ -488,15 +549,16 @@ static int slices_for(int64_t B, int64_t N, int64_t K, size_t ws_bytes) {
 }
 
 static hipError_t launch_reduce(const float* ws, int nslice, int64_t B, int64_t N, const uint8_t* flags,
-                                uint16_t* y, hipStream_t stream) {
+                                const float* carry_in, float* carry_out, uint16_t* y, hipStream_t stream) {
   const int64_t total = B * N;
-  gemv_reduce_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(ws, nslice, (int)B, (int)N,
-                                                                          (int)((N + 63) / 64 * 64), flags, y);
+  gemv_reduce_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(
+      ws, nslice, (int)B, (int)N, (int)((N + 63) / 64 * 64), flags, carry_in, carry_out, y);
   return hipGetLastError();
 }
 
 hipError_t launch_gemv_low(const uint16_t* x, int64_t B, int64_t K, int64_t N, const uint8_t* hi,
-                           const uint16_t* scales, uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+                           const uint16_t* scales, uint16_t* y, float* yf, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
   const unsigned tiles = (unsigned)((N + 63) / 64);
   if (tiles == 0) return hipSuccess;
   const int ns = slices_for(B, N, K, ws_bytes);
@@ -504,20 +566,20 @@ hipError_t launch_gemv_low(const uint16_t* x, int64_t B, int64_t K, int64_t N, c
   const int b = (int)B, k = (int)K, n = (int)N;
   float* w = static_cast<float*>(ws);
   switch (gemv_tb(B)) {
-    case 1: gemv_low_kernel<1><<<grid, 256, 0, stream>>>(x, b, k, n, hi, scales, y, w); break;
-    case 2: gemv_low_kernel<2><<<grid, 256, 0, stream>>>(x, b, k, n, hi, scales, y, w); break;
-    case 4: gemv_low_kernel<4><<<grid, 256, 0, stream>>>(x, b, k, n, hi, scales, y, w); break;
-    case 8: gemv_low_kernel<8><<<grid, 256, 0, stream>>>(x, b, k, n, hi, scales, y, w); break;
-    default: gemv_low_kernel<16><<<grid, 256, 0, stream>>>(x, b, k, n, hi, scales, y, w); break;
+    case 1: gemv_low_kernel<1><<<grid, 256, 0, stream>>>(x, b, k, n, hi, scales, y, yf, w); break;
+    case 2: gemv_low_kernel<2><<<grid, 256, 0, stream>>>(x, b, k, n, hi, scales, y, yf, w); break;
+    case 4: gemv_low_kernel<4><<<grid, 256, 0, stream>>>(x, b, k, n, hi, scales, y, yf, w); break;
+    case 8: gemv_low_kernel<8><<<grid, 256, 0, stream>>>(x, b, k, n, hi, scales, y, yf, w); break;
+    default: gemv_low_kernel<16><<<grid, 256, 0, stream>>>(x, b, k, n, hi, scales, y, yf, w); break;
   }
   hipError_t e = hipGetLastError();
-  if (e == hipSuccess && ns > 1) e = launch_reduce(w, ns, B, N, nullptr, y, stream);
+  if (e == hipSuccess && ns > 1) e = launch_reduce(w, ns, B, N, nullptr, nullptr, yf, y, stream);
   return e;
 }
 
 hipError_t launch_gemv_escalate(const uint16_t* x, int64_t B, int64_t K, int64_t N, const uint8_t* hi,
                                 const uint8_t* lo, const uint16_t* scales, const uint8_t* flags, uint16_t* y,
-                                void* ws, size_t ws_bytes, hipStream_t stream) {
+                                float* yf, void* ws, size_t ws_bytes, hipStream_t stream) {
   const unsigned tiles = (unsigned)((N + 63) / 64);
   if (tiles == 0) return hipSuccess;
   const int ns = slices_for(B, N, K, ws_bytes);
@@ -525,7 +587,11 @@ hipError_t launch_gemv_escalate(const uint16_t* x, int64_t B, int64_t K, int64_t
   float* w = static_cast<float*>(ws);
   if (ns == 1 && tiles >= 2048) {
     // enough tiles for one wave each: no cross-wave reduction
-    gemv_escalate_wave_kernel<<<(tiles + 3) / 4, 256, 0, stream>>>(x, b, k, n, hi, lo, scales, flags, y);
+    if (yf)
+      gemv_escalate_wave_kernel<kLo><<<(tiles + 3) / 4, 256, 0, stream>>>(x, b, k, n, hi, lo, scales, flags, y, yf);
+    else
+      gemv_escalate_wave_kernel<kHiLo><<<(tiles + 3) / 4, 256, 0, stream>>>(x, b, k, n, hi, lo, scales, flags, y,
+                                                                             nullptr);
     return hipGetLastError();
   }
   // four waves per tile; the flagged tokens' x of the slice staged in LDS
@@ -534,9 +600,13 @@ hipError_t launch_gemv_escalate(const uint16_t* x, int64_t B, int64_t K, int64_t
   const int staged = per * 32 <= kXStageElems ? 1 : 0;
   const size_t shm = staged ? (size_t)kEscTokens * per * 32 * 2 : 0;
   const dim3 grid3(tiles, ns);
-  gemv_escalate_kernel<<<grid3, 256, shm, stream>>>(x, b, k, n, hi, lo, scales, flags, y, w, staged);
+  if (yf)
+    gemv_escalate_kernel<kLo><<<grid3, 256, shm, stream>>>(x, b, k, n, hi, lo, scales, flags, y, yf, w, staged);
+  else
+    gemv_escalate_kernel<kHiLo><<<grid3, 256, shm, stream>>>(x, b, k, n, hi, lo, scales, flags, y, nullptr, w,
+                                                             staged);
   hipError_t e = hipGetLastError();
-  if (e == hipSuccess && ns > 1) e = launch_reduce(w, ns, B, N, flags, y, stream);
+  if (e == hipSuccess && ns > 1) e = launch_reduce(w, ns, B, N, flags, yf, nullptr, y, stream);
   return e;
 }
 

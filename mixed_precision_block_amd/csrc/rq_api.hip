@@ -314,8 +314,10 @@ size_t rq_gemv_workspace_bytes(int64_t B, int64_t N, int64_t K) {
 
 rq_status rq_gemv_nibble_escalate(const void* x_bf16, int64_t B, int64_t K, int64_t N, const uint8_t* w_hi,
                                   const uint8_t* w_lo, const uint16_t* scales_tiled, const uint8_t* flags, int phase,
-                                  void* workspace, size_t ws_bytes, void* y_bf16, void* stream) {
-  if (!x_bf16 || !have(w_hi, N == 0) || !have(scales_tiled, N == 0) || !have(y_bf16, N == 0))
+                                  void* workspace, size_t ws_bytes, float* y_f32, void* y_bf16, void* stream) {
+  // the hi plane is read by the low pass and by an escalation without a carry
+  const bool need_hi = (phase & RQ_LOW) || !y_f32;
+  if (!x_bf16 || (need_hi && !have(w_hi, N == 0)) || !have(scales_tiled, N == 0) || !have(y_bf16, N == 0))
     return fail(RQ_EINVAL, "rq_gemv_nibble_escalate: null pointer");
   if (phase != RQ_LOW && phase != RQ_ESCALATE && phase != RQ_BOTH)
     return fail(RQ_EINVAL, "rq_gemv_nibble_escalate: unknown phase %d", phase);
@@ -326,6 +328,8 @@ rq_status rq_gemv_nibble_escalate(const void* x_bf16, int64_t B, int64_t K, int6
     return fail(RQ_ESHAPE, "rq_gemv_nibble_escalate: need K > 0, K %% 32 == 0");
   if (!aligned16(x_bf16) || !aligned16(w_hi) || (w_lo && !aligned16(w_lo)))
     return fail(RQ_EALIGN, "rq_gemv_nibble_escalate: x and planes must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(y_f32) & 3u) != 0)
+    return fail(RQ_EALIGN, "rq_gemv_nibble_escalate: y_f32 must be 4-byte aligned");
   if (workspace && !aligned16(workspace)) return fail(RQ_EALIGN, "rq_gemv_nibble_escalate: workspace must be 16-byte aligned");
   if (rq_status s = need_device(); s != RQ_OK) return s;
   hipStream_t st = as_stream(stream);
@@ -333,9 +337,9 @@ rq_status rq_gemv_nibble_escalate(const void* x_bf16, int64_t B, int64_t K, int6
   uint16_t* y = static_cast<uint16_t*>(y_bf16);
   hipError_t e = hipSuccess;
   const size_t wsb = workspace ? ws_bytes : 0;
-  if (phase & RQ_LOW) e = rq::launch_gemv_low(x, B, K, N, w_hi, scales_tiled, y, workspace, wsb, st);
+  if (phase & RQ_LOW) e = rq::launch_gemv_low(x, B, K, N, w_hi, scales_tiled, y, y_f32, workspace, wsb, st);
   if (e == hipSuccess && (phase & RQ_ESCALATE))
-    e = rq::launch_gemv_escalate(x, B, K, N, w_hi, w_lo, scales_tiled, flags, y, workspace, wsb, st);
+    e = rq::launch_gemv_escalate(x, B, K, N, w_hi, w_lo, scales_tiled, flags, y, y_f32, workspace, wsb, st);
   return hip_status(e, "rq_gemv_nibble_escalate launch");
 }
 
@@ -357,6 +361,10 @@ int64_t rq_gemv_group_plan(rq_gemv_problem* problems, int count) {
     }
     if (!aligned16(p.x_bf16) || !aligned16(p.w_hi) || (p.w_lo && !aligned16(p.w_lo))) {
       fail(RQ_EALIGN, "rq_gemv_group_plan: problem %d: x and planes must be 16-byte aligned", i);
+      return -1;
+    }
+    if ((reinterpret_cast<uintptr_t>(p.y_f32) & 3u) != 0) {
+      fail(RQ_EALIGN, "rq_gemv_group_plan: problem %d: y_f32 must be 4-byte aligned", i);
       return -1;
     }
     p.tile_start = tiles;

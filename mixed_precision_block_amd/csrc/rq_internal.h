@@ -65,11 +65,14 @@ hipError_t launch_pack_nibble_planes(const int8_t* w, const uint16_t* scales, in
 // 0 when the shape needs no split.  With less workspace than this the
 // kernels run unsplit.
 size_t gemv_workspace_bytes(int64_t B, int64_t N, int64_t K);
+// yf: optional FP32 carry [B x N]: the low pass also stores its sums there;
+// an escalation given it reads only the lo plane and adds to the carry.
 hipError_t launch_gemv_low(const uint16_t* x, int64_t B, int64_t K, int64_t N, const uint8_t* hi,
-                           const uint16_t* scales, uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream);
+                           const uint16_t* scales, uint16_t* y, float* yf, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
 hipError_t launch_gemv_escalate(const uint16_t* x, int64_t B, int64_t K, int64_t N,
                                 const uint8_t* hi, const uint8_t* lo, const uint16_t* scales,
-                                const uint8_t* flags, uint16_t* y, void* ws, size_t ws_bytes,
+                                const uint8_t* flags, uint16_t* y, float* yf, void* ws, size_t ws_bytes,
                                 hipStream_t stream);
 // One launch over many problems (rq_gemv_problem table in device memory,
 // tile_start set by rq_gemv_group_plan): phase 1 low pass, 2 escalation,

@@ -32,7 +32,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert rq.rq_abi_version() == 1
+    assert rq.rq_abi_version() == L.ABI_VERSION == 2
     lib = L.lib()
     assert lib.rq_status_str(L.RQ_ESHAPE) == b"RQ_ESHAPE"
     assert lib.rq_status_str(99) == b"RQ_UNKNOWN"
@@ -113,7 +113,7 @@ def test_recurrent_prefill_validation():
 
 
 def test_gemv_and_gate_validation():
-    g = [A16, 16, 1024, 64, A16, A16, A16, A16, L.RQ_BOTH, None, 0, A16]
+    g = [A16, 16, 1024, 64, A16, A16, A16, A16, L.RQ_BOTH, None, 0, None, A16]
     for i, v, want in [(1, 0, L.RQ_ESHAPE), (1, 17, L.RQ_ESHAPE), (2, 1000, L.RQ_ESHAPE), (8, 4, L.RQ_EINVAL),
                        (5, None, L.RQ_EINVAL), (7, None, L.RQ_EINVAL), (9, A16 + 4, L.RQ_EALIGN)]:
         a = list(g)
@@ -123,6 +123,18 @@ def test_gemv_and_gate_validation():
     lowonly[5] = lowonly[7] = None
     lowonly[8] = L.RQ_LOW
     assert status_of(rq.rq_gemv_nibble_escalate, *lowonly) in (L.RQ_OK, L.RQ_ENODEV)
+    # with an FP32 carry the escalation reads only the lo plane: w_hi may be
+    # NULL for RQ_ESCALATE alone, not when the low pass runs
+    carry = list(g)
+    carry[4] = None
+    carry[11] = A16
+    for phase, want in ((L.RQ_ESCALATE, (L.RQ_OK, L.RQ_ENODEV)), (L.RQ_BOTH, (L.RQ_EINVAL,)),
+                        (L.RQ_LOW, (L.RQ_EINVAL,))):
+        carry[8] = phase
+        assert status_of(rq.rq_gemv_nibble_escalate, *carry) in want, phase
+    carry[4] = A16
+    carry[11] = A16 + 2
+    assert status_of(rq.rq_gemv_nibble_escalate, *carry) == L.RQ_EALIGN  # the carry is FP32: 4-byte aligned
     assert status_of(rq.rq_escalation_gate, A16, 0, 100, 1.0, 0.1, A16, None) == L.RQ_ESHAPE
     assert status_of(rq.rq_kv_quantize, A16, 4, 2, 100, A16, A16) == L.RQ_ESHAPE
     # split-K workspace: few row tiles -> slices x 16 token rows x padded rows x FP32; many tiles or bad shapes -> 0
@@ -153,12 +165,12 @@ def test_gemv_group_plan_and_grouped_validation():
     P = rq.RqGemvProblem
     arr = (P * 3)()
     for i, (n, k) in enumerate(((100, 64), (64, 32), (151936, 1024))):
-        arr[i] = P(A16, A16, None, A16, A16, n, k, 0)
+        arr[i] = P(A16, A16, None, A16, A16, None, n, k, 0)
     assert rq.rq_gemv_group_plan(arr) == 2 + 1 + 2374
     assert [arr[i].tile_start for i in range(3)] == [0, 2, 3]
     for field, value in (("K", 33), ("N", 0), ("x_bf16", None), ("w_hi", A16 + 8)):
         bad = (P * 1)()
-        bad[0] = P(A16, A16, None, A16, A16, 64, 32, 0)
+        bad[0] = P(A16, A16, None, A16, A16, None, 64, 32, 0)
         setattr(bad[0], field, value)
         with pytest.raises(L.RQError):
             rq.rq_gemv_group_plan(bad)
@@ -230,8 +242,8 @@ def test_empty_tensors_may_be_null_and_nothing_else():
                      1e-6, None, 0) in passed
     assert status_of(rq.rq_pack_nibble_planes, None, None, 0, 64, None, None, None) in passed
     assert status_of(rq.rq_gemv_nibble_escalate, A16, 4, 64, 0, None, None, None, A16, L.RQ_BOTH, None, 0,
-                     None) in passed
+                     None, None) in passed
     assert status_of(rq.rq_gemv_nibble_escalate, None, 4, 64, 0, None, None, None, A16, L.RQ_BOTH, None, 0,
-                     None) == L.RQ_EINVAL  # x [B, K] is not empty
+                     None, None) == L.RQ_EINVAL  # x [B, K] is not empty
     assert status_of(rq.rq_kv_quantize, None, 0, 2, 128, None, None) in passed
     assert status_of(rq.rq_kv_quantize, None, 3, 2, 128, None, None) == L.RQ_EINVAL

@@ -154,7 +154,7 @@ def test_split_workspace_reused_across_calls():
             y = torch.empty((16, n), dtype=torch.int16, device="cuda")
             hi, lo, st = planes
             assert L.rq_gemv_workspace_bytes(16, n, k) > 0
-            L.rq_gemv_nibble_escalate(x, 16, k, n, hi, lo, st, fl, L.RQ_BOTH, ws, wsb, y)
+            L.rq_gemv_nibble_escalate(x, 16, k, n, hi, lo, st, fl, L.RQ_BOTH, ws, wsb, None, y)
             fresh = host_bits(api.gemv_nibble_escalate(x, n, planes, fl, L.RQ_BOTH))
             assert np.array_equal(host_bits(y), fresh), (rep, n, k)
             ref = V.low_pass(d["x"], d["w"], d["scales"])
@@ -200,3 +200,80 @@ def test_grouped_equals_per_problem(B):
     for i, (w, (_, _, y)) in enumerate(zip(want_both, probs)):
         assert np.array_equal(host_bits(y), w), shapes[i]
     log(f"grouped GEMV B={B}: {len(shapes)} problems, {table[2]} tiles, equal to per-problem calls")
+
+
+def esc_ref(d, flags):
+    ref = V.low_pass(d["x"], d["w"], d["scales"])
+    f = np.asarray(flags) == 1
+    ref[f] = V.full_pass(d["x"][f], d["w"], d["scales"])
+    hi, _ = V.split_nibbles(d["w"])
+    bound = V.abs_bound(d["x"], d["w"], d["scales"]) + V.abs_bound(d["x"], 16 * hi.astype(np.int64), d["scales"])
+    return ref, bound
+
+
+@pytest.mark.parametrize("split", [True, False])
+@pytest.mark.parametrize("B", [2, 16])
+@pytest.mark.parametrize("N,K", [(200, 96), (1000, 1024), (130, 3072)])
+def test_carry_lo_plane_escalation(B, N, K, split):
+    """With an FP32 carry the low pass is unchanged (its BF16 output is the
+    carry rounded), and an escalation from the carry reads only the lo
+    plane (w_hi NULL) yet matches the oracle's 8-bit recompute."""
+    d = W.c5_linear(5, B=B, N=N, K=K)
+    flags = np.zeros(B, np.uint8)
+    flags[1::2] = 1
+    planes = gpu_planes(d["w"], d["scales"])
+    x, fl = dev_bf16(d["x"]), dev(flags)
+    carry = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")  # every row gets written
+    y = api.gemv_nibble_escalate(x, N, planes, None, L.RQ_LOW, split=split, carry=carry)
+    y_low = host_bits(y)
+    assert np.array_equal(y_low, host_bits(api.gemv_nibble_escalate(x, N, planes, None, L.RQ_LOW, split=split)))
+    c = host(carry)
+    assert np.array_equal(F.f64_to_bf16(c.astype(np.float64)), y_low)  # the BF16 output is the carry rounded
+    hi8, _ = V.split_nibbles(d["w"])
+    low_ref = V.low_pass(d["x"], d["w"], d["scales"])
+    low_bound = V.abs_bound(d["x"], 16 * hi8.astype(np.int64), d["scales"])
+    assert np.all(np.abs(c - low_ref) <= 1e-3 * low_bound + 1e-30)
+    api.gemv_nibble_escalate(x, N, (None, planes[1], planes[2]), fl, L.RQ_ESCALATE, y=y, split=split, carry=carry)
+    got = host_bits(y)
+    ref, bound = esc_ref(d, flags)
+    n = check_bf16(got, ref, bound, f"carry escalation B={B} {N}x{K} split={split}", k=K)
+    assert np.array_equal(got[flags == 0], y_low[flags == 0])
+    assert np.array_equal(host(carry), c)  # the carry is read, not written, by the escalation
+    log(f"carry escalation B={B} {N}x{K} split={split}: {n} outputs one BF16 step from the oracle")
+
+
+def test_carry_both_phases_lm_head_sampled():
+    """RQ_BOTH with a carry on the LM head (one wave per row tile)."""
+    i = len(W.c5_linear_list()) - 1
+    d = W.c5_linear(i)
+    N, K = 151936, 1024
+    planes = gpu_planes(d["w"], d["scales"])
+    carry = torch.empty((16, N), dtype=torch.float32, device="cuda")
+    y = host_bits(api.gemv_nibble_escalate(dev_bf16(d["x"]), N, planes, dev(d["flags"]), L.RQ_BOTH, carry=carry))
+    cols = np.sort(np.random.default_rng(9).choice(N, 2048, replace=False))
+    ds = dict(x=d["x"], w=d["w"][cols], scales=d["scales"][cols])
+    ref, bound = esc_ref(ds, d["flags"])
+    n = check_bf16(y[:, cols], ref, bound, "LM head with carry", k=K)
+    log(f"LM head with carry: {n} of {ref.size} sampled outputs one BF16 step off")
+
+
+def test_grouped_with_carry_equals_per_problem():
+    """Grouped launches where some problems carry FP32 sums: each problem's
+    outputs equal its own unsplit call with the same carry choice."""
+    B = 16
+    shapes = [(200, 96), (1000, 1024), (130, 3072), (64, 64)]
+    flags = dev(W.c5_flags(B))
+    probs, want = [], []
+    for i, (n, k) in enumerate(shapes):
+        d = W.c5_linear(20 + i, N=n, K=k, B=B)
+        planes = gpu_planes(d["w"], d["scales"])
+        x = dev_bf16(d["x"])
+        use = i % 2 == 0
+        c1 = torch.empty((B, n), dtype=torch.float32, device="cuda") if use else None
+        want.append(host_bits(api.gemv_nibble_escalate(x, n, planes, flags, L.RQ_BOTH, split=False, carry=c1)))
+        c2 = torch.empty((B, n), dtype=torch.float32, device="cuda") if use else None
+        probs.append((x, planes, torch.zeros((B, n), dtype=torch.bfloat16, device="cuda"), c2))
+    table = api.gemv_group(probs)
+    api.gemv_nibble_escalate_grouped(table, B, flags, L.RQ_BOTH)
+    for i, (w, p) in enumerate(zip(want, probs)):
+        assert np.array_equal(host_bits(p[2]), w), shapes[i]

@@ -43,7 +43,7 @@ def test_graph_replays_match_eager():
         for v in gemvs:
             hi, lo, st = v["planes"]
             L.rq_gemv_nibble_escalate(v["x"], 16, v["k"], v["n"], hi, lo, st, v["flags"], L.RQ_BOTH, v["ws"],
-                                      v["wsb"], v["y"])
+                                      v["wsb"], None, v["y"])
 
     def snapshot():
         torch.cuda.synchronize()
