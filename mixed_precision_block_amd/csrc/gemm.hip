@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ A
           reinterpret_cast<uint16_t*>(Y)[o] = (uint16_t)f32_to_bf16(v);
         } else if constexpr (EPI == kEpiSiluBf16) {
           const float z = bf16_to_f32(f32_to_bf16(v));
-          reinterpret_cast<uint16_t*>(Y)[o] = (uint16_t)f32_to_bf16(z / (1.0f + expf(-z)));
+          reinterpret_cast<uint16_t*>(Y)[o] = (uint16_t)f32_to_bf16(silu_f32(z));
         } else {
           uint16_t* h = reinterpret_cast<uint16_t*>(Y);
           const float sum = bf16_to_f32(h[o]) + bf16_to_f32(f32_to_bf16(v));

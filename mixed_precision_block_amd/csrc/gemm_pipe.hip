@@ -354,7 +354,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
               b[t] = pack_bf16(acc[i][j][4 * g + 2 * t], acc[i][j][4 * g + 2 * t + 1]);
               if constexpr (EPI == kEpiSiluBf16) {
                 const float z0 = bf16_to_f32(b[t] & 0xFFFFu), z1 = bf16_to_f32(b[t] >> 16);
-                b[t] = pack_bf16(z0 / (1.0f + expf(-z0)), z1 / (1.0f + expf(-z1)));
+                b[t] = pack_bf16(silu_f32(z0), silu_f32(z1));
               }
             }
             *reinterpret_cast<uint2*>(dst) = uint2{b[0], b[1]};

@@ -47,6 +47,14 @@ RQ_HD uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
+// SiLU(z) = z / (1 + e^-z) from the hardware base-2 exponential and
+// reciprocal (each within about an ulp of fp32; the GEMM epilogues round
+// the result to BF16).  Very negative z gives e^-z = inf and a zero
+// reciprocal: SiLU tends to -0, as it should.
+__device__ __forceinline__ float silu_f32(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.44269504088896341f));
+}
+
 // Two floats to packed BF16 (lo in bits 15:0) by the hardware conversion
 // (v_cvt_pk_bf16_f32): round to nearest even, the same bits as f32_to_bf16
 // for finite values.
