@@ -37,6 +37,7 @@
 // 2 kk and 2 kk + 1 of the row's stage scales, lane half h taking 2 kk + h.
 #include <type_traits>
 
+#include "rq_block.h"
 #include "rq_device.h"
 #include "rq_internal.h"
 
@@ -111,7 +112,8 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
                                                                       const uint8_t* __restrict__ As,
                                                                       const uint8_t* __restrict__ W,
                                                                       const uint8_t* __restrict__ Ws, int M, int N,
-                                                                      int K, void* __restrict__ Y, int tiles_m,
+                                                                      int K, void* __restrict__ Y,
+                                                                      uint8_t* __restrict__ Ys, int tiles_m,
                                                                       int tiles_n) {
   using C = DmaCfg<FMT, BM, BN, RB, WMW, WNW, NSTG>;
   using T = PipeTraits<FMT, RB>;
@@ -352,7 +354,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
               b[t] = pack_bf16(acc[i][j][4 * g + 2 * t], acc[i][j][4 * g + 2 * t + 1]);
-              if constexpr (EPI == kEpiSiluBf16) {
+              if constexpr (EPI == kEpiSiluBf16 || EPI == kEpiSiluQuant) {
                 const float z0 = bf16_to_f32(b[t] & 0xFFFFu), z1 = bf16_to_f32(b[t] >> 16);
                 b[t] = pack_bf16(silu_f32(z0), silu_f32(z1));
               }
@@ -369,6 +371,17 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
         const uint4 v = *reinterpret_cast<const uint4*>(strip + rho * RSTR + 16 * q);
         const int m = m_strip + rho, n = n_wave + p * SC + EPC * q;
         if (m >= M || n >= N) continue;
+        if constexpr (EPI == kEpiSiluQuant) {
+          // MX-quantize the BF16 u: lanes q = 4i .. 4i + 3 of a strip row
+          // hold one 32-block (N % 32 == 0, so a quad is masked together),
+          // encoded exactly as quant_rows_kernel does
+          using Fq = typename std::conditional<FMT == 1, FmtE2M1, FmtE4M3>::type;
+          const uint32_t sb = (uint32_t)(mx_block_exp<Fq>(quad_max(amax8(v))) + 127);
+          uint8_t* crow = static_cast<uint8_t*>(Y) + (int64_t)m * (FMT == 1 ? N / 2 : N);
+          encode_store8<Fq>(v, sb, crow + (FMT == 1 ? n / 2 : n));
+          if ((q & 3) == 0) Ys[(int64_t)m * (N / 32) + n / 32] = (uint8_t)sb;
+          continue;
+        }
         const bool whole = N % EPC == 0 && n + EPC <= N;
         if constexpr (EPI == kEpiStoreF32) {
           float* yrow = reinterpret_cast<float*>(Y) + (int64_t)m * N;
@@ -431,53 +444,64 @@ bool gemm_pipe_supported(int fmt, int64_t M, int64_t N, int64_t K) {
 
 template <int FMT, int EPI, int BM, int BN, int RB, int WMW, int WNW, int NSTG>
 static hipError_t launch_pipe_t(const void* a, const uint8_t* as, const void* w, const uint8_t* ws, int64_t M,
-                                int64_t N, int64_t K, void* y, hipStream_t stream) {
+                                int64_t N, int64_t K, void* y, uint8_t* ys, hipStream_t stream) {
   const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
   gemm_pipe_kernel<FMT, EPI, BM, BN, RB, WMW, WNW, NSTG><<<tm * tn, 64 * WMW * WNW, 0, stream>>>(
-      static_cast<const uint8_t*>(a), as, static_cast<const uint8_t*>(w), ws, (int)M, (int)N, (int)K, y, tm, tn);
+      static_cast<const uint8_t*>(a), as, static_cast<const uint8_t*>(w), ws, (int)M, (int)N, (int)K, y, ys, tm,
+      tn);
   return hipGetLastError();
 }
 
 template <int FMT, int EPI, int RB>
 static hipError_t launch_pipe_r(const void* a, const uint8_t* as, const void* w, const uint8_t* ws, int64_t M,
-                                int64_t N, int64_t K, void* y, hipStream_t stream) {
+                                int64_t N, int64_t K, void* y, uint8_t* ys, hipStream_t stream) {
   // 256 x 256 tiles (eight waves, two stages) when they fill the 256 CUs at
   // least once.  Otherwise 128 x 128 tiles: three stages when one workgroup
   // per CU covers every tile (MXFP8 on four waves of 64 x 64, MXFP4 and BF16
   // on eight of 64 x 32: the faster layout of each, measured), else two so
   // that two workgroups share a CU.
   const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
-  if (big >= 256) return launch_pipe_t<FMT, EPI, 256, 256, RB, 2, 4, 2>(a, as, w, ws, M, N, K, y, stream);
+  if (big >= 256) return launch_pipe_t<FMT, EPI, 256, 256, RB, 2, 4, 2>(a, as, w, ws, M, N, K, y, ys, stream);
   const int64_t small = ((M + 127) / 128) * ((N + 127) / 128);
   if constexpr (FMT != 2) {
-    if (small <= 256) return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 4, 3>(a, as, w, ws, M, N, K, y, stream);
+    if (small <= 256) return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 4, 3>(a, as, w, ws, M, N, K, y, ys, stream);
   }
-  if (small <= 256) return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 2, 3>(a, as, w, ws, M, N, K, y, stream);
-  return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 2, 2>(a, as, w, ws, M, N, K, y, stream);
+  if (small <= 256) return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 2, 3>(a, as, w, ws, M, N, K, y, ys, stream);
+  return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 2, 2>(a, as, w, ws, M, N, K, y, ys, stream);
 }
 
 template <int FMT, int EPI>
 static hipError_t launch_pipe_e(const void* a, const uint8_t* as, const void* w, const uint8_t* ws, int64_t M,
-                                int64_t N, int64_t K, void* y, hipStream_t stream) {
-  return launch_pipe_r<FMT, EPI, 128>(a, as, w, ws, M, N, K, y, stream);
+                                int64_t N, int64_t K, void* y, uint8_t* ys, hipStream_t stream) {
+  return launch_pipe_r<FMT, EPI, 128>(a, as, w, ws, M, N, K, y, ys, stream);
 }
 
 template <int FMT>
 static hipError_t launch_pipe_f(int epi, const void* a, const uint8_t* as, const void* w, const uint8_t* ws,
-                                int64_t M, int64_t N, int64_t K, void* y, hipStream_t stream) {
+                                int64_t M, int64_t N, int64_t K, void* y, uint8_t* ys, hipStream_t stream) {
   switch (epi) {
-    case kEpiStoreBf16: return launch_pipe_e<FMT, kEpiStoreBf16>(a, as, w, ws, M, N, K, y, stream);
-    case kEpiStoreF32: return launch_pipe_e<FMT, kEpiStoreF32>(a, as, w, ws, M, N, K, y, stream);
-    case kEpiSiluBf16: return launch_pipe_e<FMT, kEpiSiluBf16>(a, as, w, ws, M, N, K, y, stream);
-    default: return launch_pipe_e<FMT, kEpiResAddBf16>(a, as, w, ws, M, N, K, y, stream);
+    case kEpiStoreBf16: return launch_pipe_e<FMT, kEpiStoreBf16>(a, as, w, ws, M, N, K, y, ys, stream);
+    case kEpiStoreF32: return launch_pipe_e<FMT, kEpiStoreF32>(a, as, w, ws, M, N, K, y, ys, stream);
+    case kEpiSiluBf16: return launch_pipe_e<FMT, kEpiSiluBf16>(a, as, w, ws, M, N, K, y, ys, stream);
+    default: return launch_pipe_e<FMT, kEpiResAddBf16>(a, as, w, ws, M, N, K, y, ys, stream);
   }
 }
 
 hipError_t launch_gemm_pipe(int fmt, int epi, const void* a, const uint8_t* a_scales, const void* w,
                             const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y, hipStream_t stream) {
-  if (fmt == 1) return launch_pipe_f<1>(epi, a, a_scales, w, w_scales, M, N, K, y, stream);
-  if (fmt == 2) return launch_pipe_f<2>(epi, a, a_scales, w, w_scales, M, N, K, y, stream);
-  return launch_pipe_f<3>(epi, a, a_scales, w, w_scales, M, N, K, y, stream);
+  if (fmt == 1) return launch_pipe_f<1>(epi, a, a_scales, w, w_scales, M, N, K, y, nullptr, stream);
+  if (fmt == 2) return launch_pipe_f<2>(epi, a, a_scales, w, w_scales, M, N, K, y, nullptr, stream);
+  return launch_pipe_f<3>(epi, a, a_scales, w, w_scales, M, N, K, y, nullptr, stream);
+}
+
+hipError_t launch_gemm_silu_quant(int fmt, const void* a, const uint8_t* a_scales, const void* w,
+                                  const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, uint8_t* codes,
+                                  uint8_t* scales, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (N % 32 != 0 || !gemm_pipe_supported(fmt, M, N, K)) return hipErrorInvalidValue;
+  if (fmt == 1) return launch_pipe_e<1, kEpiSiluQuant>(a, a_scales, w, w_scales, M, N, K, codes, scales, stream);
+  if (fmt == 2) return launch_pipe_e<2, kEpiSiluQuant>(a, a_scales, w, w_scales, M, N, K, codes, scales, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace rq

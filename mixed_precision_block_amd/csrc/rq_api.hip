@@ -264,15 +264,25 @@ rq_status rq_recurrent_prefill(void* h_bf16, int64_t S, int64_t D, int64_t F, co
   uint8_t* u_sc = u_codes + round256(sz * fz);
   uint16_t* h = static_cast<uint16_t*>(h_bf16);
   hipStream_t st = as_stream(stream);
+  // shapes the pipelined GEMM takes quantize u in W1's epilogue (the same
+  // codes as the separate pass); the others go through u in BF16
+  const bool fused_u = rq::gemm_pipe_supported(fmt, S, F, D);
   for (int t = 1; t <= steps; ++t) {
     const bool q = (schedule >> (t - 1)) & 1ull;
     hipError_t e;
     if (q) {
       e = rq::launch_rmsnorm(fmt, h, S, D, eps, n_buf, n_sc, st);
-      if (e == hipSuccess) e = rq::launch_gemm(fmt, rq::kEpiSiluBf16, n_buf, n_sc, w1_q, w1_s, S, F, D, u_buf, st);
-      if (e == hipSuccess)
-        e = rq::launch_quant_rows(fmt, reinterpret_cast<const uint16_t*>(u_buf), S, F, u_codes, u_sc,
-                                  code_row_bytes(fmt, F), F / 32, st);
+      if (e == hipSuccess) {
+        if (fused_u) {
+          // SiLU and the block quantization of u in W1's epilogue
+          e = rq::launch_gemm_silu_quant(fmt, n_buf, n_sc, w1_q, w1_s, S, F, D, u_codes, u_sc, st);
+        } else {
+          e = rq::launch_gemm(fmt, rq::kEpiSiluBf16, n_buf, n_sc, w1_q, w1_s, S, F, D, u_buf, st);
+          if (e == hipSuccess)
+            e = rq::launch_quant_rows(fmt, reinterpret_cast<const uint16_t*>(u_buf), S, F, u_codes, u_sc,
+                                      code_row_bytes(fmt, F), F / 32, st);
+        }
+      }
       if (e == hipSuccess) e = rq::launch_gemm(fmt, rq::kEpiResAddBf16, u_codes, u_sc, w2_q, w2_s, S, D, F, h, st);
     } else {
       e = rq::launch_rmsnorm(RQ_BF16, h, S, D, eps, n_buf, nullptr, st);

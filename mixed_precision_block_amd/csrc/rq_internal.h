@@ -14,7 +14,8 @@ enum Epilogue {
   kEpiStoreBf16 = 0,  // y = bf16(acc)
   kEpiStoreF32 = 1,   // y = acc
   kEpiSiluBf16 = 2,   // y = bf16(SiLU(bf16(acc)))
-  kEpiResAddBf16 = 3  // y = bf16(y + bf16(acc))   (in place)
+  kEpiResAddBf16 = 3, // y = bf16(y + bf16(acc))   (in place)
+  kEpiSiluQuant = 4   // u = bf16(SiLU(bf16(acc))), stored as the GEMM's MX format: codes y, scales ys
 };
 
 // fmt: 1 = MXFP4, 2 = MXFP8, 3 = BF16 (scale pointers ignored).  Picks the
@@ -28,6 +29,13 @@ hipError_t launch_gemm_basic(int fmt, int epi, const void* a, const uint8_t* a_s
                              const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y,
                              hipStream_t stream);
 bool gemm_pipe_supported(int fmt, int64_t M, int64_t N, int64_t K);
+// y = SiLU(A W^T) rounded to BF16 and block-quantized, in one launch: codes
+// [M x N] in fmt's layout (row stride N/2 or N bytes) and scales [M x N/32].
+// MXFP4 / MXFP8 only; needs gemm_pipe_supported and N % 32 == 0, else
+// returns hipErrorInvalidValue without launching.
+hipError_t launch_gemm_silu_quant(int fmt, const void* a, const uint8_t* a_scales, const void* w,
+                                  const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, uint8_t* codes,
+                                  uint8_t* scales, hipStream_t stream);
 hipError_t launch_gemm_pipe(int fmt, int epi, const void* a, const uint8_t* a_scales, const void* w,
                             const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y,
                             hipStream_t stream);
