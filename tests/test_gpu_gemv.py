@@ -212,7 +212,7 @@ def esc_ref(d, flags):
 
 
 @pytest.mark.parametrize("split", [True, False])
-@pytest.mark.parametrize("B", [2, 16])
+@pytest.mark.parametrize("B", [1, 2, 5, 16])
 @pytest.mark.parametrize("N,K", [(200, 96), (1000, 1024), (130, 3072)])
 def test_carry_lo_plane_escalation(B, N, K, split):
     """With an FP32 carry the low pass is unchanged (its BF16 output is the
@@ -221,6 +221,7 @@ def test_carry_lo_plane_escalation(B, N, K, split):
     d = W.c5_linear(5, B=B, N=N, K=K)
     flags = np.zeros(B, np.uint8)
     flags[1::2] = 1
+    flags[-1] = 1  # at least one flagged token, also for B = 1
     planes = gpu_planes(d["w"], d["scales"])
     x, fl = dev_bf16(d["x"]), dev(flags)
     carry = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")  # every row gets written

@@ -1,8 +1,10 @@
 """HIP-graph capture of library calls: a captured sequence (quantize + GEMM,
-and nibble GEMVs including the split-K partial sums and their reduction)
-replays to the eager results, bit for bit, on every replay, with eager work
-and synchronizations between the replays.  Nothing the library launches
-records a memset, so the captured graph holds only kernel nodes."""
+nibble GEMVs including the split-K partial sums and their reduction, two of
+them through the FP32 carry, and a short recurrent prefill whose quantized
+steps quantize u in the GEMM epilogue) replays to the eager results, bit for
+bit, on every replay, with eager work and synchronizations between the
+replays.  Nothing the library launches records a memset, so the captured
+graph holds only kernel nodes."""
 
 import numpy as np
 import pytest
@@ -34,8 +36,17 @@ def test_graph_replays_match_eager():
         planes = api.pack_nibble_planes(dev(d["w"]), dev(np.asarray(d["scales"], np.float16).view(np.int16)))
         wsb = L.rq_gemv_workspace_bytes(16, n, k)
         ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
-        gemvs.append(dict(x=dev_bf16(d["x"]), planes=planes, n=n, k=k, ws=ws, wsb=wsb,
+        carry = torch.empty((16, n), dtype=torch.float32, device="cuda") if i < 2 else None
+        gemvs.append(dict(x=dev_bf16(d["x"]), planes=planes, n=n, k=k, ws=ws, wsb=wsb, carry=carry,
                           flags=dev(d["flags"]), y=torch.empty((16, n), dtype=torch.int16, device="cuda")))
+    # a short recurrent prefill: steps 1-2 MXFP4 (u quantized in the W1 epilogue), step 3 BF16
+    r = W.c4_ramp(S=256, D=256, F=512)
+    w1, w2 = dev_bf16(r["w1"]), dev_bf16(r["w2"])
+    w1q, w2q = api.quantize(w1, L.RQ_MXFP4), api.quantize(w2, L.RQ_MXFP4)
+    h0 = dev_bf16(r["h0"])
+    h = h0.clone()
+    rws = torch.empty(L.rq_recurrent_prefill_workspace_bytes(256, 256, 512, L.RQ_MXFP4), dtype=torch.uint8,
+                      device="cuda")
 
     def work():
         L.rq_quantize(a, M, K, L.RQ_MXFP8, None, 0, L.RQ_APPEND_NONE, ac, as_)
@@ -43,15 +54,20 @@ def test_graph_replays_match_eager():
         for v in gemvs:
             hi, lo, st = v["planes"]
             L.rq_gemv_nibble_escalate(v["x"], 16, v["k"], v["n"], hi, lo, st, v["flags"], L.RQ_BOTH, v["ws"],
-                                      v["wsb"], None, v["y"])
+                                      v["wsb"], v["carry"], v["y"])
+        L.rq_recurrent_prefill(h, 256, 256, 512, w1, w2, w1q[0], w1q[1], w2q[0], w2q[1], L.RQ_MXFP4, 0b011, 3,
+                               1e-6, rws, rws.numel())
+
+    outs = [ac, as_, y, h] + [v["y"] for v in gemvs] + [v["carry"] for v in gemvs if v["carry"] is not None]
 
     def snapshot():
         torch.cuda.synchronize()
-        return [t.cpu().numpy().copy() for t in [ac, as_, y] + [v["y"] for v in gemvs]]
+        return [t.cpu().numpy().copy() for t in outs]
 
     def clear():
-        for t in [ac, as_, y] + [v["y"] for v in gemvs]:
+        for t in outs:
             t.zero_()
+        h.copy_(h0)  # the prefill runs in place from h0
         torch.cuda.synchronize()
 
     clear()
@@ -70,6 +86,7 @@ def test_graph_replays_match_eager():
         for i, (e, o) in enumerate(zip(eager, got)):
             assert np.array_equal(e, o), f"replay {rep}: output {i} differs from the eager run"
         # eager work between replays
+        clear()
         work()
         again = snapshot()
         for e, o in zip(eager, again):
