@@ -95,7 +95,12 @@ struct DmaCfg {
   static constexpr int DPW = (IA + IW) / NW;          // operand DMAs per wave per stage
   static constexpr int SA = BM * RB, SW = BN * RB;
   static constexpr int SBPR = T::kSBPR;
-  static constexpr int SS = (BM + BN) * SBPR;
+  // Scale rows per stage: the tile's A then W rows, padded (rows past the W
+  // tile read as zeros: they lie beyond its buffer range) so that the
+  // 256-byte scale DMAs split evenly over the waves.
+  static constexpr int SRU = SBPR > 0 ? 256 * NW / SBPR : 1;
+  static constexpr int SR = SBPR > 0 ? (BM + BN + SRU - 1) / SRU * SRU : 0;
+  static constexpr int SS = SR * SBPR;
   static constexpr int IS = SS / 256;                 // dword DMAs of the stage's scales (0 for BF16)
   static constexpr int SPW = IS / NW;
   static constexpr int DW = DPW + SPW;                // DMAs per wave per stage
@@ -331,7 +336,10 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
   constexpr int EPC = 16 / EB;                      // elements per 16-byte chunk
   constexpr int RSTR = SC * EB + 16;                // strip row stride in bytes (16-byte aligned)
   constexpr int CPR = SC * EB / 16;                 // chunks per strip row
-  constexpr int RPI = 64 / CPR;                     // strip rows per wave-wide read
+  constexpr int RPI = 64 / CPR;                     // strip rows per wave-wide read (the last
+                                                    // 64 - RPI * CPR lanes idle)
+  constexpr int NRD = (32 + RPI - 1) / RPI;         // reads per strip
+  static_assert(CPR % 4 == 0, "a lane quad holds one 32-column block of a row");
   static_assert(C::NW * 32 * RSTR <= NSTG * C::STAGE, "epilogue strips fit in the stage buffers");
   uint8_t* const strip = smem + wave * 32 * RSTR;
   const int n_wave = n0 + wn * WN;
@@ -366,8 +374,9 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
       // a wave's LDS accesses complete in order: the reads below see the
       // writes above, and the next pass's writes follow these reads
 #pragma unroll
-      for (int t = 0; t < 32 / RPI; ++t) {
+      for (int t = 0; t < NRD; ++t) {
         const int rho = t * RPI + lane / CPR, q = lane % CPR;
+        if (lane >= RPI * CPR || rho >= 32) continue;  // whole rows, so whole quads
         const uint4 v = *reinterpret_cast<const uint4*>(strip + rho * RSTR + 16 * q);
         const int m = m_strip + rho, n = n_wave + p * SC + EPC * q;
         if (m >= M || n >= N) continue;
@@ -461,7 +470,15 @@ static hipError_t launch_pipe_r(const void* a, const uint8_t* as, const void* w,
   // on eight of 64 x 32: the faster layout of each, measured), else two so
   // that two workgroups share a CU.
   const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
-  if (big >= 256) return launch_pipe_t<FMT, EPI, 256, 256, RB, 2, 4, 2>(a, as, w, ws, M, N, K, y, ys, stream);
+  if (big >= 256) {
+    // 256 x 192 tiles (4 x 2 waves of 64 x 96) when their rounds over the
+    // 256 CUs cost less: a round of them is about 3/4 of a 256 x 256 round
+    // (gate/up's N = 6144: 2 full rounds instead of 1.5)
+    const int64_t mid = ((M + 255) / 256) * ((N + 191) / 192);
+    if (3 * ((mid + 255) / 256) < 4 * ((big + 255) / 256))
+      return launch_pipe_t<FMT, EPI, 256, 192, RB, 4, 2, 2>(a, as, w, ws, M, N, K, y, ys, stream);
+    return launch_pipe_t<FMT, EPI, 256, 256, RB, 2, 4, 2>(a, as, w, ws, M, N, K, y, ys, stream);
+  }
   const int64_t small = ((M + 127) / 128) * ((N + 127) / 128);
   if constexpr (FMT != 2) {
     if (small <= 256) return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 4, 3>(a, as, w, ws, M, N, K, y, ys, stream);

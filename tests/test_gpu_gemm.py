@@ -102,9 +102,11 @@ def test_scale_association_every_block(fmt, ofmt, M, N, K):
 
 
 @pytest.mark.parametrize("fmt,ofmt", MX + [(L.RQ_BF16, None)])
-@pytest.mark.parametrize("M,N,K", [(4000, 4100, 384), (4096, 4096, 128), (3969, 4097, 1152), (4096, 4096, 160)])
+@pytest.mark.parametrize("M,N,K", [(4000, 4100, 384), (4096, 4096, 128), (3969, 4097, 1152), (4096, 4096, 160),
+                                   (4096, 6100, 384), (4000, 5700, 1152)])
 def test_large_tiles_ragged_sampled(fmt, ofmt, M, N, K):
-    """Shapes with at least 256 tiles of 256 x 256 (the large-tile path),
+    """Shapes with at least 256 tiles of 256 x 256 (the large-tile paths:
+    256 x 256, and 256 x 192 for the last two, whose rounds it fills),
     ragged in M and N, K of one stage, an odd number of stages, a long tail
     and K ending in a partial stage (MXFP4 at 384 and 1152, BF16 at 160);
     the oracle runs on sampled rows that include the last one."""
