@@ -316,8 +316,8 @@ def main():
                                "q/k/v and gate/up share their inputs and run as one GEMM each",
                    "tokens": M, "gemm_gflop_per_step": round(flops_step / 1e9, 2),
                    "gemms_per_step": [f"{g['name']} {M}x{g['N']}x{g['K']}" for g in groups]},
-        "roofline": {"bound": "mfma", "kernel": "gemm_pipe_kernel<MXFP8, BF16 out> (256x256 tiles for qkv and "
-                               "gate_up, 128x128 for o and down)",
+        "roofline": {"bound": "mfma", "kernel": "gemm_pipe_kernel<MXFP8, BF16 out> (256x256 tiles for qkv, "
+                               "256x192 for gate_up, 128x128 for o and down)",
                      "achieved": round(achieved / 1e12, 2), "peak": PEAK["mxfp8"] / 1e12, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK["mxfp8"], 4), "traffic": traffic,
                      "avg_launch_us": round(gemm_ms * 1e3, 2), "per_gemm": per_gemm},
