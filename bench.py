@@ -199,7 +199,8 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run plain 256 MiB device copies (the reference for HBM byte counters)")
     ap.add_argument("--only", choices=["square", "gemv"],
-                    help="run only one group of rows (4096^3 GEMMs and the ARC front end, or the nibble GEMV) "
+                    help="run only one group of rows (4096^3 GEMMs and the ARC front end, or the nibble GEMV "
+                         "with the escalation gate and the KV tiles) "
                          "and print them; for profiling runs")
     ap.add_argument("--traffic-from", metavar="DIR",
                     help="write the traffic summary from rocprofv3 --pmc CSV runs under DIR (pmc_main_FETCH_SIZE, "
@@ -231,6 +232,7 @@ def main():
             out = measure_square(torch, api, L, W, to_dev_only, dev)
         else:
             out = measure_gemv(torch, np, api, L, W, dev)
+            out["kv_quantize_fp8_tile128_4096x8x128"] = measure_kv(torch, L, dev)
         print(json.dumps(out), flush=True)
         return
     if args.calibrate_copy:
@@ -366,7 +368,22 @@ def measure_rows(torch, np, api, L, W, to_dev, dev):
 
     # ---- nibble GEMV: weights drawn on the GPU with the same recipe
     rows.update(measure_gemv(torch, np, api, L, W, dev))
+
+    # ---- FP8 KV tiles: one 4096-token prefill's keys, 8 heads of 128
+    rows["kv_quantize_fp8_tile128_4096x8x128"] = measure_kv(torch, L, dev)
     return rows
+
+
+def measure_kv(torch, L, dev, T=4096, H=8, D=128):
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20261209)
+    x = torch.randn((T, H, D), generator=gen, device=dev).to(torch.bfloat16)
+    codes = torch.empty((T, H, D), dtype=torch.uint8, device=dev)
+    scales = torch.empty((T, H, D // 128), dtype=torch.float32, device=dev)
+    ms = time_calls(torch, lambda: L.rq_kv_quantize(x, T, H, D, codes, scales), 100, graph=True)
+    nbytes = T * H * D * 3 + T * H * (D // 128) * 4
+    return {"us": round(ms * 1e3, 2), "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(nbytes / (ms * 1e-3) / PEAK["hbm"], 4), "bytes": nbytes}
 
 
 def measure_square(torch, api, L, W, to_dev, dev):
@@ -739,6 +756,39 @@ def measure_gemv(torch, np, api, L, W, dev):
         "us": round(ms * 1e3, 2), "gb_s": round(esc_lo_bytes(N, K, nf_lm) / (ms * 1e-3) / 1e9, 1),
         "frac_hbm": round(esc_lo_bytes(N, K, nf_lm) / (ms * 1e-3) / PEAK["hbm"], 4),
         "bytes": esc_lo_bytes(N, K, nf_lm)}
+    # the escalation gate over the LM head's low-pass logits [16 x 151936]
+    # (softmax entropy and top-1 / top-2 margin per token), alone and as the
+    # middle of the LM head's whole decode step on the device: low pass with
+    # the carry, gate, lo-plane escalation of the tokens it flags.  tau sits
+    # between the second and third largest entropy, so the gate flags two
+    # tokens as the seeded flags above do; delta = 0 leaves the margin test
+    # off (random logits have no confident tokens).
+    lm_low_carry()
+    logits = ys[N]
+    gflags = torch.empty(B, dtype=torch.uint8, device=dev)
+    gstats = torch.empty((B, 2), dtype=torch.float32, device=dev)
+    L.rq_escalation_gate(logits, B, N, 0.0, 0.0, gflags, gstats)
+    ent = sorted(gstats[:, 0].tolist(), reverse=True)
+    tau = 0.5 * (ent[1] + ent[2])
+    ms = time_calls(torch, lambda: L.rq_escalation_gate(logits, B, N, tau, 0.0, gflags, gstats), 100, graph=True)
+    gate_bytes = B * N * 2
+    out["escalation_gate_lm_head_logits_16x151936"] = {
+        "us": round(ms * 1e3, 2), "gb_s": round(gate_bytes / (ms * 1e-3) / 1e9, 1),
+        "frac_hbm": round(gate_bytes / (ms * 1e-3) / PEAK["hbm"], 4), "bytes": gate_bytes}
+
+    def lm_decode_step():
+        lm_low_carry()
+        L.rq_escalation_gate(logits, B, N, tau, 0.0, gflags, gstats)
+        c = copies[it[0] % 4]
+        it[0] += 1
+        L.rq_gemv_nibble_escalate(xs[K], B, K, N, None, c[1], c[2], gflags, L.RQ_ESCALATE, wsp, wsb, carry, ys[N])
+
+    ms = time_calls(torch, lm_decode_step, 40)
+    out["gemv_lm_head_decode_step_low_gate_escalate_b16"] = {
+        "us": round(ms * 1e3, 2), "flagged": int(gflags.sum().item()),
+        "us_parts_sum": round(out["gemv_lm_head_low_pass_b16_with_carry"]["us"]
+                              + out["escalation_gate_lm_head_logits_16x151936"]["us"]
+                              + out["gemv_lm_head_escalation_2_of_16_lo_plane_from_carry"]["us"], 2)}
     del copies, carry
 
     def sweep(phase):

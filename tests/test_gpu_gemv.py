@@ -75,7 +75,7 @@ def test_worked_example():
 
 
 @pytest.mark.parametrize("split", [True, False])
-@pytest.mark.parametrize("B", [1, 2, 5, 16])
+@pytest.mark.parametrize("B", [1, 2, 5, 8, 9, 16])
 @pytest.mark.parametrize("N,K", [(200, 96), (64, 32), (1000, 1024), (130, 3072)])
 def test_small_against_oracle(B, N, K, split):
     """Few row tiles: with a workspace the launch splits K over workgroups
