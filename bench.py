@@ -767,10 +767,13 @@ def measure_gemv(torch, np, api, L, W, dev):
     logits = ys[N]
     gflags = torch.empty(B, dtype=torch.uint8, device=dev)
     gstats = torch.empty((B, 2), dtype=torch.float32, device=dev)
-    L.rq_escalation_gate(logits, B, N, 0.0, 0.0, gflags, gstats)
+    gwsb = L.rq_escalation_gate_workspace_bytes(B, N)
+    gws = torch.empty(max(gwsb, 16), dtype=torch.uint8, device=dev)
+    L.rq_escalation_gate(logits, B, N, 0.0, 0.0, gflags, gstats, gws, gwsb)
     ent = sorted(gstats[:, 0].tolist(), reverse=True)
     tau = 0.5 * (ent[1] + ent[2])
-    ms = time_calls(torch, lambda: L.rq_escalation_gate(logits, B, N, tau, 0.0, gflags, gstats), 100, graph=True)
+    ms = time_calls(torch, lambda: L.rq_escalation_gate(logits, B, N, tau, 0.0, gflags, gstats, gws, gwsb), 100,
+                    graph=True)
     gate_bytes = B * N * 2
     out["escalation_gate_lm_head_logits_16x151936"] = {
         "us": round(ms * 1e3, 2), "gb_s": round(gate_bytes / (ms * 1e-3) / 1e9, 1),
@@ -778,7 +781,7 @@ def measure_gemv(torch, np, api, L, W, dev):
 
     def lm_decode_step():
         lm_low_carry()
-        L.rq_escalation_gate(logits, B, N, tau, 0.0, gflags, gstats)
+        L.rq_escalation_gate(logits, B, N, tau, 0.0, gflags, gstats, gws, gwsb)
         c = copies[it[0] % 4]
         it[0] += 1
         L.rq_gemv_nibble_escalate(xs[K], B, K, N, None, c[1], c[2], gflags, L.RQ_ESCALATE, wsp, wsb, carry, ys[N])

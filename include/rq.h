@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define RQ_ABI_VERSION 2
+#define RQ_ABI_VERSION 3
 
 typedef enum {
   RQ_OK = 0,
@@ -323,12 +323,20 @@ rq_status rq_gemv_nibble_escalate_grouped(const rq_gemv_problem *problems_dev,
  * article, setup paragraph: recompute when the output distribution's
  * entropy is above a threshold or the top-1/top-2 probability gap is
  * small).  flags[t] = (H(softmax(logits[t])) > tau) || (p1 - p2 < delta).
- * logits_bf16 [B x V]; flags [B] uint8; stats [B x 2] float (entropy in
- * nats, p1 - p2) or NULL.  B in [1, 16].  FP32 arithmetic.
+ * logits_bf16 [B x V] (finite, 2-byte aligned); flags [B] uint8; stats [B x 2] float
+ * (entropy in nats, p1 - p2; 4-byte aligned) or NULL.  B in [1, 16],
+ * 2 <= V < 2^31.  FP32 arithmetic.
+ * workspace: device scratch of ws_bytes >= rq_escalation_gate_workspace_bytes
+ * (B, V) bytes (caller-owned, 16-byte aligned, contents irrelevant) lets
+ * each row split over many workgroups whose partial statistics a second
+ * kernel merges; NULL / smaller takes one workgroup per row.  The two
+ * differ only in FP32 summation order; each is deterministic.
  */
+size_t rq_escalation_gate_workspace_bytes(int64_t B, int64_t V);
 rq_status rq_escalation_gate(const void *logits_bf16, int64_t B, int64_t V,
                              float tau, float delta, uint8_t *flags,
-                             float *stats, void *stream);
+                             float *stats, void *workspace, size_t ws_bytes,
+                             void *stream);
 
 /*
  * rq_kv_quantize -- FP8 per-token-head-tile quantize-on-write (Day 0 LLM

@@ -66,14 +66,15 @@ _SIGNATURES = {
     "rq_gemv_nibble_escalate": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _INT, _P, _SZ, _P, _P, _P]),
     "rq_gemv_group_plan": (_I64, [ctypes.POINTER(RqGemvProblem), _INT]),
     "rq_gemv_nibble_escalate_grouped": (_INT, [_P, _INT, _I64, _I64, _P, _INT, _P]),
-    "rq_escalation_gate": (_INT, [_P, _I64, _I64, _F, _F, _P, _P, _P]),
+    "rq_escalation_gate_workspace_bytes": (_SZ, [_I64, _I64]),
+    "rq_escalation_gate": (_INT, [_P, _I64, _I64, _F, _F, _P, _P, _P, _SZ, _P]),
     "rq_kv_quantize": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P]),
 }
 
 _lib = None
 
 # The RQ_ABI_VERSION these signatures and RqGemvProblem follow (include/rq.h).
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 def lib():
@@ -210,9 +211,14 @@ def rq_gemv_nibble_escalate_grouped(problems_dev, count, total_tiles, B, flags, 
                                                  _stream(stream)))
 
 
-def rq_escalation_gate(logits, B, V, tau, delta, flags, stats, stream=None):
+def rq_escalation_gate_workspace_bytes(B, V):
+    return lib().rq_escalation_gate_workspace_bytes(B, V)
+
+
+def rq_escalation_gate(logits, B, V, tau, delta, flags, stats, workspace, ws_bytes, stream=None):
     _check("rq_escalation_gate", lib().rq_escalation_gate(_ptr(logits), B, V, tau, delta, _ptr(flags),
-                                                          _ptr(stats), _stream(stream)))
+                                                          _ptr(stats), _ptr(workspace), ws_bytes,
+                                                          _stream(stream)))
 
 
 def rq_kv_quantize(x, T, H, D, codes, scales, stream=None):

@@ -154,11 +154,15 @@ def gemv_nibble_escalate_grouped(table, B, flags=None, phase=L.RQ_BOTH, stream=N
     L.rq_gemv_nibble_escalate_grouped(dev_table, count, total, B, flags, phase, stream)
 
 
-def escalation_gate(logits, tau, delta, stream=None):
+def escalation_gate(logits, tau, delta, split=True, stream=None):
+    """flags [B] uint8 and stats [B, 2] (entropy, p1 - p2) of logits [B, V];
+    split=False runs one workgroup per row (no workspace)."""
     B, V = logits.shape
     flags = _u8((B,), logits.device)
     stats = torch.empty((B, 2), dtype=torch.float32, device=logits.device)
-    L.rq_escalation_gate(logits, B, V, tau, delta, flags, stats, stream)
+    wsb = L.rq_escalation_gate_workspace_bytes(B, V) if split else 0
+    ws = _u8((max(wsb, 16),), logits.device) if wsb else None
+    L.rq_escalation_gate(logits, B, V, tau, delta, flags, stats, ws, wsb, stream)
     return flags, stats
 
 

@@ -7,6 +7,8 @@
 //    article, setup paragraph);
 //  * FP8 per-token-head-tile-128 KV quantize-on-write (Day-0 page, section
 //    III.3.3 with the section V listing's amax/448 scale).
+#include <algorithm>
+
 #include "rq_block.h"
 #include "rq_internal.h"
 
@@ -70,9 +72,12 @@ hipError_t launch_rmsnorm(int fmt, const uint16_t* h, int64_t rows, int64_t D, f
 }
 
 // ------------------------------------------------------------------ gate --
-// One workgroup per token.  Pass 1: the two largest logits (m1 >= m2).
-// Pass 2: Z = sum e^(z - m1) and W = sum (z - m1) e^(z - m1).  Then
-// H = log Z - W / Z and p1 - p2 = (1 - e^(m2 - m1)) / Z.
+// Softmax entropy and top-1 / top-2 margin from a row's two largest logits
+// m1 >= m2, Z = sum e^(z - m1) and W = sum (z - m1) e^(z - m1):
+// H = log Z - W / Z and p1 - p2 = (1 - e^(m2 - m1)) / Z.  A row splits into
+// ranges whose statistics (each relative to its own m1) merge exactly:
+// with M the larger maximum, Z = sum_g Z_g e^(m1_g - M) and
+// W = sum_g e^(m1_g - M) (W_g + (m1_g - M) Z_g).
 __device__ __forceinline__ void top2_merge(float& a1, float& a2, float b1, float b2) {
   if (b1 > a1) {
     a2 = fmaxf(a1, b2);
@@ -82,51 +87,136 @@ __device__ __forceinline__ void top2_merge(float& a1, float& a2, float b1, float
   }
 }
 
-__global__ __launch_bounds__(256) void gate_kernel(const uint16_t* __restrict__ logits, int64_t V, float tau,
-                                                   float delta, uint8_t* __restrict__ flags,
-                                                   float* __restrict__ stats) {
-  __shared__ float sh1[256], sh2[256];
-  __shared__ float shs[4];
-  const int64_t t = blockIdx.x;
-  const uint16_t* z = logits + t * V;
-  float m1 = -INFINITY, m2 = -INFINITY;
-  for (int64_t i = threadIdx.x; i < V; i += 256) top2_merge(m1, m2, bf16_to_f32(z[i]), -INFINITY);
-  sh1[threadIdx.x] = m1;
-  sh2[threadIdx.x] = m2;
-  __syncthreads();
-  for (int s = 128; s >= 1; s >>= 1) {
-    if ((int)threadIdx.x < s) {
-      float a1 = sh1[threadIdx.x], a2 = sh2[threadIdx.x];
-      top2_merge(a1, a2, sh1[threadIdx.x + s], sh2[threadIdx.x + s]);
-      sh1[threadIdx.x] = a1;
-      sh2[threadIdx.x] = a2;
-    }
-    __syncthreads();
-  }
-  const float M1 = sh1[0], M2 = sh2[0];
-  float zs = 0.0f, ws = 0.0f;
-  for (int64_t i = threadIdx.x; i < V; i += 256) {
-    const float d = bf16_to_f32(z[i]) - M1;
-    const float e = expf(d);
-    zs += e;
-    ws = fmaf(d, e, ws);
-  }
-  const float Z = block_sum(zs, shs);
-  const float Wt = block_sum(ws, shs);
-  if (threadIdx.x == 0) {
-    const float H = logf(Z) - Wt / Z;
-    const float gap = (1.0f - expf(M2 - M1)) / Z;
-    flags[t] = (H > tau || gap < delta) ? 1 : 0;
-    if (stats) {
-      stats[2 * t] = H;
-      stats[2 * t + 1] = gap;
+// Visits elements [lo, hi) of a BF16 row with the 256 threads of a
+// workgroup: the part from the first 16-byte boundary on in 8-element
+// vector loads, the few elements before it and after the last full vector
+// one per thread.
+template <typename F>
+__device__ __forceinline__ void gate_visit(const uint16_t* __restrict__ z, int64_t lo, int64_t hi, F&& fn) {
+  const int64_t head = ((16 - (reinterpret_cast<uintptr_t>(z + lo) & 15)) & 15) / 2;
+  const int64_t v0 = min(hi, lo + head);
+  const int64_t nv = (hi - v0) / 8, v1 = v0 + nv * 8;
+  const int tid = (int)threadIdx.x;
+  if (lo + tid < v0) fn(bf16_to_f32(z[lo + tid]));
+  if (v1 + tid < hi) fn(bf16_to_f32(z[v1 + tid]));
+  const uint4* zv = reinterpret_cast<const uint4*>(z + v0);
+  for (int64_t c = tid; c < nv; c += 256) {
+    const uint4 q = zv[c];
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fn(bf16_to_f32(w[i] & 0xFFFFu));
+      fn(bf16_to_f32(w[i] >> 16));
     }
   }
 }
 
+// The statistics of z[lo, hi) (non-empty), computed by a 256-thread
+// workgroup and returned to every thread; two passes, the second reading
+// the range again (from cache).
+__device__ __forceinline__ float4 gate_range(const uint16_t* __restrict__ z, int64_t lo, int64_t hi) {
+  __shared__ float s1[4], s2[4], ss[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float m1 = -INFINITY, m2 = -INFINITY;
+  gate_visit(z, lo, hi, [&](float v) {
+    m2 = fmaxf(m2, fminf(m1, v));
+    m1 = fmaxf(m1, v);
+  });
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) top2_merge(m1, m2, __shfl_xor(m1, o, 64), __shfl_xor(m2, o, 64));
+  if (lane == 0) s1[wave] = m1, s2[wave] = m2;
+  __syncthreads();
+  float M1 = s1[0], M2 = s2[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) top2_merge(M1, M2, s1[w], s2[w]);
+  float zs = 0.0f, ws = 0.0f;
+  gate_visit(z, lo, hi, [&](float v) {
+    const float d = v - M1;
+    const float e = expf(d);
+    zs += e;
+    ws = fmaf(d, e, ws);
+  });
+  const float Z = block_sum(zs, ss);
+  const float W = block_sum(ws, ss);
+  return make_float4(M1, M2, Z, W);
+}
+
+__device__ __forceinline__ void gate_finish(float M1, float M2, float Z, float W, float tau, float delta,
+                                            uint8_t* __restrict__ flags, float* __restrict__ stats, int64_t t) {
+  const float H = logf(Z) - W / Z;
+  const float gap = (1.0f - expf(M2 - M1)) / Z;
+  flags[t] = (H > tau || gap < delta) ? 1 : 0;
+  if (stats) {
+    stats[2 * t] = H;
+    stats[2 * t + 1] = gap;
+  }
+}
+
+// Without a workspace: one workgroup per token over its whole row.
+__global__ __launch_bounds__(256) void gate_kernel(const uint16_t* __restrict__ logits, int64_t V, float tau,
+                                                   float delta, uint8_t* __restrict__ flags,
+                                                   float* __restrict__ stats) {
+  const int64_t t = blockIdx.x;
+  const float4 r = gate_range(logits + t * V, 0, V);
+  if (threadIdx.x == 0) gate_finish(r.x, r.y, r.z, r.w, tau, delta, flags, stats, t);
+}
+
+// With a workspace: workgroup (g, t) takes range g of token t's row and
+// stores its statistics; gate_merge_kernel (one wave per token) combines
+// the token's ranges in a fixed order.
+__global__ __launch_bounds__(256) void gate_part_kernel(const uint16_t* __restrict__ logits, int64_t V,
+                                                        int64_t chunk, float4* __restrict__ parts) {
+  const int64_t g = blockIdx.x, t = blockIdx.y;
+  const int64_t lo = g * chunk, hi = min(V, lo + chunk);
+  const float4 r = gate_range(logits + t * V, lo, hi);
+  if (threadIdx.x == 0) parts[t * gridDim.x + g] = r;
+}
+
+__global__ __launch_bounds__(64) void gate_merge_kernel(const float4* __restrict__ parts, int G, float tau,
+                                                        float delta, uint8_t* __restrict__ flags,
+                                                        float* __restrict__ stats) {
+  const int64_t t = blockIdx.x;
+  const int lane = threadIdx.x;
+  const bool have = lane < G;
+  const float4 p = have ? parts[t * G + lane] : make_float4(-INFINITY, -INFINITY, 0.0f, 0.0f);
+  float M1 = p.x, M2 = p.y;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) top2_merge(M1, M2, __shfl_xor(M1, o, 64), __shfl_xor(M2, o, 64));
+  const float sc = have ? expf(p.x - M1) : 0.0f;
+  const float Z = wave_sum(have ? p.z * sc : 0.0f);
+  const float W = wave_sum(have ? sc * fmaf(p.x - M1, p.z, p.w) : 0.0f);
+  if (lane == 0) gate_finish(M1, M2, Z, W, tau, delta, flags, stats, t);
+}
+
+// Ranges per token for a split gate: about 512 workgroups in all, at most
+// 64 per token (one merge lane each), each range a multiple of 8 elements.
+static void gate_split(int64_t B, int64_t V, int64_t& G, int64_t& chunk) {
+  G = std::min<int64_t>(64, std::max<int64_t>(1, (512 + B - 1) / B));
+  chunk = ((V + G - 1) / G + 7) / 8 * 8;
+  G = (V + chunk - 1) / chunk;
+}
+
+size_t gate_workspace_bytes(int64_t B, int64_t V) {
+  if (B < 1 || V < 2) return 0;
+  int64_t G, chunk;
+  gate_split(B, V, G, chunk);
+  return G > 1 ? (size_t)(B * G) * sizeof(float4) : 0;
+}
+
 hipError_t launch_gate(const uint16_t* logits, int64_t B, int64_t V, float tau, float delta, uint8_t* flags,
-                       float* stats, hipStream_t stream) {
-  gate_kernel<<<(unsigned)B, 256, 0, stream>>>(logits, V, tau, delta, flags, stats);
+                       float* stats, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const size_t need = gate_workspace_bytes(B, V);
+  if (need == 0 || ws == nullptr || ws_bytes < need) {
+    gate_kernel<<<(unsigned)B, 256, 0, stream>>>(logits, V, tau, delta, flags, stats);
+    return hipGetLastError();
+  }
+  int64_t G, chunk;
+  gate_split(B, V, G, chunk);
+  float4* parts = static_cast<float4*>(ws);
+  gate_part_kernel<<<dim3((unsigned)G, (unsigned)B), 256, 0, stream>>>(logits, V, chunk, parts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  gate_merge_kernel<<<(unsigned)B, 64, 0, stream>>>(parts, (int)G, tau, delta, flags, stats);
   return hipGetLastError();
 }
 

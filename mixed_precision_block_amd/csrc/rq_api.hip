@@ -405,13 +405,19 @@ rq_status rq_gemv_nibble_escalate_grouped(const rq_gemv_problem* problems_dev, i
                     "rq_gemv_nibble_escalate_grouped launch");
 }
 
+size_t rq_escalation_gate_workspace_bytes(int64_t B, int64_t V) { return rq::gate_workspace_bytes(B, V); }
+
 rq_status rq_escalation_gate(const void* logits_bf16, int64_t B, int64_t V, float tau, float delta, uint8_t* flags,
-                             float* stats, void* stream) {
+                             float* stats, void* workspace, size_t ws_bytes, void* stream) {
   if (!logits_bf16 || !flags) return fail(RQ_EINVAL, "rq_escalation_gate: null pointer");
-  if (B < 1 || B > 16 || V < 2) return fail(RQ_ESHAPE, "rq_escalation_gate: need B in [1, 16] and V >= 2");
+  if (B < 1 || B > 16 || V < 2 || V > kInt32Max) return fail(RQ_ESHAPE, "rq_escalation_gate: need B in [1, 16] and V >= 2");
+  if ((reinterpret_cast<uintptr_t>(logits_bf16) & 1u) != 0)
+    return fail(RQ_EALIGN, "rq_escalation_gate: logits must be 2-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(stats) & 3u) != 0) return fail(RQ_EALIGN, "rq_escalation_gate: stats must be 4-byte aligned");
+  if (workspace && !aligned16(workspace)) return fail(RQ_EALIGN, "rq_escalation_gate: workspace must be 16-byte aligned");
   if (rq_status s = need_device(); s != RQ_OK) return s;
   return hip_status(rq::launch_gate(static_cast<const uint16_t*>(logits_bf16), B, V, tau, delta, flags, stats,
-                                    as_stream(stream)),
+                                    workspace, ws_bytes, as_stream(stream)),
                     "rq_escalation_gate launch");
 }
 

@@ -32,7 +32,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert rq.rq_abi_version() == L.ABI_VERSION == 2
+    assert rq.rq_abi_version() == L.ABI_VERSION == 3
     lib = L.lib()
     assert lib.rq_status_str(L.RQ_ESHAPE) == b"RQ_ESHAPE"
     assert lib.rq_status_str(99) == b"RQ_UNKNOWN"
@@ -136,7 +136,25 @@ def test_gemv_and_gate_validation():
     carry[4] = A16
     carry[11] = A16 + 2
     assert status_of(rq.rq_gemv_nibble_escalate, *carry) == L.RQ_EALIGN  # the carry is FP32: 4-byte aligned
-    assert status_of(rq.rq_escalation_gate, A16, 0, 100, 1.0, 0.1, A16, None) == L.RQ_ESHAPE
+    gate = [A16, 4, 100, 1.0, 0.1, A16, A16, A16, 1024]
+    for i, v, want in [(1, 0, L.RQ_ESHAPE), (1, 17, L.RQ_ESHAPE), (2, 1, L.RQ_ESHAPE), (2, 1 << 31, L.RQ_ESHAPE),
+                       (0, None, L.RQ_EINVAL), (5, None, L.RQ_EINVAL), (0, A16 + 1, L.RQ_EALIGN),
+                       (6, A16 + 2, L.RQ_EALIGN),
+                       (7, A16 + 8, L.RQ_EALIGN)]:
+        a = list(gate)
+        a[i] = v
+        assert status_of(rq.rq_escalation_gate, *a) == want, (i, v)
+    for i in (6, 7):  # stats and the workspace are optional
+        a = list(gate)
+        a[i] = None
+        assert status_of(rq.rq_escalation_gate, *a) in (L.RQ_OK, L.RQ_ENODEV)
+    # split gate: about 512 workgroups, at most 64 ranges per row, ranges a
+    # multiple of 8 elements, one float4 of statistics per range; a row that
+    # fits one range needs none
+    assert rq.rq_escalation_gate_workspace_bytes(16, 151936) == 16 * 32 * 16
+    assert rq.rq_escalation_gate_workspace_bytes(1, 100) == 13 * 16
+    assert rq.rq_escalation_gate_workspace_bytes(16, 2) == 0
+    assert rq.rq_escalation_gate_workspace_bytes(0, 100) == 0
     assert status_of(rq.rq_kv_quantize, A16, 4, 2, 100, A16, A16) == L.RQ_ESHAPE
     # split-K workspace: few row tiles -> slices x 16 token rows x padded rows x FP32; many tiles or bad shapes -> 0
     assert rq.rq_gemv_workspace_bytes(16, 1024, 1024) == 8 * 16 * 1024 * 4

@@ -21,18 +21,38 @@ def logits_batch(V=151936):
     return F.f64_to_bf16(z)
 
 
-def test_gate_stats_and_flags():
+@pytest.mark.parametrize("split", [True, False])
+def test_gate_stats_and_flags(split):
     z = logits_batch()
     h_o, gap_o = GT.softmax_stats(z)
     for tau, delta in ((5.0, 0.05), (11.0, 0.5), (0.0, 0.0)):
-        flags, stats = api.escalation_gate(dev_bf16(z), tau, delta)
+        flags, stats = api.escalation_gate(dev_bf16(z), tau, delta, split=split)
         st = host(stats)
         assert np.allclose(st[:, 0], h_o, rtol=1e-4, atol=1e-4), (st[:, 0], h_o)
         assert np.allclose(st[:, 1], gap_o, rtol=1e-4, atol=1e-6), (st[:, 1], gap_o)
         want = GT.escalation_flags(z, tau, delta)
         clear = (np.abs(h_o - tau) > 1e-3) & (np.abs(gap_o - delta) > 1e-4)
         assert np.array_equal(host(flags)[clear], want[clear])
-        log(f"gate tau={tau} delta={delta}: flags {host(flags).tolist()}")
+        log(f"gate split={split} tau={tau} delta={delta}: flags {host(flags).tolist()}")
+
+
+@pytest.mark.parametrize("B,V", [(16, 151936), (3, 1001), (5, 7), (2, 2), (16, 4097)])
+def test_gate_ragged_rows_split_and_whole(B, V):
+    """Row lengths that leave rows off 16-byte boundaries (scalar head and
+    tail elements), rows shorter than one vector, and a row that splits into
+    ranges with a short last one: both launch forms against the oracle."""
+    rng = np.random.default_rng(B * 100003 + V)
+    z = F.f64_to_bf16(rng.standard_normal((B, V)) * rng.uniform(0.5, 6.0, (B, 1)))
+    h_o, gap_o = GT.softmax_stats(z)
+    got = {}
+    for split in (True, False):
+        flags, stats = api.escalation_gate(dev_bf16(z), 1.0, 0.01, split=split)
+        st = host(stats)
+        assert np.allclose(st[:, 0], h_o, rtol=1e-4, atol=1e-4), (split, st[:, 0], h_o)
+        assert np.allclose(st[:, 1], gap_o, rtol=1e-4, atol=1e-6), (split, st[:, 1], gap_o)
+        got[split] = st
+    assert np.allclose(got[True], got[False], rtol=1e-5, atol=1e-6)
+    log(f"gate B={B} V={V}: split and whole-row statistics agree with the oracle")
 
 
 @pytest.mark.parametrize("T,H,D", [(256, 8, 128), (37, 3, 256), (1, 1, 128)])
