@@ -232,7 +232,7 @@ rq_status rq_recurrent_prefill(void *h_bf16, int64_t S, int64_t D, int64_t F,
  *     (j = 0..3);
  *   scale of (n, b) at ((n/64) * (K/32) + b) * 64 + (n%64).
  * hi, lo: rq_nibble_plane_bytes(N, K) bytes each; scales_tiled:
- * rq_nibble_scale_bytes(N, K) bytes; all three 16-byte aligned.
+ * rq_nibble_scale_bytes(N, K) bytes; the planes 16-byte aligned.
  */
 size_t rq_nibble_plane_bytes(int64_t N, int64_t K);
 size_t rq_nibble_scale_bytes(int64_t N, int64_t K);
@@ -249,10 +249,9 @@ rq_status rq_pack_nibble_planes(const int8_t *w, const uint16_t *scales_f16,
  *                is set
  *   RQ_BOTH      RQ_LOW then RQ_ESCALATE
  * x_bf16 [B x K] BF16 with B in [1, 16]; planes/scales from
- * rq_pack_nibble_planes; x, planes and scales_tiled 16-byte aligned;
- * flags [B] uint8 (device; may be NULL for RQ_LOW); y_bf16 [B x N] BF16.
- * FP32 accumulation, BF16 output (for B > 4 the low pass forms each
- * 32-block's sum on the matrix cores, BF16 products summed in FP32).
+ * rq_pack_nibble_planes; x and planes 16-byte aligned; flags [B] uint8
+ * (device; may be NULL for RQ_LOW); y_bf16 [B x N] BF16.  FP32
+ * accumulation, BF16 output.
  * workspace: device scratch of ws_bytes >= rq_gemv_workspace_bytes(B, N,
  * K) bytes (caller-owned, contents irrelevant) lets shapes with few 64-row
  * tiles split K over more workgroups; NULL / smaller runs them unsplit.
@@ -288,8 +287,8 @@ rq_status rq_gemv_nibble_escalate(const void *x_bf16, int64_t B, int64_t K,
  * filled by rq_gemv_group_plan.
  *
  * rq_gemv_group_plan (host): validates every entry (non-NULL x, w_hi,
- * scales_tiled and y; N > 0; K > 0 with K % 32 == 0; 16-byte aligned x,
- * planes and scales_tiled), sets tile_start to the running sum of ceil(N / 64), and returns
+ * scales_tiled and y; N > 0; K > 0 with K % 32 == 0; 16-byte aligned x and
+ * planes), sets tile_start to the running sum of ceil(N / 64), and returns
  * the total number of 64-row tiles, or -1 (with rq_last_error) if an entry
  * is invalid or count < 1.
  *

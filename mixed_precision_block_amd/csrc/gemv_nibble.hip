@@ -1,8 +1,6 @@
 // Decode GEMV on 8-bit weights read through their top nibble, with 8-bit
 // recompute of flagged tokens (Escalating Weight Precision Only When
-// Decoding Becomes Uncertain, setup paragraph).  The low pass over 8 or 16
-// tokens is a dense 16-column contraction and runs on the matrix cores
-// (16x16x32 BF16 MFMA); fewer tokens and the escalation use the VALU.
+// Decoding Becomes Uncertain, setup paragraph).  VALU only: no MFMA.
 //
 // Storage (made by pack_planes_kernel): two nibble planes, hi = w >> 4
 // (two's complement) and lo = w & 15, tiled by 64 rows so that a wave's
@@ -77,19 +75,6 @@ __device__ __forceinline__ void unpack_hi16(const uint4 d, bf16x2 wp[16]) {
   for (int q = 0; q < 4; ++q) pairs_from_bytes((dq[q] << 4) & 0xF0F0F0F0u, dq[q] & 0xF0F0F0F0u, wp + 4 * q);
 }
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-// 16 * hi for the 8 nibbles of one dword of a hi-plane chunk (k = 8q ..
-// 8q + 7 in order) as the eight BF16 values of an MFMA operand.
-__device__ __forceinline__ bf16x8 unpack_hi8(uint32_t d) {
-  bf16x2 wp[4];
-  pairs_from_bytes((d << 4) & 0xF0F0F0F0u, d & 0xF0F0F0F0u, wp);
-  const uint4 u = make_uint4(__builtin_bit_cast(uint32_t, wp[0]), __builtin_bit_cast(uint32_t, wp[1]),
-                             __builtin_bit_cast(uint32_t, wp[2]), __builtin_bit_cast(uint32_t, wp[3]));
-  return __builtin_bit_cast(bf16x8, u);
-}
-
 // lo (0..15) for the 16 pairs of a lo-plane chunk: each nibble in the low
 // half of its byte.
 __device__ __forceinline__ void unpack_lo16(const uint4 d, bf16x2 wp[16]) {
@@ -123,32 +108,6 @@ enum Planes { kHi = 0, kHiLo = 1, kLo = 2 };
 // ws[slice][token][row] (16 token rows per slice) that gemv_reduce_kernel
 // adds in slice order.
 constexpr int kWsTokens = 16;
-
-// The four waves' sums of a tile, red[wave][token slot][row], added in wave
-// order; with one slice BF16 outputs (kHi: also the FP32 carry yf when
-// given; kLo: adds the carry first), else FP32 partials to
-// ws[slice][token][row] for gemv_reduce_kernel.
-template <int TB, int kP>
-__device__ __forceinline__ void finish_tile(const int* tok, int nt, int N, uint16_t* __restrict__ y,
-                                            float* __restrict__ yf, float* __restrict__ ws, float (*red)[TB][64],
-                                            int tile, int slice, int nslice) {
-  for (int o = threadIdx.x; o < TB * 64; o += 256) {
-    const int t = o >> 6, l = o & 63;
-    const int n = tile * 64 + l;
-    if (t >= nt) continue;
-    float v = ((red[0][t][l] + red[1][t][l]) + red[2][t][l]) + red[3][t][l];
-    if (nslice == 1) {
-      if (n < N) {
-        const size_t o = (size_t)tok[t] * N + n;
-        if constexpr (kP == kLo) v = yf[o] + v;
-        if (kP == kHi && yf != nullptr) yf[o] = v;
-        y[o] = (uint16_t)f32_to_bf16(v);
-      }
-    } else {
-      ws[((size_t)slice * kWsTokens + tok[t]) * ((size_t)((N + 63) / 64) * 64) + n] = v;
-    }
-  }
-}
 
 template <int TB, int kP>
 __device__ __forceinline__ void gemv_tile(const uint16_t* __restrict__ x, int B, int K, int N,
@@ -250,91 +209,22 @@ __device__ __forceinline__ void gemv_tile(const uint16_t* __restrict__ x, int B,
 #pragma unroll
   for (int t = 0; t < TB; ++t) red[wave][t][lane] = acc[t];
   __syncthreads();
-  finish_tile<TB, kP>(tok, nt, N, y, yf, ws, red, tile, slice, nslice);
-}
-
-// Low pass on the matrix cores, for 8 or 16 tokens.  The tile is 64 rows
-// x 16 token columns; per 32-block one wave issues four 16x16x32 BF16
-// MFMAs, one per 16-row group g: operand A is 16 * hi of rows 16g + (l %
-// 16), eight k each (lane l takes dword l / 16 of the row's chunk, k = 8
-// (l / 16) .. + 7), operand B the same eight k of token l % 16 (one 16-byte
-// load of the BF16 row; tokens past B repeat the last and are not stored).
-// Lane l receives rows 16g + 4 (l / 16) + i, i < 4, of token l % 16; the
-// block's FP16 scales of those rows multiply them into FP32 accumulators.
-// Blocks are interleaved over the four waves as in gemv_tile, whose
-// epilogue (finish_tile) this shares.  Each wave loads kLowPF blocks of
-// operands ahead.  The VALU work of unpacking the nibbles (about 60 of the
-// block's 100 instructions) and each wave's fixed cost bound it, not the
-// memory: loads from a fixed block time the same, and deeper, strictly
-// ordered prefetch was slower (it stops the scheduler interleaving one
-// block's unpacking with another block's MFMAs).
-constexpr int kLowPF = 3;
-
-template <int TB>
-__device__ __forceinline__ void gemv_low_mfma_tile(const uint16_t* __restrict__ x, int B, int K, int N,
-                                                   const uint8_t* __restrict__ hi, const uint16_t* __restrict__ sc,
-                                                   const int* tok, int nt, uint16_t* __restrict__ y,
-                                                   float* __restrict__ yf, float* __restrict__ ws,
-                                                   float (*red)[TB][64], int tile, int slice, int nslice) {
-  static_assert(TB == 8 || TB == 16, "the MFMA low pass takes 8 or 16 token slots");
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int col = lane & 15, q = lane >> 4;
-  const int nb = K >> 5;
-  const int per = (nb + nslice - 1) / nslice;
-  const int b0 = slice * per, b1 = min(nb, b0 + per);
-  const int xt = col < B ? col : B - 1;
-  // block b: x chunk xg[4 b]; weight dword of group g at hp[256 b + 64 g];
-  // scales of rows 16 g + 4 q .. + 3 at sp[16 b + 4 g]
-  const uint4* xg = reinterpret_cast<const uint4*>(x + (size_t)xt * K) + q;
-  const uint32_t* hp = reinterpret_cast<const uint32_t*>(hi) + (size_t)tile * nb * 256 + col * 4 + q;
-  const uint2* sp = reinterpret_cast<const uint2*>(sc + (size_t)tile * nb * 64) + q;
-  f32x4 acc[4];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) acc[g] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-  // a ring of kLowPF blocks in flight per wave: slot f holds the operands of
-  // block b + 4 f and is refilled with block b + 4 (f + kLowPF) once used
-  uint4 rx[kLowPF];
-  uint32_t rd[kLowPF][4];
-  uint2 rs[kLowPF][4];
-  const auto fill = [&](int f, int bb) {
-    rx[f] = xg[(size_t)bb * 4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) rd[f][g] = hp[(size_t)bb * 256 + 64 * g], rs[f][g] = sp[(size_t)bb * 16 + 4 * g];
-  };
-  int b = b0 + wave;
-#pragma unroll
-  for (int f = 0; f < kLowPF; ++f)
-    if (b + 4 * f < b1) fill(f, b + 4 * f);
-  for (; b < b1; b += 4 * kLowPF) {
-#pragma unroll
-    for (int f = 0; f < kLowPF; ++f) {
-      const int bb = b + 4 * f;
-      if (bb >= b1) break;
-      const bf16x8 bx = __builtin_bit_cast(bf16x8, rx[f]);
-      f32x4 c[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        c[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unpack_hi8(rd[f][g]), bx, (f32x4){0.0f, 0.0f, 0.0f, 0.0f},
-                                                      0, 0, 0);
-      uint32_t sv[4][2];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) sv[g][0] = rs[f][g].x, sv[g][1] = rs[f][g].y;
-      if (bb + 4 * kLowPF < b1) fill(f, bb + 4 * kLowPF);
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[g][i] = fmaf(c[g][i], f16_to_f32((uint16_t)(sv[g][i >> 1] >> (16 * (i & 1)))), acc[g][i]);
+  for (int o = threadIdx.x; o < TB * 64; o += 256) {
+    const int t = o >> 6, l = o & 63;
+    const int n = tile * 64 + l;
+    if (t >= nt) continue;
+    float v = ((red[0][t][l] + red[1][t][l]) + red[2][t][l]) + red[3][t][l];
+    if (nslice == 1) {
+      if (n < N) {
+        const size_t o = (size_t)tok[t] * N + n;
+        if constexpr (kP == kLo) v = yf[o] + v;
+        if (kP == kHi && yf != nullptr) yf[o] = v;
+        y[o] = (uint16_t)f32_to_bf16(v);
+      }
+    } else {
+      ws[((size_t)slice * kWsTokens + tok[t]) * ((size_t)((N + 63) / 64) * 64) + n] = v;
     }
   }
-  if (col < TB) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-      *reinterpret_cast<f32x4*>(&red[wave][col][16 * g + 4 * q]) = acc[g];
-  }
-  __syncthreads();
-  finish_tile<TB, kHi>(tok, nt, N, y, yf, ws, red, tile, slice, nslice);
 }
 
 template <int TB>
@@ -342,17 +232,13 @@ __global__ __launch_bounds__(256) void gemv_low_kernel(const uint16_t* __restric
                                                        const uint8_t* __restrict__ hi,
                                                        const uint16_t* __restrict__ sc, uint16_t* __restrict__ y,
                                                        float* __restrict__ yf, float* __restrict__ ws) {
-  __shared__ __attribute__((aligned(16))) float red[4][TB][64];  // float4 stores of the MFMA tile
+  __shared__ float red[4][TB][64];
   __shared__ uint4 xs[4 * 64];
   int tok[TB];
 #pragma unroll
   for (int t = 0; t < TB; ++t) tok[t] = t;
-  if constexpr (TB >= 8)
-    gemv_low_mfma_tile<TB>(x, B, K, N, hi, sc, tok, B < TB ? B : TB, y, yf, ws, red, blockIdx.x, blockIdx.y,
-                           gridDim.y);
-  else
-    gemv_tile<TB, kHi>(x, B, K, N, hi, nullptr, sc, tok, B < TB ? B : TB, y, yf, ws, red, xs, blockIdx.x,
-                       blockIdx.y, gridDim.y);
+  gemv_tile<TB, kHi>(x, B, K, N, hi, nullptr, sc, tok, B < TB ? B : TB, y, yf, ws, red, xs, blockIdx.x, blockIdx.y,
+                     gridDim.y);
 }
 
 // Escalation: a workgroup takes the flagged tokens in groups of four (in
@@ -550,7 +436,7 @@ __device__ __forceinline__ const rq_gemv_problem* find_problem(const rq_gemv_pro
 template <int TB>
 __global__ __launch_bounds__(256) void gemv_low_grouped_kernel(const rq_gemv_problem* __restrict__ probs, int count,
                                                                int B) {
-  __shared__ __attribute__((aligned(16))) float red[4][TB][64];  // float4 stores of the MFMA tile
+  __shared__ float red[4][TB][64];
   __shared__ uint4 xs[4 * 64];
   const rq_gemv_problem* p = find_problem(probs, count, blockIdx.x);
   const int64_t tile = (int64_t)blockIdx.x - p->tile_start;
@@ -558,14 +444,9 @@ __global__ __launch_bounds__(256) void gemv_low_grouped_kernel(const rq_gemv_pro
   int tok[TB];
 #pragma unroll
   for (int t = 0; t < TB; ++t) tok[t] = t;
-  if constexpr (TB >= 8)
-    gemv_low_mfma_tile<TB>(static_cast<const uint16_t*>(p->x_bf16), B, (int)p->K, (int)p->N, p->w_hi,
-                           p->scales_tiled, tok, B < TB ? B : TB, static_cast<uint16_t*>(p->y_bf16), p->y_f32,
-                           nullptr, red, (int)tile, 0, 1);
-  else
-    gemv_tile<TB, kHi>(static_cast<const uint16_t*>(p->x_bf16), B, (int)p->K, (int)p->N, p->w_hi, nullptr,
-                       p->scales_tiled, tok, B < TB ? B : TB, static_cast<uint16_t*>(p->y_bf16), p->y_f32, nullptr,
-                       red, xs, (int)tile, 0, 1);
+  gemv_tile<TB, kHi>(static_cast<const uint16_t*>(p->x_bf16), B, (int)p->K, (int)p->N, p->w_hi, nullptr,
+                     p->scales_tiled, tok, B < TB ? B : TB, static_cast<uint16_t*>(p->y_bf16), p->y_f32, nullptr,
+                     red, xs, (int)tile, 0, 1);
 }
 
 // LDS for the grouped escalation's copy of the flagged tokens' x: problems

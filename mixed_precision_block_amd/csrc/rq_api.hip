@@ -311,8 +311,7 @@ rq_status rq_pack_nibble_planes(const int8_t* w, const uint16_t* scales_f16, int
     return fail(RQ_EINVAL, "rq_pack_nibble_planes: null pointer");
   if (N < 0 || K <= 0 || K % 32 || N > kInt32Max || K > kInt32Max)
     return fail(RQ_ESHAPE, "rq_pack_nibble_planes: need K > 0, K %% 32 == 0");
-  if (!aligned16(hi) || !aligned16(lo) || !aligned16(scales_tiled))
-    return fail(RQ_EALIGN, "rq_pack_nibble_planes: planes and tiled scales must be 16-byte aligned");
+  if (!aligned16(hi) || !aligned16(lo)) return fail(RQ_EALIGN, "rq_pack_nibble_planes: planes must be 16-byte aligned");
   if (rq_status s = need_device(); s != RQ_OK) return s;
   return hip_status(rq::launch_pack_nibble_planes(w, scales_f16, N, K, hi, lo, scales_tiled, as_stream(stream)),
                     "rq_pack_nibble_planes launch");
@@ -337,8 +336,8 @@ rq_status rq_gemv_nibble_escalate(const void* x_bf16, int64_t B, int64_t K, int6
   if (B < 1 || B > 16) return fail(RQ_ESHAPE, "rq_gemv_nibble_escalate: B must be in [1, 16]");
   if (N < 0 || K <= 0 || K % 32 || N > kInt32Max || K > kInt32Max)
     return fail(RQ_ESHAPE, "rq_gemv_nibble_escalate: need K > 0, K %% 32 == 0");
-  if (!aligned16(x_bf16) || !aligned16(w_hi) || (w_lo && !aligned16(w_lo)) || !aligned16(scales_tiled))
-    return fail(RQ_EALIGN, "rq_gemv_nibble_escalate: x, planes and scales must be 16-byte aligned");
+  if (!aligned16(x_bf16) || !aligned16(w_hi) || (w_lo && !aligned16(w_lo)))
+    return fail(RQ_EALIGN, "rq_gemv_nibble_escalate: x and planes must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(y_f32) & 3u) != 0)
     return fail(RQ_EALIGN, "rq_gemv_nibble_escalate: y_f32 must be 4-byte aligned");
   if (workspace && !aligned16(workspace)) return fail(RQ_EALIGN, "rq_gemv_nibble_escalate: workspace must be 16-byte aligned");
@@ -370,8 +369,8 @@ int64_t rq_gemv_group_plan(rq_gemv_problem* problems, int count) {
       fail(RQ_ESHAPE, "rq_gemv_group_plan: problem %d needs N > 0, K > 0, K %% 32 == 0", i);
       return -1;
     }
-    if (!aligned16(p.x_bf16) || !aligned16(p.w_hi) || (p.w_lo && !aligned16(p.w_lo)) || !aligned16(p.scales_tiled)) {
-      fail(RQ_EALIGN, "rq_gemv_group_plan: problem %d: x, planes and scales must be 16-byte aligned", i);
+    if (!aligned16(p.x_bf16) || !aligned16(p.w_hi) || (p.w_lo && !aligned16(p.w_lo))) {
+      fail(RQ_EALIGN, "rq_gemv_group_plan: problem %d: x and planes must be 16-byte aligned", i);
       return -1;
     }
     if ((reinterpret_cast<uintptr_t>(p.y_f32) & 3u) != 0) {

@@ -115,8 +115,7 @@ def test_recurrent_prefill_validation():
 def test_gemv_and_gate_validation():
     g = [A16, 16, 1024, 64, A16, A16, A16, A16, L.RQ_BOTH, None, 0, None, A16]
     for i, v, want in [(1, 0, L.RQ_ESHAPE), (1, 17, L.RQ_ESHAPE), (2, 1000, L.RQ_ESHAPE), (8, 4, L.RQ_EINVAL),
-                       (5, None, L.RQ_EINVAL), (7, None, L.RQ_EINVAL), (9, A16 + 4, L.RQ_EALIGN),
-                       (6, A16 + 2, L.RQ_EALIGN), (6, A16 + 8, L.RQ_EALIGN)]:  # tiled scales: 16-byte aligned
+                       (5, None, L.RQ_EINVAL), (7, None, L.RQ_EINVAL), (9, A16 + 4, L.RQ_EALIGN)]:
         a = list(g)
         a[i] = v
         assert status_of(rq.rq_gemv_nibble_escalate, *a) == want, (i, v)
@@ -187,7 +186,7 @@ def test_gemv_group_plan_and_grouped_validation():
         arr[i] = P(A16, A16, None, A16, A16, None, n, k, 0)
     assert rq.rq_gemv_group_plan(arr) == 2 + 1 + 2374
     assert [arr[i].tile_start for i in range(3)] == [0, 2, 3]
-    for field, value in (("K", 33), ("N", 0), ("x_bf16", None), ("w_hi", A16 + 8), ("scales_tiled", A16 + 2)):
+    for field, value in (("K", 33), ("N", 0), ("x_bf16", None), ("w_hi", A16 + 8)):
         bad = (P * 1)()
         bad[0] = P(A16, A16, None, A16, A16, None, 64, 32, 0)
         setattr(bad[0], field, value)
