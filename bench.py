@@ -200,7 +200,7 @@ def main():
                     help="only run plain 256 MiB device copies (the reference for HBM byte counters)")
     ap.add_argument("--only", choices=["square", "gemv"],
                     help="run only one group of rows (4096^3 GEMMs and the ARC front end, or the nibble GEMV "
-                         "with the escalation gate and the KV tiles) "
+                         "kernels without the escalation gate) "
                          "and print them; for profiling runs")
     ap.add_argument("--traffic-from", metavar="DIR",
                     help="write the traffic summary from rocprofv3 --pmc CSV runs under DIR (pmc_main_FETCH_SIZE, "
@@ -231,8 +231,7 @@ def main():
         if args.only == "square":
             out = measure_square(torch, api, L, W, to_dev_only, dev)
         else:
-            out = measure_gemv(torch, np, api, L, W, dev)
-            out["kv_quantize_fp8_tile128_4096x8x128"] = measure_kv(torch, L, dev)
+            out = measure_gemv(torch, np, api, L, W, dev, gate=False)
         print(json.dumps(out), flush=True)
         return
     if args.calibrate_copy:
@@ -671,7 +670,7 @@ def gpu_int8_weights(torch, gen, N, K, dev):
     return q, s.view(torch.int16)
 
 
-def measure_gemv(torch, np, api, L, W, dev):
+def measure_gemv(torch, np, api, L, W, dev, gate=True):
     out = {}
     B = 16
     gen = torch.Generator(device=dev)
@@ -756,42 +755,10 @@ def measure_gemv(torch, np, api, L, W, dev):
         "us": round(ms * 1e3, 2), "gb_s": round(esc_lo_bytes(N, K, nf_lm) / (ms * 1e-3) / 1e9, 1),
         "frac_hbm": round(esc_lo_bytes(N, K, nf_lm) / (ms * 1e-3) / PEAK["hbm"], 4),
         "bytes": esc_lo_bytes(N, K, nf_lm)}
-    # the escalation gate over the LM head's low-pass logits [16 x 151936]
-    # (softmax entropy and top-1 / top-2 margin per token), alone and as the
-    # middle of the LM head's whole decode step on the device: low pass with
-    # the carry, gate, lo-plane escalation of the tokens it flags.  tau sits
-    # between the second and third largest entropy, so the gate flags two
-    # tokens as the seeded flags above do; delta = 0 leaves the margin test
-    # off (random logits have no confident tokens).
-    lm_low_carry()
-    logits = ys[N]
-    gflags = torch.empty(B, dtype=torch.uint8, device=dev)
-    gstats = torch.empty((B, 2), dtype=torch.float32, device=dev)
-    gwsb = L.rq_escalation_gate_workspace_bytes(B, N)
-    gws = torch.empty(max(gwsb, 16), dtype=torch.uint8, device=dev)
-    L.rq_escalation_gate(logits, B, N, 0.0, 0.0, gflags, gstats, gws, gwsb)
-    ent = sorted(gstats[:, 0].tolist(), reverse=True)
-    tau = 0.5 * (ent[1] + ent[2])
-    ms = time_calls(torch, lambda: L.rq_escalation_gate(logits, B, N, tau, 0.0, gflags, gstats, gws, gwsb), 100,
-                    graph=True)
-    gate_bytes = B * N * 2
-    out["escalation_gate_lm_head_logits_16x151936"] = {
-        "us": round(ms * 1e3, 2), "gb_s": round(gate_bytes / (ms * 1e-3) / 1e9, 1),
-        "frac_hbm": round(gate_bytes / (ms * 1e-3) / PEAK["hbm"], 4), "bytes": gate_bytes}
-
-    def lm_decode_step():
-        lm_low_carry()
-        L.rq_escalation_gate(logits, B, N, tau, 0.0, gflags, gstats, gws, gwsb)
-        c = copies[it[0] % 4]
-        it[0] += 1
-        L.rq_gemv_nibble_escalate(xs[K], B, K, N, None, c[1], c[2], gflags, L.RQ_ESCALATE, wsp, wsb, carry, ys[N])
-
-    ms = time_calls(torch, lm_decode_step, 40)
-    out["gemv_lm_head_decode_step_low_gate_escalate_b16"] = {
-        "us": round(ms * 1e3, 2), "flagged": int(gflags.sum().item()),
-        "us_parts_sum": round(out["gemv_lm_head_low_pass_b16_with_carry"]["us"]
-                              + out["escalation_gate_lm_head_logits_16x151936"]["us"]
-                              + out["gemv_lm_head_escalation_2_of_16_lo_plane_from_carry"]["us"], 2)}
+    if gate:
+        parts_us = (out["gemv_lm_head_low_pass_b16_with_carry"]["us"]
+                    + out["gemv_lm_head_escalation_2_of_16_lo_plane_from_carry"]["us"])
+        out.update(measure_gate(torch, L, dev, N, K, xs, ys, copies, it, carry, wsp, wsb, lm_low_carry, parts_us))
     del copies, carry
 
     def sweep(phase):
@@ -857,6 +824,48 @@ def measure_gemv(torch, np, api, L, W, dev):
         "us": round(ms_esc * 1e3, 1), "gb_s": round(tot_esc / (ms_esc * 1e-3) / 1e9, 1),
         "frac_hbm": round(tot_esc / (ms_esc * 1e-3) / PEAK["hbm"], 4), "bytes": tot_esc}
     log(f"rows: GEMV {out}")
+    return out
+
+
+def measure_gate(torch, L, dev, N, K, xs, ys, copies, it, carry, wsp, wsb, lm_low_carry, parts_us):
+    """The escalation gate rows; parts_us: the carry low pass plus the
+    lo-plane escalation of the LM head, microseconds."""
+    out = {}
+    B = ys[N].shape[0]
+    # the escalation gate over the LM head's low-pass logits [16 x 151936]
+    # (softmax entropy and top-1 / top-2 margin per token), alone and as the
+    # middle of the LM head's whole decode step on the device: low pass with
+    # the carry, gate, lo-plane escalation of the tokens it flags.  tau sits
+    # between the second and third largest entropy, so the gate flags two
+    # tokens as the seeded flags above do; delta = 0 leaves the margin test
+    # off (random logits have no confident tokens).
+    lm_low_carry()
+    logits = ys[N]
+    gflags = torch.empty(B, dtype=torch.uint8, device=dev)
+    gstats = torch.empty((B, 2), dtype=torch.float32, device=dev)
+    gwsb = L.rq_escalation_gate_workspace_bytes(B, N)
+    gws = torch.empty(max(gwsb, 16), dtype=torch.uint8, device=dev)
+    L.rq_escalation_gate(logits, B, N, 0.0, 0.0, gflags, gstats, gws, gwsb)
+    ent = sorted(gstats[:, 0].tolist(), reverse=True)
+    tau = 0.5 * (ent[1] + ent[2])
+    ms = time_calls(torch, lambda: L.rq_escalation_gate(logits, B, N, tau, 0.0, gflags, gstats, gws, gwsb), 100,
+                    graph=True)
+    gate_bytes = B * N * 2
+    out["escalation_gate_lm_head_logits_16x151936"] = {
+        "us": round(ms * 1e3, 2), "gb_s": round(gate_bytes / (ms * 1e-3) / 1e9, 1),
+        "frac_hbm": round(gate_bytes / (ms * 1e-3) / PEAK["hbm"], 4), "bytes": gate_bytes}
+
+    def lm_decode_step():
+        lm_low_carry()
+        L.rq_escalation_gate(logits, B, N, tau, 0.0, gflags, gstats, gws, gwsb)
+        c = copies[it[0] % 4]
+        it[0] += 1
+        L.rq_gemv_nibble_escalate(xs[K], B, K, N, None, c[1], c[2], gflags, L.RQ_ESCALATE, wsp, wsb, carry, ys[N])
+
+    ms = time_calls(torch, lm_decode_step, 40)
+    out["gemv_lm_head_decode_step_low_gate_escalate_b16"] = {
+        "us": round(ms * 1e3, 2), "flagged": int(gflags.sum().item()),
+        "us_parts_sum": round(parts_us + out["escalation_gate_lm_head_logits_16x151936"]["us"], 2)}
     return out
 
 
