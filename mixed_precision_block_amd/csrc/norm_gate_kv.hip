@@ -222,7 +222,8 @@ hipError_t launch_gate(const uint16_t* logits, int64_t B, int64_t V, float tau, 
 
 // -------------------------------------------------------------- KV tiles --
 // 16 threads per 128-element tile, 8 elements each; amax over the 16 lanes
-// by xor-shuffles; float32 scale amax / 448 and float32 division.
+// by xor-shuffles; float32 scale amax / 448 and float32 division (correctly
+// rounded, as the listing's division is).
 __global__ __launch_bounds__(256) void kv_quant_kernel(const uint16_t* __restrict__ x, int64_t tiles,
                                                        uint8_t* __restrict__ codes, float* __restrict__ scales) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -245,14 +246,16 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(const uint16_t* __restric
   if (!active) return;
   const float amax = bf16_to_f32(m);
   const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
-  uint32_t c0 = 0, c1 = 0;
+  // clipped quotients -> E4M3FN by the hardware conversion (round to
+  // nearest even, subnormals included; nothing left to saturate), two per
+  // instruction, element i in byte i
+  float c[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float a = fminf(fmaxf(v[i] / scale, -448.0f), 448.0f);
-    const float b = fminf(fmaxf(v[4 + i] / scale, -448.0f), 448.0f);
-    c0 |= e4m3_encode_f32(a) << (8 * i);
-    c1 |= e4m3_encode_f32(b) << (8 * i);
-  }
+  for (int i = 0; i < 8; ++i) c[i] = fminf(fmaxf(v[i] / scale, -448.0f), 448.0f);
+  uint32_t c0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+  c0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], (int)c0, true);
+  uint32_t c1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
+  c1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], (int)c1, true);
   *reinterpret_cast<uint2*>(codes + tile * 128 + sub * 8) = make_uint2(c0, c1);
   if (sub == 0) scales[tile] = scale;
 }

@@ -62,3 +62,30 @@ def test_kv_quant_bit_exact(T, H, D):
     oc, os_ = KV.quantize_kv(x)
     assert np.array_equal(host(scales), os_)
     assert np.array_equal(host(codes), oc)
+
+
+def test_kv_quant_rounding_boundaries():
+    """Tiles whose amax is 448 have scale 1, so x / scale is x itself: BF16
+    values placed on every E4M3 rounding tie (normal binades and the
+    subnormal range), both signs, -0 and BF16 subnormals pin the encoding of
+    the clipped quotients to the oracle's round-to-nearest-even bit for bit."""
+    mids = [(1 + (2 * j + 1) / 16) * 2.0 ** e for e in range(-6, 9) for j in range(8)]
+    mids = [m for m in mids if m < 448]                      # ties between normal codes
+    subs = [(2 * m + 1) * 2.0 ** -10 for m in range(8)]     # ties in the subnormal range
+    exact = [k * 2.0 ** -9 for k in range(16)] + [2.0 ** e for e in range(-9, 9)]
+    tiny = [2.0 ** -133, 2.0 ** -127, 2.0 ** -126, 2.0 ** -11]  # BF16 subnormals and quotients far below 2^-9
+    vals = mids + subs + exact + tiny
+    vals = vals + [-v for v in vals] + [-0.0]
+    tiles = []
+    for i in range(0, len(vals), 127):
+        chunk = vals[i:i + 127]
+        tiles.append([448.0] + chunk + [0.0] * (127 - len(chunk)))
+    x = np.asarray(tiles, np.float64).reshape(len(tiles), 1, 128)
+    bits = F.f64_to_bf16(x)
+    assert np.array_equal(F.bf16_to_f64(bits), x), "every probe value is a BF16 value"
+    codes, scales = api.kv_quantize(dev_bf16(bits))
+    oc, os_ = KV.quantize_kv(bits)
+    assert np.array_equal(host(scales), os_)
+    assert np.all(host(scales) == 1.0)
+    assert np.array_equal(host(codes), oc)
+    log(f"KV rounding boundaries: {len(vals)} values in {len(tiles)} tiles encode as the oracle does")

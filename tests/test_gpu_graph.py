@@ -1,7 +1,8 @@
 """HIP-graph capture of library calls: a captured sequence (quantize + GEMM,
 nibble GEMVs including the split-K partial sums and their reduction, two of
-them through the FP32 carry, and a short recurrent prefill whose quantized
-steps quantize u in the GEMM epilogue) replays to the eager results, bit for
+them through the FP32 carry, a short recurrent prefill whose quantized
+steps quantize u in the GEMM epilogue, and the escalation gate split over
+ranges with its merge) replays to the eager results, bit for
 bit, on every replay, with eager work and synchronizations between the
 replays.  Nothing the library launches records a memset, so the captured
 graph holds only kernel nodes."""
@@ -47,6 +48,12 @@ def test_graph_replays_match_eager():
     h = h0.clone()
     rws = torch.empty(L.rq_recurrent_prefill_workspace_bytes(256, 256, 512, L.RQ_MXFP4), dtype=torch.uint8,
                       device="cuda")
+    # the escalation gate over the second GEMV's outputs (16 x 20000 logits), split over ranges
+    gv = gemvs[1]
+    gwsb = L.rq_escalation_gate_workspace_bytes(16, gv["n"])
+    gws = torch.empty(gwsb, dtype=torch.uint8, device="cuda")
+    gflags = torch.empty(16, dtype=torch.uint8, device="cuda")
+    gstats = torch.empty((16, 2), dtype=torch.float32, device="cuda")
 
     def work():
         L.rq_quantize(a, M, K, L.RQ_MXFP8, None, 0, L.RQ_APPEND_NONE, ac, as_)
@@ -57,8 +64,10 @@ def test_graph_replays_match_eager():
                                       v["wsb"], v["carry"], v["y"])
         L.rq_recurrent_prefill(h, 256, 256, 512, w1, w2, w1q[0], w1q[1], w2q[0], w2q[1], L.RQ_MXFP4, 0b011, 3,
                                1e-6, rws, rws.numel())
+        L.rq_escalation_gate(gv["y"], 16, gv["n"], 1.0, 0.01, gflags, gstats, gws, gwsb)
 
-    outs = [ac, as_, y, h] + [v["y"] for v in gemvs] + [v["carry"] for v in gemvs if v["carry"] is not None]
+    outs = [ac, as_, y, h, gflags, gstats] + [v["y"] for v in gemvs] + [v["carry"] for v in gemvs
+                                                                        if v["carry"] is not None]
 
     def snapshot():
         torch.cuda.synchronize()
@@ -73,7 +82,8 @@ def test_graph_replays_match_eager():
     clear()
     work()
     eager = snapshot()
-    assert any(gv["wsb"] > 0 for gv in gemvs), "the split-K path is part of the capture"
+    assert any(g["wsb"] > 0 for g in gemvs), "the split-K path is part of the capture"
+    assert gwsb > 0, "the split gate is part of the capture"
     work()  # warm the capture path on the side stream torch uses for capture
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
