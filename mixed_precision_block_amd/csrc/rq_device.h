@@ -123,35 +123,4 @@ RQ_HD float mx_mag_value<FmtE2M1>(uint32_t c) { return e2m1_mag_value(c); }
 template <>
 RQ_HD float mx_mag_value<FmtE4M3>(uint32_t c) { return e4m3_mag_value(c); }
 
-// E4M3FN code of a finite float32 v with |v| <= 448, nearest-even, sign
-// kept for negative values that round to zero.  Same integer rounding as
-// mx_encode_mag, on the 24-bit float32 significand.
-RQ_HD uint32_t e4m3_encode_f32(float v) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, v);
-  const uint32_t sign = (u >> 31) << 7;
-  const uint32_t Ex = (u >> 23) & 0xFFu;
-  const uint32_t m = u & 0x7FFFFFu;
-  if (Ex == 0 && m == 0) return sign;
-  const uint32_t M = Ex ? (0x800000u | m) : m;
-  const int s = Ex ? (int)Ex - 150 : -149;     // value = M * 2^s
-  const int L = 32 - __builtin_clz(M);
-  int k = L - 1 + s;
-  if (k < -6) k = -6;
-  const int r = (k - 3) - s;
-  uint32_t n;
-  if (r <= 0) {
-    n = M << (-r);
-  } else if (r >= 25) {
-    n = 0;
-  } else {
-    n = M >> r;
-    const uint32_t rem = M & ((1u << r) - 1u);
-    const uint32_t half = 1u << (r - 1);
-    n += (rem > half || (rem == half && (n & 1u))) ? 1u : 0u;
-  }
-  uint32_t code = ((uint32_t)(k + 6) << 3) + n;
-  if (code > 0x7Eu) code = 0x7Eu;
-  return code | sign;
-}
-
 }  // namespace rq
