@@ -467,8 +467,9 @@ static hipError_t launch_pipe_r(const void* a, const uint8_t* as, const void* w,
   // 256 x 256 tiles (eight waves, two stages) when they fill the 256 CUs at
   // least once.  Otherwise 128 x 128 tiles: three stages when one workgroup
   // per CU covers every tile (MXFP8 on four waves of 64 x 64, MXFP4 and BF16
-  // on eight of 64 x 32: the faster layout of each, measured), else two so
-  // that two workgroups share a CU.
+  // on eight of 64 x 32: the faster layout of each, measured), else 256 x 128
+  // tiles for long K (below), else two stages so that two workgroups share a
+  // CU.
   const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
   if (big >= 256) {
     // 256 x 192 tiles (4 x 2 waves of 64 x 96) when their rounds over the
@@ -484,6 +485,15 @@ static hipError_t launch_pipe_r(const void* a, const uint8_t* as, const void* w,
     if (small <= 256) return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 4, 3>(a, as, w, ws, M, N, K, y, ys, stream);
   }
   if (small <= 256) return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 2, 3>(a, as, w, ws, M, N, K, y, ys, stream);
+  // More 128 x 128 tiles than CUs: 256 x 128 tiles (4 x 2 waves of 64 x 64,
+  // three stages, one workgroup per CU) when they make a single round and K
+  // spans at least 16 stages (the recurrent block's second GEMM, N = 2048,
+  // K = 5632: 12-20% faster than two 128 x 128 workgroups per CU; at 8
+  // stages or fewer they are no faster)
+  const int64_t tall = ((M + 255) / 256) * ((N + 127) / 128);
+  const int64_t stages = FMT == 1 ? K / 256 : FMT == 2 ? K / 128 : K / 64;
+  if (tall <= 256 && stages >= 16)
+    return launch_pipe_t<FMT, EPI, 256, 128, RB, 4, 2, 3>(a, as, w, ws, M, N, K, y, ys, stream);
   return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 2, 2>(a, as, w, ws, M, N, K, y, ys, stream);
 }
 

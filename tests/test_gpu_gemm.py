@@ -110,17 +110,32 @@ def test_large_tiles_ragged_sampled(fmt, ofmt, M, N, K):
     ragged in M and N, K of one stage, an odd number of stages, a long tail
     and K ending in a partial stage (MXFP4 at 384 and 1152, BF16 at 160);
     the oracle runs on sampled rows that include the last one."""
+    sampled_shape_check(fmt, ofmt, M, N, K, "large-tile")
+
+
+def sampled_shape_check(fmt, ofmt, M, N, K, label):
     rng = np.random.default_rng(M + 3 * N + K)
     a = F.f64_to_bf16(rng.standard_t(3, (M, K)))
     w = F.f64_to_bf16(rng.normal(0, 0.02, (N, K)))
     rows = np.union1d(rng.choice(M, 24, replace=False), [0, M - 1])
-    log(f"large-tile gemm fmt={fmt} M={M} N={N} K={K}")
+    log(f"{label} gemm fmt={fmt} M={M} N={N} K={K}")
     if fmt == L.RQ_BF16:
         y = host(api.gemm(fmt, dev_bf16(a), None, dev_bf16(w), None, K, L.RQ_OUT_F32))[rows]
         da, dw = F.bf16_to_f64(a[rows]), F.bf16_to_f64(w)
-        check_f32(y, G.matmul_f64(da, dw), G.abs_bound(da, dw), "large-tile BF16")
+        check_f32(y, G.matmul_f64(da, dw), G.abs_bound(da, dw), f"{label} BF16")
         return
-    sampled_rows_check(fmt, ofmt, a, w, rows, f"large-tile {ofmt} {M}x{N}x{K}")
+    sampled_rows_check(fmt, ofmt, a, w, rows, f"{label} {ofmt} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("fmt,ofmt", MX + [(L.RQ_BF16, None)])
+@pytest.mark.parametrize("M,N,K", [(4000, 2000, 4160), (4096, 2048, 5632), (3000, 1900, 2048)])
+def test_tall_tiles_long_k_sampled(fmt, ofmt, M, N, K):
+    """Shapes with more 128 x 128 tiles than CUs but at most 256 tiles of
+    256 x 128, and K of at least 16 stages (the 256 x 128 path): ragged M
+    and N, K ending in a partial stage (MXFP4 at 4160), the recurrent
+    block's second GEMM; at 3000 x 1900 x 2048 MXFP8 and BF16 take the path
+    and MXFP4 (8 stages) stays on 128 x 128 tiles."""
+    sampled_shape_check(fmt, ofmt, M, N, K, "tall-tile")
 
 
 @pytest.mark.parametrize("M,N,K", [(200, 130, 96), (129, 257, 512), (64, 64, 32)])
