@@ -58,17 +58,98 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict
   }
 }
 
+// Rows of up to 4096 elements: one wave per row, four rows per workgroup,
+// the row held in registers between the two passes and no workgroup
+// barrier.  Lane l plays threads l, l + 64, l + 128 and l + 192 of
+// rmsnorm_kernel: it keeps their partial sums of squares apart, each over
+// the same chunks in the same order, and adds the four wave sums in that
+// kernel's order, so the two give the same bits.
+template <int FMT, int MC>
+__global__ __launch_bounds__(256) void rmsnorm_wave_kernel(const uint16_t* __restrict__ h, int64_t rows, int64_t D,
+                                                           float eps, uint8_t* __restrict__ out,
+                                                           uint8_t* __restrict__ out_scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;  // wave-uniform
+  const uint16_t* hr = h + row * D;
+  const int chunks = (int)(D >> 3);
+  uint4 q[4][MC];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int m = 0; m < MC; ++m) {
+      const int c = 256 * m + 64 * k + lane;
+      q[k][m] = c < chunks ? *reinterpret_cast<const uint4*>(hr + c * 8) : make_uint4(0, 0, 0, 0);
+    }
+  float part[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float ss = 0.0f;
+#pragma unroll
+    for (int m = 0; m < MC; ++m) {
+      if (256 * m + 64 * k + lane >= chunks) continue;
+      const uint32_t w[4] = {q[k][m].x, q[k][m].y, q[k][m].z, q[k][m].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = bf16_to_f32(w[i] & 0xFFFFu), b = bf16_to_f32(w[i] >> 16);
+        ss = fmaf(a, a, ss);
+        ss = fmaf(b, b, ss);
+      }
+    }
+    part[k] = wave_sum(ss);
+  }
+  const float total = ((part[0] + part[1]) + part[2]) + part[3];
+  const float inv = 1.0f / sqrtf(total / (float)D + eps);
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int m = 0; m < MC; ++m) {
+      const int c = 256 * m + 64 * k + lane;
+      if (256 * m + 64 * k >= chunks) continue;  // wave-uniform: no chunk of this round is in the row
+      const uint32_t w[4] = {q[k][m].x, q[k][m].y, q[k][m].z, q[k][m].w};
+      uint32_t pw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        pw[i] = pack_bf16(bf16_to_f32(w[i] & 0xFFFFu) * inv, bf16_to_f32(w[i] >> 16) * inv);
+      const uint4 pk = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+      if constexpr (FMT == 3) {
+        if (c < chunks) *reinterpret_cast<uint4*>(out + (row * D + c * 8) * 2) = pk;
+      } else {
+        // a quad of lanes owns one 32-block; with chunks % 4 == 0 the quad is in or out together
+        using Fm = typename std::conditional<FMT == 1, FmtE2M1, FmtE4M3>::type;
+        const uint32_t mx = quad_max(amax8(pk));
+        const uint32_t sb = (uint32_t)(mx_block_exp<Fm>(mx) + 127);
+        if (c < chunks) {
+          if constexpr (FMT == 1)
+            *reinterpret_cast<uint32_t*>(out + row * (D / 2) + c * 4) = cvt8_e2m1(pk, e8m0_to_f32(sb));
+          else
+            *reinterpret_cast<uint2*>(out + row * D + c * 8) = cvt8_e4m3(pk, e8m0_to_f32(sb));
+          if ((c & 3) == 0) out_scales[row * (D / 32) + (c >> 2)] = (uint8_t)sb;
+        }
+      }
+    }
+}
+
+template <int FMT>
+static hipError_t launch_rmsnorm_f(const uint16_t* h, int64_t rows, int64_t D, float eps, uint8_t* o,
+                                   uint8_t* out_scales, hipStream_t stream) {
+  const unsigned g4 = (unsigned)((rows + 3) / 4);
+  if (D <= 2048)
+    rmsnorm_wave_kernel<FMT, 1><<<g4, 256, 0, stream>>>(h, rows, D, eps, o, out_scales);
+  else if (D <= 4096)
+    rmsnorm_wave_kernel<FMT, 2><<<g4, 256, 0, stream>>>(h, rows, D, eps, o, out_scales);
+  else
+    rmsnorm_kernel<FMT><<<(unsigned)rows, 256, 0, stream>>>(h, D, eps, o, out_scales);
+  return hipGetLastError();
+}
+
 hipError_t launch_rmsnorm(int fmt, const uint16_t* h, int64_t rows, int64_t D, float eps, void* out,
                           uint8_t* out_scales, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   uint8_t* o = static_cast<uint8_t*>(out);
-  if (fmt == 1)
-    rmsnorm_kernel<1><<<(unsigned)rows, 256, 0, stream>>>(h, D, eps, o, out_scales);
-  else if (fmt == 2)
-    rmsnorm_kernel<2><<<(unsigned)rows, 256, 0, stream>>>(h, D, eps, o, out_scales);
-  else
-    rmsnorm_kernel<3><<<(unsigned)rows, 256, 0, stream>>>(h, D, eps, o, out_scales);
-  return hipGetLastError();
+  if (fmt == 1) return launch_rmsnorm_f<1>(h, rows, D, eps, o, out_scales, stream);
+  if (fmt == 2) return launch_rmsnorm_f<2>(h, rows, D, eps, o, out_scales, stream);
+  return launch_rmsnorm_f<3>(h, rows, D, eps, o, out_scales, stream);
 }
 
 // ------------------------------------------------------------------ gate --
