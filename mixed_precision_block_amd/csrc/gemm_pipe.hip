@@ -465,7 +465,8 @@ template <int FMT, int EPI, int RB>
 static hipError_t launch_pipe_r(const void* a, const uint8_t* as, const void* w, const uint8_t* ws, int64_t M,
                                 int64_t N, int64_t K, void* y, uint8_t* ys, hipStream_t stream) {
   // 256 x 256 tiles (eight waves, two stages) when they fill the 256 CUs at
-  // least once.  Otherwise 128 x 128 tiles: three stages when one workgroup
+  // least once.  Small problems: 64 x 64 tiles (below).  Otherwise 128 x 128
+  // tiles: three stages when one workgroup
   // per CU covers every tile (MXFP8 on four waves of 64 x 64, MXFP4 and BF16
   // on eight of 64 x 32: the faster layout of each, measured), else 256 x 128
   // tiles for long K (below), else two stages so that two workgroups share a
@@ -481,6 +482,11 @@ static hipError_t launch_pipe_r(const void* a, const uint8_t* as, const void* w,
     return launch_pipe_t<FMT, EPI, 256, 256, RB, 2, 4, 2>(a, as, w, ws, M, N, K, y, ys, stream);
   }
   const int64_t small = ((M + 127) / 128) * ((N + 127) / 128);
+  // Fewer 128 x 128 tiles than 64 CUs: 64 x 64 tiles (2 x 2 waves of 32 x 32,
+  // three stages) spread the same work over four times the CUs (the
+  // 128 x 1024 x 1024 MXFP4 GEMM 5.5 -> 3.9 us, 512 x 1024 x 4096 MXFP8
+  // 18.9 -> 9.3 us)
+  if (small < 64) return launch_pipe_t<FMT, EPI, 64, 64, RB, 2, 2, 3>(a, as, w, ws, M, N, K, y, ys, stream);
   if constexpr (FMT != 2) {
     if (small <= 256) return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 4, 3>(a, as, w, ws, M, N, K, y, ys, stream);
   }
