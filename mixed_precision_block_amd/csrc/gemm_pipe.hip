@@ -482,11 +482,13 @@ static hipError_t launch_pipe_r(const void* a, const uint8_t* as, const void* w,
     return launch_pipe_t<FMT, EPI, 256, 256, RB, 2, 4, 2>(a, as, w, ws, M, N, K, y, ys, stream);
   }
   const int64_t small = ((M + 127) / 128) * ((N + 127) / 128);
-  // Fewer 128 x 128 tiles than 64 CUs: 64 x 64 tiles (2 x 2 waves of 32 x 32,
-  // three stages) spread the same work over four times the CUs (the
-  // 128 x 1024 x 1024 MXFP4 GEMM 5.5 -> 3.9 us, 512 x 1024 x 4096 MXFP8
-  // 18.9 -> 9.3 us)
-  if (small < 64) return launch_pipe_t<FMT, EPI, 64, 64, RB, 2, 2, 3>(a, as, w, ws, M, N, K, y, ys, stream);
+  // 128 x 128 tiles for at most half the CUs: 64 x 64 tiles (2 x 2 waves of
+  // 32 x 32, three stages) spread the same work over four times the CUs
+  // (128 x 1024 x 1024 MXFP4 5.5 -> 3.9 us, 512 x 1024 x 4096 MXFP8
+  // 18.9 -> 9.3 us, 2048 x 1024 x 1024 BF16 10.1 -> 8.4 us).  With one
+  // 128 x 128 tile per CU they move twice the operand bytes per FLOP and
+  // lose (4096 x 1024 x 2048 MXFP8 14.0 -> 18.7 us).
+  if (small <= 128) return launch_pipe_t<FMT, EPI, 64, 64, RB, 2, 2, 3>(a, as, w, ws, M, N, K, y, ys, stream);
   if constexpr (FMT != 2) {
     if (small <= 256) return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 4, 3>(a, as, w, ws, M, N, K, y, ys, stream);
   }
