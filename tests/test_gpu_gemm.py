@@ -128,6 +128,16 @@ def sampled_shape_check(fmt, ofmt, M, N, K, label):
 
 
 @pytest.mark.parametrize("fmt,ofmt", MX + [(L.RQ_BF16, None)])
+@pytest.mark.parametrize("M,N,K", [(2048, 1024, 1056), (2049, 1000, 1024), (1000, 900, 544)])
+def test_small_tile_boundary_sampled(fmt, ofmt, M, N, K):
+    """Either side of the 64 x 64 rule (128 x 128 tiles for at most half
+    the CUs): 2048 x 1024 makes exactly 128 such tiles (64 x 64 path, K
+    ending in a partial stage), 2049 x 1000 makes 136 (128 x 128, three
+    stages, ragged M and N), 1000 x 900 makes 64 (64 x 64, ragged)."""
+    sampled_shape_check(fmt, ofmt, M, N, K, "tile-boundary")
+
+
+@pytest.mark.parametrize("fmt,ofmt", MX + [(L.RQ_BF16, None)])
 @pytest.mark.parametrize("M,N,K", [(4000, 2000, 4160), (4096, 2048, 5632), (3000, 1900, 2048)])
 def test_tall_tiles_long_k_sampled(fmt, ofmt, M, N, K):
     """Shapes with more 128 x 128 tiles than CUs but at most 256 tiles of
