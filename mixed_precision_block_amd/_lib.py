@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "librq.so")
 
 RQ_OK, RQ_EINVAL, RQ_ESHAPE, RQ_EALIGN, RQ_EHIP, RQ_ENODEV = range(6)
-RQ_MXFP4, RQ_MXFP8, RQ_BF16 = 1, 2, 3
+RQ_MXFP4, RQ_MXFP8, RQ_BF16, RQ_MXFP8_F8MFMA = 1, 2, 3, 4
 RQ_APPEND_NONE, RQ_APPEND_RESIDUAL, RQ_APPEND_COPY = 0, 1, 2
 RQ_OUT_BF16, RQ_OUT_F32 = 0, 1
 RQ_LOW, RQ_ESCALATE, RQ_BOTH = 1, 2, 3
@@ -74,7 +74,7 @@ _SIGNATURES = {
 _lib = None
 
 # The RQ_ABI_VERSION these signatures and RqGemvProblem follow (include/rq.h).
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 def lib():

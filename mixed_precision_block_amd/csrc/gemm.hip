@@ -1,12 +1,17 @@
 // Block-scaled GEMM on gfx950 matrix cores: Y[M x N] = A . W^T, K-major
 // operands, FP32 accumulation.
 //
-// MXFP4 / MXFP8: v_mfma_scale_f32_32x32x64_f8f6f4 consumes 32 K-elements
-// per lane together with that lane's E8M0 block scale, so the block scales
-// of the ARCQuant unified GEMM and of the Day-0 page (section V item 3:
-// scales applied inside the multiply-accumulate) never produce a
-// dequantized intermediate.  BF16: v_mfma_f32_32x32x16_bf16 on the same
-// tiling (the reference-precision steps of RAMP, section 4.2).
+// MXFP4: v_mfma_scale_f32_32x32x64_f8f6f4 consumes 32 K-elements per lane
+// together with that lane's E8M0 block scale, so the block scales of the
+// ARCQuant unified GEMM and of the Day-0 page (section V item 3: scales
+// applied inside the multiply-accumulate) never produce a dequantized
+// intermediate in memory; E2M1 products are exact.  MXFP8: the same
+// instruction on FP8 truncates products inside runs of 8 K terms (about
+// 4e-5 relative on normal data), so each lane dequantizes its E4M3 codes
+// with their block scale to BF16 in registers (exact) and the BF16
+// instruction accumulates in FP32; the FP8 instruction itself is FMT 4.
+// BF16: v_mfma_f32_32x32x16_bf16 on the same tiling (the reference-precision
+// steps of RAMP, section 4.2).
 //
 // Operand layout per MFMA (pinned by the single-tile GPU parity test):
 //   lane l supplies row (l % 32) of a 64-deep MX slice plus the E8M0 byte
@@ -24,6 +29,7 @@
 // buffered through registers: the next slice's global loads are in flight
 // while the current one feeds the MFMAs.  Tails in M, N and K are
 // zero-filled (zero codes with scale byte 127 contribute nothing).
+#include "rq_cvt.h"
 #include "rq_device.h"
 #include "rq_internal.h"
 
@@ -47,6 +53,8 @@ struct GemmTraits<2> {  // MXFP8 (E4M3)
   static constexpr int kCbsz = 0;
   static constexpr bool kScaled = true;
 };
+template <>
+struct GemmTraits<4> : GemmTraits<2> {};  // MXFP8 on the FP8 scaled MFMA
 template <>
 struct GemmTraits<3> {  // BF16
   static constexpr int kStepElems = 64, kRowBytes = 128, kKK = 4, kOpBytes = 16, kKKBytes = 32;
@@ -72,7 +80,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ A
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int m0 = blockIdx.y * kTile, n0 = blockIdx.x * kTile;
-  const int64_t ld = FMT == 1 ? K / 2 : (FMT == 2 ? K : 2 * (int64_t)K);  // row bytes
+  constexpr bool kF8 = FMT == 2 || FMT == 4;
+  const int64_t ld = FMT == 1 ? K / 2 : (kF8 ? K : 2 * (int64_t)K);  // row bytes
   const int ksb = K / 32;
   const int nk = (K + T::kStepElems - 1) / T::kStepElems;
 
@@ -137,13 +146,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ A
       v8i a_op[2], b_op[2];
       v8bf a_bf[2], b_bf[2];
       int sa[2], sb[2];
+      float fa[2][2], fb[2][2];  // exact MXFP8: both block scales of the slice
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int ar = wm * 64 + i * 32 + lrow;
         const int br = wn * 64 + i * 32 + lrow;
         // FP8 lane halves interleave at 16 bytes (see the layout note above)
-        constexpr int kHalfStride = FMT == 2 ? 16 : T::kOpBytes;
-        constexpr int kSecond = FMT == 2 ? 32 : 16;
+        constexpr int kHalfStride = kF8 ? 16 : T::kOpBytes;
+        constexpr int kSecond = kF8 ? 32 : 16;
         const uint8_t* pa = &sA[buf][ar * LDSR + kk * T::kKKBytes + half * kHalfStride];
         const uint8_t* pb = &sW[buf][br * LDSR + kk * T::kKKBytes + half * kHalfStride];
         if constexpr (FMT == 3) {
@@ -161,7 +171,36 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ A
           b_op[i] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
           sa[i] = sS[buf][ar * 4 + kk * 2 + half];
           sb[i] = sS[buf][kTile * 4 + br * 4 + kk * 2 + half];
+          if constexpr (FMT == 2) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+              fa[i][b] = e8m0_to_f32(sS[buf][ar * 4 + kk * 2 + b]);
+              fb[i][b] = e8m0_to_f32(sS[buf][kTile * 4 + br * 4 + kk * 2 + b]);
+            }
+          }
         }
+      }
+      if constexpr (FMT == 2) {
+        // exact MXFP8: BF16 MFMA q takes 8 codes per lane (dwords 2 (q % 2),
+        // +1 of 16-byte chunk q / 2, scaled by block q / 2), dequantized to
+        // BF16; the same K for both operands, so the four cover the slice
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          rq_v8bf da[2], dw[2];
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int lo = q / 2 ? 4 : 0;
+            const int d0 = lo + 2 * (q % 2);
+            da[i] = deq8_e4m3((uint32_t)a_op[i][d0], (uint32_t)a_op[i][d0 + 1], fa[i][q / 2]);
+            dw[i] = deq8_e4m3((uint32_t)b_op[i][d0], (uint32_t)b_op[i][d0 + 1], fb[i][q / 2]);
+          }
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[i], dw[j], acc[i][j], 0, 0, 0);
+        }
+        continue;
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -245,6 +284,7 @@ hipError_t launch_gemm_basic(int fmt, int epi, const void* a, const uint8_t* a_s
   if (M == 0 || N == 0) return hipSuccess;
   if (fmt == 1) return launch_fmt<1>(epi, a, a_scales, w, w_scales, M, N, K, y, stream);
   if (fmt == 2) return launch_fmt<2>(epi, a, a_scales, w, w_scales, M, N, K, y, stream);
+  if (fmt == 4) return launch_fmt<4>(epi, a, a_scales, w, w_scales, M, N, K, y, stream);
   return launch_fmt<3>(epi, a, a_scales, w, w_scales, M, N, K, y, stream);
 }
 

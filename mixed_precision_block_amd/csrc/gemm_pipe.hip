@@ -35,6 +35,12 @@
 // K [16h, 16h+16) and [32+16h, 32+16h+16); BF16 lane half h holds 8
 // elements at 8h of a 16-deep slice.  Slice kk's block scales are bytes
 // 2 kk and 2 kk + 1 of the row's stage scales, lane half h taking 2 kk + h.
+//
+// MXFP8 (FMT 2) reads the FP8 fragments the same way but does not use the
+// FP8 scaled instruction, which truncates products inside runs of 8 K
+// terms: each lane dequantizes its codes with their block scale to BF16
+// (exact) and the slice becomes four BF16 MFMAs with FP32 accumulation.
+// FMT 4 issues the FP8 scaled instruction on the same data.
 #include <type_traits>
 
 #include "rq_block.h"
@@ -61,6 +67,8 @@ struct PipeTraits<2, RB> {  // MXFP8: RB K per stage in 64-deep slices
   static constexpr int kStepElems = RB, kKK = RB / 64, kCbsz = 0, kSBPR = RB / 32;
   static constexpr bool kScaled = true;
 };
+template <int RB>
+struct PipeTraits<4, RB> : PipeTraits<2, RB> {};  // MXFP8 on the FP8 scaled MFMA: same stages
 template <int RB>
 struct PipeTraits<3, RB> {  // BF16: RB / 2 K per stage in 16-deep slices
   static constexpr int kStepElems = RB / 2, kKK = RB / 32, kCbsz = 0, kSBPR = 0;
@@ -139,7 +147,8 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
   const int tm = first_m + (v % (GM * tiles_n)) % gsz, tn = (v % (GM * tiles_n)) / gsz;
   const int m0 = tm * BM, n0 = tn * BN;
 
-  const uint32_t ld = FMT == 1 ? (uint32_t)K / 2 : (FMT == 2 ? (uint32_t)K : 2u * (uint32_t)K);  // row bytes
+  constexpr bool kF8 = FMT == 2 || FMT == 4;  // E4M3 codes, one byte per element
+  const uint32_t ld = FMT == 1 ? (uint32_t)K / 2 : (kF8 ? (uint32_t)K : 2u * (uint32_t)K);  // row bytes
   const uint32_t ksb = (uint32_t)K / 32;
   const int nk = (K + T::kStepElems - 1) / T::kStepElems;  // stages, the last one maybe partial
   const int nfull = K / T::kStepElems;
@@ -216,7 +225,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
   // slices; the lane's byte is extracted per slice.
   auto compute = [&](const uint8_t* st, int nkk) {
     constexpr int KK = T::kKK;
-    constexpr int NQ = FMT == 2 ? 2 : 1;  // 16-byte chunks per lane per fragment
+    constexpr int NQ = kF8 ? 2 : 1;  // 16-byte chunks per lane per fragment
     const uint8_t* sc = st + C::SA + C::SW;
     int za[TM], zb[TN];
     // the row's scale dword holding slices kk of the current pair
@@ -230,7 +239,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
       if (kk >= nkk) break;  // nkk == KK (folded) except in a partial last stage
       v4i fa[TM][NQ], fb[TN][NQ];
       // 16-byte chunk(s) of this slice for the lane's half
-      const int c0 = FMT == 2 ? kk * 4 + half : kk * 2 + half;
+      const int c0 = kF8 ? kk * 4 + half : kk * 2 + half;
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const uint8_t* row = st + (wm * C::WM + i * 32 + lrow) * RB;
@@ -246,6 +255,45 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
       // scale byte 2 kk + half of the row's stage scales: dword kk / 2
       const int sbyte = 2 * kk + half;
       uint32_t esa[TM], esb[TN];
+      if constexpr (FMT == 2) {
+        // exact MXFP8: both block scales of the slice, as floats; each lane
+        // dequantizes its codes to BF16 and the BF16 MFMA accumulates in FP32
+        if (kk % 2 == 0) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+            sa[i] = *reinterpret_cast<const uint32_t*>(sc + (wm * C::WM + i * 32 + lrow) * C::SBPR + 4 * (kk / 2));
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            sb[j] = *reinterpret_cast<const uint32_t*>(sc + (BM + wn * C::WN + j * 32 + lrow) * C::SBPR +
+                                                       4 * (kk / 2));
+        }
+        // MFMA q of the slice takes 8 codes per lane: dwords 2 (q % 2), +1
+        // of chunk q / 2 (lane half h: K 16 h + 8 (q % 2) of block q / 2),
+        // the same K for both operands, so the four MFMAs cover the slice
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int sh = 8 * ((2 * kk + q / 2) & 3);
+          rq_v8bf da[TM], dw[TN];
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+            const v4i c = fa[i][q / 2];
+            const float f = e8m0_to_f32(__builtin_amdgcn_ubfe(sa[i], sh, 8));
+            da[i] = q % 2 ? deq8_e4m3(c.z, c.w, f) : deq8_e4m3(c.x, c.y, f);
+          }
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const v4i c = fb[j][q / 2];
+            const float f = e8m0_to_f32(__builtin_amdgcn_ubfe(sb[j], sh, 8));
+            dw[j] = q % 2 ? deq8_e4m3(c.z, c.w, f) : deq8_e4m3(c.x, c.y, f);
+          }
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dw[j], da[i], acc[i][j], 0, 0, 0);
+        }
+        continue;
+      }
       if constexpr (T::kScaled) {
         if (kk % 2 == 0) {
 #pragma unroll
@@ -447,7 +495,7 @@ static int pipe_row_bytes(int fmt, int64_t K) {
 
 bool gemm_pipe_supported(int fmt, int64_t M, int64_t N, int64_t K) {
   if (K <= 0 || pipe_row_bytes(fmt, K) == 0) return false;
-  const int64_t ld = fmt == 1 ? K / 2 : (fmt == 2 ? K : 2 * K);
+  const int64_t ld = fmt == 1 ? K / 2 : (fmt == 3 ? 2 * K : K);
   return 256 * ld < (int64_t)0x7FFFFFFF && M > 0 && N > 0;
 }
 
@@ -489,7 +537,7 @@ static hipError_t launch_pipe_r(const void* a, const uint8_t* as, const void* w,
   // 128 x 128 tile per CU they move twice the operand bytes per FLOP and
   // lose (4096 x 1024 x 2048 MXFP8 14.0 -> 18.7 us).
   if (small <= 128) return launch_pipe_t<FMT, EPI, 64, 64, RB, 2, 2, 3>(a, as, w, ws, M, N, K, y, ys, stream);
-  if constexpr (FMT != 2) {
+  if constexpr (FMT != 4) {
     if (small <= 256) return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 4, 3>(a, as, w, ws, M, N, K, y, ys, stream);
   }
   if (small <= 256) return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 2, 3>(a, as, w, ws, M, N, K, y, ys, stream);
@@ -499,7 +547,7 @@ static hipError_t launch_pipe_r(const void* a, const uint8_t* as, const void* w,
   // K = 5632: 12-20% faster than two 128 x 128 workgroups per CU; at 8
   // stages or fewer they are no faster)
   const int64_t tall = ((M + 255) / 256) * ((N + 127) / 128);
-  const int64_t stages = FMT == 1 ? K / 256 : FMT == 2 ? K / 128 : K / 64;
+  const int64_t stages = FMT == 1 ? K / 256 : FMT == 3 ? K / 64 : K / 128;
   if (tall <= 256 && stages >= 16)
     return launch_pipe_t<FMT, EPI, 256, 128, RB, 4, 2, 3>(a, as, w, ws, M, N, K, y, ys, stream);
   return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 2, 2>(a, as, w, ws, M, N, K, y, ys, stream);
@@ -526,6 +574,7 @@ hipError_t launch_gemm_pipe(int fmt, int epi, const void* a, const uint8_t* a_sc
                             const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, void* y, hipStream_t stream) {
   if (fmt == 1) return launch_pipe_f<1>(epi, a, a_scales, w, w_scales, M, N, K, y, nullptr, stream);
   if (fmt == 2) return launch_pipe_f<2>(epi, a, a_scales, w, w_scales, M, N, K, y, nullptr, stream);
+  if (fmt == 4) return launch_pipe_f<4>(epi, a, a_scales, w, w_scales, M, N, K, y, nullptr, stream);
   return launch_pipe_f<3>(epi, a, a_scales, w, w_scales, M, N, K, y, nullptr, stream);
 }
 
@@ -536,6 +585,7 @@ hipError_t launch_gemm_silu_quant(int fmt, const void* a, const uint8_t* a_scale
   if (N % 32 != 0 || !gemm_pipe_supported(fmt, M, N, K)) return hipErrorInvalidValue;
   if (fmt == 1) return launch_pipe_e<1, kEpiSiluQuant>(a, a_scales, w, w_scales, M, N, K, codes, scales, stream);
   if (fmt == 2) return launch_pipe_e<2, kEpiSiluQuant>(a, a_scales, w, w_scales, M, N, K, codes, scales, stream);
+  if (fmt == 4) return launch_pipe_e<4, kEpiSiluQuant>(a, a_scales, w, w_scales, M, N, K, codes, scales, stream);
   return hipErrorInvalidValue;
 }
 

@@ -172,7 +172,8 @@ rq_status rq_gemm(int fmt, const void* a, const uint8_t* a_scales, const void* w
                   int64_t M, int64_t N, int64_t K, int out, void* y, void* stream) {
   if (!have(a, M == 0) || !have(w, N == 0) || !have(y, M == 0 || N == 0))
     return fail(RQ_EINVAL, "rq_gemm: null tensor pointer");
-  if (fmt != RQ_MXFP4 && fmt != RQ_MXFP8 && fmt != RQ_BF16) return fail(RQ_EINVAL, "rq_gemm: unknown fmt %d", fmt);
+  if (fmt != RQ_MXFP4 && fmt != RQ_MXFP8 && fmt != RQ_BF16 && fmt != RQ_MXFP8_F8MFMA)
+    return fail(RQ_EINVAL, "rq_gemm: unknown fmt %d", fmt);
   if (fmt == RQ_BF16 && (a_scales || w_scales)) return fail(RQ_EINVAL, "rq_gemm: RQ_BF16 takes no scales");
   if (fmt != RQ_BF16 && (!have(a_scales, M == 0) || !have(w_scales, N == 0)))
     return fail(RQ_EINVAL, "rq_gemm: MX formats need scales");

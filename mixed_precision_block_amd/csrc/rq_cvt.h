@@ -16,6 +16,7 @@ namespace rq {
 
 typedef short rq_v2s __attribute__((ext_vector_type(2)));
 typedef __bf16 rq_v2bf __attribute__((ext_vector_type(2)));
+typedef __bf16 rq_v8bf __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
   return __builtin_bit_cast(float, b ? b << 23 : 0x00400000u);
@@ -38,6 +39,19 @@ __device__ __forceinline__ uint2 cvt8_e4m3(uint4 q, float scale) {
   rq_v2s hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16((rq_v2s){0, 0}, __builtin_bit_cast(rq_v2bf, q.z), scale, false);
   hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, __builtin_bit_cast(rq_v2bf, q.w), scale, true);
   return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
+
+// Eight E4M3FN codes (byte k of the pair = element k) times a float scale
+// to BF16, by v_cvt_scalef32_pk_bf16_fp8.  Every E4M3 value has four
+// significant bits, so the result is the exact product whenever it lies in
+// BF16's normal range (block exponents from -117 up; the quantizer's
+// exponents for BF16 inputs never reach the top of the range).
+__device__ __forceinline__ rq_v8bf deq8_e4m3(uint32_t lo, uint32_t hi, float scale) {
+  const rq_v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, false);
+  const rq_v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, true);
+  const rq_v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, false);
+  const rq_v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, true);
+  return rq_v8bf{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
 }  // namespace rq

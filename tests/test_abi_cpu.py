@@ -32,7 +32,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert rq.rq_abi_version() == L.ABI_VERSION == 3
+    assert rq.rq_abi_version() == L.ABI_VERSION == 4
     lib = L.lib()
     assert lib.rq_status_str(L.RQ_ESHAPE) == b"RQ_ESHAPE"
     assert lib.rq_status_str(99) == b"RQ_UNKNOWN"
@@ -72,6 +72,8 @@ def test_quantize_validation(args, want):
     ((L.RQ_MXFP4, None, A16, A16, A16, 4, 4, 64, 0, A16), L.RQ_EINVAL),
     ((L.RQ_BF16, A16, A16, A16, None, 4, 4, 64, 0, A16), L.RQ_EINVAL),        # BF16 with scales
     ((L.RQ_MXFP8, A16, None, A16, A16, 4, 4, 64, 0, A16), L.RQ_EINVAL),       # MX without scales
+    ((L.RQ_MXFP8_F8MFMA, A16, A16, A16, None, 4, 4, 64, 0, A16), L.RQ_EINVAL),  # FP8 instruction without scales
+    ((5, A16, A16, A16, A16, 4, 4, 64, 0, A16), L.RQ_EINVAL),                # unknown fmt
     ((L.RQ_MXFP4, A16, A16, A16, A16, 4, 4, 64, 5, A16), L.RQ_EINVAL),        # bad out
     ((L.RQ_MXFP4, A16, A16, A16, A16, 4, 4, 0, 0, A16), L.RQ_ESHAPE),
     ((L.RQ_MXFP4, A16, A16, A16, A16, -1, 4, 64, 0, A16), L.RQ_ESHAPE),

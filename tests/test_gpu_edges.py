@@ -128,3 +128,25 @@ def test_grouped_gemv_one_problem_all_flagged():
     y = torch.zeros((B, N), dtype=torch.bfloat16, device="cuda")
     api.gemv_nibble_escalate_grouped(api.gemv_group([(x, planes, y)]), B, fl, L.RQ_BOTH)
     assert np.array_equal(host_bits(y), want)
+
+
+@pytest.mark.parametrize("a_exp,w_exp", [((10, 13), (200, 231)), ((240, 247), (20, 51))])
+def test_mxfp8_exact_at_extreme_block_exponents(a_exp, w_exp):
+    """RQ_MXFP8 dequantizes to BF16 in registers: exact down to block
+    exponent -117 (scale byte 10: every E4M3 value, subnormals included,
+    is then a normal BF16) and up to the largest exponent a BF16 block
+    produces (119, byte 246); tiny activations meet huge weights and the
+    reverse, so the products come back into the FP32 range."""
+    rng = np.random.default_rng(a_exp[0])
+    M, N, K = 64, 64, 256
+    ac = rng.integers(0, 256, (M, K)).astype(np.uint8)
+    ac[(ac & 0x7F) == 0x7F] = 0x7E
+    wc = rng.integers(0, 256, (N, K)).astype(np.uint8)
+    wc[(wc & 0x7F) == 0x7F] = 0x7E
+    as_ = rng.integers(*a_exp, (M, K // 32)).astype(np.uint8)
+    ws = rng.integers(*w_exp, (N, K // 32)).astype(np.uint8)
+    log(f"MXFP8 extreme block exponents a {a_exp} w {w_exp}")
+    y = host(api.gemm(L.RQ_MXFP8, dev(ac), dev(as_), dev(wc), dev(ws), K, L.RQ_OUT_F32))
+    ref = G.gemm_mx(ac, as_, wc, ws, F.FMT_MXFP8)
+    bound = G.abs_bound(Q.dequantize_mx(ac, as_, F.FMT_MXFP8), Q.dequantize_mx(wc, ws, F.FMT_MXFP8))
+    check_f32(y, ref, bound, "extreme exponents")

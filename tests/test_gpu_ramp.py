@@ -67,9 +67,7 @@ def test_small_schedules_against_oracle(ofmt):
         o = R.ramp_prefill(d["h0"], d["w1"], d["w2"], sched, 8, ofmt)
         err_sched = R.hidden_relative_error(o, ref_bf16)
         err_gpu = rel_fro(F.bf16_to_f64(g), F.bf16_to_f64(o))
-        # MXFP8 steps add the FP8 matrix core's truncating accumulation
-        # (about 3e-5 per GEMM), which flips some requantized codes
-        tol = max(1e-3, (0.25 if ofmt == F.FMT_MXFP8 else 0.1) * err_sched)
+        tol = max(1e-3, 0.1 * err_sched)
         log(f"{ofmt} {name}: gpu-vs-oracle {err_gpu:.3e} (tol {tol:.2e}); schedule error vs BF16 {err_sched:.3e}")
         assert err_gpu <= tol
 
