@@ -351,6 +351,26 @@ rq_status rq_escalation_gate(const void *logits_bf16, int64_t B, int64_t V,
                              void *stream);
 
 /*
+ * rq_escalation_gate_noalloc -- rq_escalation_gate with the split-row
+ * kernels, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments and results as rq_escalation_gate given a workspace of
+ * rq_escalation_gate_workspace_bytes(B, V); the per-range statistics go to
+ * a static 16 KiB device scratch instead (each GPU the library runs on
+ * holds one until the process ends; B <= 16 always fits, a larger need
+ * returns RQ_ESHAPE).  It calls no allocating routine: the scratch's
+ * device address is looked up once per device, on its first call there.
+ * Calls on one GPU share that GPU's scratch, so calls that overlap on one
+ * GPU (concurrent streams, threads) race; calls in one stream are ordered.
+ * Nothing in the scratch needs clearing: every call overwrites what it
+ * reads.
+ */
+rq_status rq_escalation_gate_noalloc(const void *logits_bf16, int64_t B,
+                                     int64_t V, float tau, float delta,
+                                     uint8_t *flags, float *stats,
+                                     void *stream);
+
+/*
  * rq_kv_quantize -- FP8 per-token-head-tile quantize-on-write (Day 0 LLM
  * Inference Support, section III.3.3, tile = 128, with the section V
  * listing's scale rule): per (token, head, 128-element tile),

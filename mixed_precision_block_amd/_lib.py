@@ -68,6 +68,7 @@ _SIGNATURES = {
     "rq_gemv_nibble_escalate_grouped": (_INT, [_P, _INT, _I64, _I64, _P, _INT, _P]),
     "rq_escalation_gate_workspace_bytes": (_SZ, [_I64, _I64]),
     "rq_escalation_gate": (_INT, [_P, _I64, _I64, _F, _F, _P, _P, _P, _SZ, _P]),
+    "rq_escalation_gate_noalloc": (_INT, [_P, _I64, _I64, _F, _F, _P, _P, _P]),
     "rq_kv_quantize": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P]),
 }
 
@@ -219,6 +220,12 @@ def rq_escalation_gate(logits, B, V, tau, delta, flags, stats, workspace, ws_byt
     _check("rq_escalation_gate", lib().rq_escalation_gate(_ptr(logits), B, V, tau, delta, _ptr(flags),
                                                           _ptr(stats), _ptr(workspace), ws_bytes,
                                                           _stream(stream)))
+
+
+def rq_escalation_gate_noalloc(logits, B, V, tau, delta, flags, stats, stream=None):
+    _check("rq_escalation_gate_noalloc", lib().rq_escalation_gate_noalloc(_ptr(logits), B, V, tau, delta,
+                                                                          _ptr(flags), _ptr(stats),
+                                                                          _stream(stream)))
 
 
 def rq_kv_quantize(x, T, H, D, codes, scales, stream=None):

@@ -8,6 +8,7 @@
 //  * FP8 per-token-head-tile-128 KV quantize-on-write (Day-0 page, section
 //    III.3.3 with the section V listing's amax/448 scale).
 #include <algorithm>
+#include <mutex>
 
 #include "rq_block.h"
 #include "rq_internal.h"
@@ -275,6 +276,33 @@ static void gate_split(int64_t B, int64_t V, int64_t& G, int64_t& chunk) {
   G = std::min<int64_t>(64, std::max<int64_t>(1, (512 + B - 1) / B));
   chunk = ((V + G - 1) / G + 7) / 8 * 8;
   G = (V + chunk - 1) / chunk;
+}
+
+// Scratch of the allocation-free gate entry point: the per-range partial
+// statistics of gate_part_kernel (at most 16 rows x 64 ranges of float4).
+// Each device holds its own copy; host code uses the per-device address
+// from hipGetSymbolAddress, never the symbol itself.
+constexpr size_t kGateScratchBytes = 16 * 64 * sizeof(float4);
+static __device__ __align__(256) uint8_t scratch[kGateScratchBytes];
+
+hipError_t gate_scratch(void** ptr, size_t* bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  *bytes = kGateScratchBytes;
+  return hipSuccess;
 }
 
 size_t gate_workspace_bytes(int64_t B, int64_t V) {

@@ -421,6 +421,29 @@ rq_status rq_escalation_gate(const void* logits_bf16, int64_t B, int64_t V, floa
                     "rq_escalation_gate launch");
 }
 
+rq_status rq_escalation_gate_noalloc(const void* logits_bf16, int64_t B, int64_t V, float tau, float delta,
+                                     uint8_t* flags, float* stats, void* stream) {
+  if (!logits_bf16 || !flags) return fail(RQ_EINVAL, "rq_escalation_gate_noalloc: null pointer");
+  if (B < 1 || B > 16 || V < 2 || V > kInt32Max)
+    return fail(RQ_ESHAPE, "rq_escalation_gate_noalloc: need B in [1, 16] and V >= 2");
+  if ((reinterpret_cast<uintptr_t>(logits_bf16) & 1u) != 0)
+    return fail(RQ_EALIGN, "rq_escalation_gate_noalloc: logits must be 2-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(stats) & 3u) != 0)
+    return fail(RQ_EALIGN, "rq_escalation_gate_noalloc: stats must be 4-byte aligned");
+  if (rq_status s = need_device(); s != RQ_OK) return s;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (hipError_t e = rq::gate_scratch(&ws, &ws_bytes); e != hipSuccess)
+    return fail(RQ_EHIP, "rq_escalation_gate_noalloc: scratch lookup: %s", hipGetErrorString(e));
+  const size_t need = rq::gate_workspace_bytes(B, V);
+  if (need > ws_bytes)
+    return fail(RQ_ESHAPE, "rq_escalation_gate_noalloc: needs %zu bytes of scratch, the static scratch holds %zu",
+                need, ws_bytes);
+  return hip_status(rq::launch_gate(static_cast<const uint16_t*>(logits_bf16), B, V, tau, delta, flags, stats, ws,
+                                    ws_bytes, as_stream(stream)),
+                    "rq_escalation_gate_noalloc launch");
+}
+
 rq_status rq_kv_quantize(const void* x_bf16, int64_t T, int64_t H, int64_t D, uint8_t* codes, float* scales,
                          void* stream) {
   const bool kv_empty = T == 0 || H == 0;

@@ -88,6 +88,9 @@ hipError_t launch_gemv_escalate(const uint16_t* x, int64_t B, int64_t K, int64_t
 hipError_t launch_gemv_grouped(const ::rq_gemv_problem* probs, int count, int64_t total_tiles, int64_t B,
                                const uint8_t* flags, int phase, hipStream_t stream);
 size_t gate_workspace_bytes(int64_t B, int64_t V);
+// The calling thread's current device's copy of the gate scratch (a static
+// device array, looked up once per device): its address and size.
+hipError_t gate_scratch(void** ptr, size_t* bytes);
 hipError_t launch_gate(const uint16_t* logits, int64_t B, int64_t V, float tau, float delta,
                        uint8_t* flags, float* stats, void* ws, size_t ws_bytes, hipStream_t stream);
 hipError_t launch_kv_quant(const uint16_t* x, int64_t T, int64_t H, int64_t D, uint8_t* codes,
