@@ -84,11 +84,3 @@ def abs_bound(x_bits, wint, scales_f16):
     """sum_k |x_k * w_k| per output, for the per-element tolerance."""
     x = np.abs(F.bf16_to_f64(x_bits))
     return x @ np.abs(_scaled(np.asarray(wint, np.int64), scales_f16)).T
-
-
-def weight_bytes_per_token(N, K, escalated_fraction):
-    """Byte cost model of the article: bytes of weight read per token for
-    a low pass over the hi plane plus, for the escalated share of steps, a
-    second pass over both planes (scales excluded)."""
-    low = N * K / 2
-    return low + escalated_fraction * N * K

@@ -96,3 +96,23 @@ def test_config4_full_size_sampled_rows():
     tol = max(1e-3, 0.1 * R.hidden_relative_error(o, o_bf))
     log(f"config-4 RAMP full size, sampled rows: gpu-vs-oracle {err:.3e} (tol {tol:.2e})")
     assert err <= tol
+
+
+def test_config4_literal_32_step_mxfp8_schedule_sampled_rows():
+    """The pages' fixed-budget schedule (RAMP section 4.2: T = 32 steps, the
+    first K = 24 in low precision, here MXFP8 W/A, the last 8 BF16) on the
+    recurrent block's full shape (4096 tokens, hidden 2048, FFN 5632); the
+    oracle runs the sampled rows, which the token-wise block makes an exact
+    sub-problem."""
+    d = W.c4_ramp()
+    sched = (1 << 24) - 1
+    rows = np.sort(np.random.default_rng(8).choice(4096, 16, replace=False))
+    log("config-4 32-step schedule, steps 1-24 MXFP8")
+    g = gpu_prefill(d["h0"], d["w1"], d["w2"], sched, 32, F.FMT_MXFP8)[rows]
+    o = R.ramp_prefill(d["h0"][rows], d["w1"], d["w2"], sched, 32, F.FMT_MXFP8)
+    o_bf = R.ramp_prefill(d["h0"][rows], d["w1"], d["w2"], 0, 32, F.FMT_MXFP8)
+    err = rel_fro(F.bf16_to_f64(g), F.bf16_to_f64(o))
+    err_sched = R.hidden_relative_error(o, o_bf)
+    tol = max(1e-3, 0.1 * err_sched)
+    log(f"gpu-vs-oracle {err:.3e} (tol {tol:.2e}); schedule error vs BF16 {err_sched:.3e}")
+    assert err <= tol

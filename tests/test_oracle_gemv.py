@@ -48,6 +48,21 @@ def test_worked_gemv():
     assert lo[0, :3].tolist() == [int(v) for v in g["lo_plane_row0"]]
 
 
+def test_abs_bound_hand_values():
+    """sum_k |x_k w_k s| on the worked example, by hand: row 0 of W is
+    [127, -128, -1, 16, 15, -17] at scale 0.5 (low weights 16 hi =
+    [112, -128, -16, 16, 0, -32]); row 1 is all 16 at scale 0.25."""
+    w, s, x = worked()
+    full = V.abs_bound(x, w, s)
+    assert full.tolist() == [[(127 + 128 + 1 + 16 + 15 + 17) * 0.5, 6 * 4.0], [(2 * 127 + 17) * 0.5, 3 * 4.0]]
+    hi, _ = V.split_nibbles(w)
+    low = V.abs_bound(x, 16 * hi.astype(np.int64), s)
+    assert low.tolist() == [[(112 + 128 + 16 + 16 + 0 + 32) * 0.5, 24.0], [(2 * 112 + 32) * 0.5, 12.0]]
+    # a sign flip of x or w leaves it unchanged; it bounds |y| of every sign pattern
+    assert np.array_equal(V.abs_bound(F.f64_to_bf16(-F.bf16_to_f64(x)), -w.astype(np.int64), s), full)
+    assert np.all(np.abs(V.full_pass(x, w, s)) <= full)
+
+
 def test_multiples_of_16_low_equals_full():
     rng = np.random.default_rng(0)
     w = (rng.integers(-8, 8, (40, 64)) * 16).astype(np.int8)
