@@ -674,7 +674,7 @@ def measure_ramp_study(torch, np, api, L, W, to_dev, dev, time_calls):
         h0 = to_dev(d["h0"][:s_tok])
         h = torch.empty_like(h0)
         wsb = L.rq_recurrent_prefill_workspace_bytes(s_tok, D, F, L.RQ_MXFP4)
-        wsp = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+        wsp = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)  # arrival counters start at zero
         t = {}
         for name, sched in (("all_bf16", 0x00), ("ramp", 0x3F)):
             t[name] = time_calls(torch, lambda sched=sched: L.rq_recurrent_prefill(
@@ -714,7 +714,7 @@ def measure_gemv(torch, np, api, L, W, dev, gate=True):
     ys = {N: torch.empty((B, N), dtype=torch.int16, device=dev) for _, _, N in lins}
     # one split-K workspace, large enough for every shape (launches are stream-ordered)
     wsb = max(L.rq_gemv_workspace_bytes(B, N, K) for _, K, N in lins)
-    wsp = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    wsp = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)  # arrival counters start at zero
 
     def low_bytes(N, K):
         return N * K // 2 + N * K // 32 * 2 + B * K * 2 + B * N * 2
@@ -842,6 +842,7 @@ def measure_gemv(torch, np, api, L, W, dev, gate=True):
         "us": round(ms_esc_lo * 1e3, 1), "gb_s": round(tot_esc_lo / (ms_esc_lo * 1e-3) / 1e9, 1),
         "frac_hbm": round(tot_esc_lo / (ms_esc_lo * 1e-3) / PEAK["hbm"], 4), "bytes": tot_esc_lo}
     del table, gys, carries
+    out.update(measure_decode_layer_ordered(torch, api, L, W, dev, gen, xs, flags, planes[-1], low_bytes, esc_bytes))
     out["gemv_full_sweep_197_linears_low_pass_b16"] = {
         "us": round(ms_low * 1e3, 1), "gb_s": round(tot_low / (ms_low * 1e-3) / 1e9, 1),
         "frac_hbm": round(tot_low / (ms_low * 1e-3) / PEAK["hbm"], 4), "bytes": tot_low,
@@ -850,6 +851,56 @@ def measure_gemv(torch, np, api, L, W, dev, gate=True):
         "us": round(ms_esc * 1e3, 1), "gb_s": round(tot_esc / (ms_esc * 1e-3) / 1e9, 1),
         "frac_hbm": round(tot_esc / (ms_esc * 1e-3) / PEAK["hbm"], 4), "bytes": tot_esc}
     log(f"rows: GEMV {out}")
+    return out
+
+
+def measure_decode_layer_ordered(torch, api, L, W, dev, gen, xs, flags, lm, low_bytes, esc_bytes):
+    """The decode step in layer order, as a model runs it: per layer q/k/v
+    (one GEMV on the stacked weights, as they share their input), o,
+    gate/up (stacked), down, then the LM head -- 28 x 4 + 1 = 113 launches
+    on one stream, each waiting for the one before (no batching across
+    layers).  Small-N shapes split K inside their launch.  The low pass over
+    all 16 tokens, and the escalation of the 2 flagged tokens with both
+    planes (their hidden states differ from the low pass's, so no carry);
+    eager, and captured once in a HIP graph and replayed."""
+    out = {}
+    B = 16
+    shapes = [("qkv", 1024, 2048 + 1024 + 1024), ("o", 2048, 1024), ("gate_up", 1024, 2 * 3072),
+              ("down", 3072, 1024)]
+    layer = []
+    for _ in range(len(W.c5_linear_list()) // 7):
+        for name, K, N in shapes:
+            q, sc = gpu_int8_weights(torch, gen, N, K, dev)
+            layer.append((N, K, api.pack_nibble_planes(q, sc)))
+            del q, sc
+    seq = layer + [lm]
+    ys = {N: torch.empty((B, N), dtype=torch.int16, device=dev) for N, _, _ in seq}
+    wsb = max(L.rq_gemv_workspace_bytes(B, N, K) for N, K, _ in seq)
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)  # arrival counters start at zero
+
+    def step(phase):
+        for N, K, (hi, lo, st) in seq:
+            L.rq_gemv_nibble_escalate(xs[K], B, K, N, hi, lo, st, flags, phase, ws, wsb, None, ys[N])
+
+    nf = int(flags.sum().item())
+    tot = {L.RQ_LOW: sum(low_bytes(N, K) for N, K, _ in seq), L.RQ_ESCALATE: sum(esc_bytes(N, K, nf) for N, K, _ in seq)}
+    tag = {L.RQ_LOW: "low_pass_b16", L.RQ_ESCALATE: "escalation_2_of_16"}
+    for phase in (L.RQ_LOW, L.RQ_ESCALATE):
+        ms = time_calls(torch, lambda: step(phase), 10)
+        step(phase)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(phase)
+        ms_g = time_calls(torch, g.replay, 10)
+        del g
+        for form, t in (("eager", ms), ("hip_graph", ms_g)):
+            out[f"gemv_decode_step_layer_ordered_{tag[phase]}_{form}"] = {
+                "us": round(t * 1e3, 1), "gb_s": round(tot[phase] / (t * 1e-3) / 1e9, 1),
+                "frac_hbm": round(tot[phase] / (t * 1e-3) / PEAK["hbm"], 4), "bytes": tot[phase],
+                "launches": len(seq), "split_k_launches": sum(L.rq_gemv_workspace_bytes(B, N, K) > 0 for N, K, _ in seq)}
+    del layer, seq, ys, ws
+    log(f"rows: layer-ordered decode step {out}")
     return out
 
 

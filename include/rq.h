@@ -266,10 +266,18 @@ rq_status rq_pack_nibble_planes(const int8_t *w, const uint16_t *scales_f16,
  * (device; may be NULL for RQ_LOW); y_bf16 [B x N] BF16.  FP32
  * accumulation, BF16 output.
  * workspace: device scratch of ws_bytes >= rq_gemv_workspace_bytes(B, N,
- * K) bytes (caller-owned, contents irrelevant) lets shapes with few 64-row
- * tiles split K over more workgroups; NULL / smaller runs them unsplit.
- * The result is the same bits either way only up to FP32 summation
- * order; a given (shape, workspace) choice is deterministic.
+ * K) bytes (caller-owned, 16-byte aligned) lets shapes with few 64-row
+ * tiles split K over more workgroups within the one launch: each writes
+ * FP32 partial sums and bumps a per-tile arrival counter kept in the
+ * workspace's first 1 KiB, and the last to arrive adds the partials in a
+ * fixed order and resets the counter.  Those 1 KiB must be ZERO before
+ * the first call (zero the workspace once after allocating it); every call
+ * leaves them zero again, so the workspace can be reused by later calls of
+ * any shape and by graph replays.  Calls sharing a workspace must not
+ * overlap.
+ * NULL / smaller runs the shape unsplit.  The result is the same bits
+ * either way only up to FP32 summation order; a given (shape, workspace)
+ * choice is deterministic.
  * y_f32: optional FP32 carry [B x N] (caller-owned, 4-byte aligned, NULL
  * for none).  RQ_LOW with it also stores every row's unrounded FP32 sum.
  * RQ_ESCALATE with it takes those sums as the hi part -- they must come

@@ -126,7 +126,8 @@ def gemv_nibble_escalate(x, N, planes, flags=None, phase=L.RQ_BOTH, y=None, stre
     if y is None:
         y = torch.empty((B, N), dtype=torch.bfloat16, device=x.device)
     wsb = L.rq_gemv_workspace_bytes(B, N, K) if split else 0
-    ws = _u8((wsb,), x.device) if wsb else None
+    # the workspace's arrival counters must start at zero (each call leaves them zero)
+    ws = torch.zeros((wsb,), dtype=torch.uint8, device=x.device) if wsb else None
     L.rq_gemv_nibble_escalate(x, B, K, N, hi, lo, st, flags, phase, ws, wsb, carry, y, stream)
     return y
 

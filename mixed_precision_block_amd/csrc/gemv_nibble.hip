@@ -21,7 +21,11 @@
 // where they fit, else come through the scalar cache, the address being
 // wave-uniform).  FP32 block partials are scaled by
 // the block's FP16 scale and accumulated; the four waves' sums are added in
-// a fixed order through LDS.
+// a fixed order through LDS.  Shapes with few row tiles split K over
+// workgroups (grid y); each writes its FP32 partial sums to the caller's
+// workspace and bumps its tile's arrival counter, and the last workgroup
+// of a tile to arrive adds the partials in slice order, writes the output
+// and resets the counter -- one launch, deterministic, no reduce kernel.
 //
 // Carry: the low pass can also keep its FP32 sums in a caller buffer.  As
 // w = 16 hi + lo, an escalation that starts from those sums needs only the
@@ -35,6 +39,19 @@ namespace rq {
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
+
+// Loads through the global address space: global loads count only against
+// the vector-memory counter, while a generic (flat) load also counts
+// against the LDS counter, so every LDS wait would also wait for the
+// weight prefetch in flight.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 gload16(const uint4* p, size_t i) {
+  const u32x4 v = ((const __attribute__((address_space(1))) u32x4*)(const void*)p)[i];
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint16_t gload2(const uint16_t* p, size_t i) {
+  return ((const __attribute__((address_space(1))) uint16_t*)(const void*)p)[i];
+}
 __device__ __forceinline__ float f16_to_f32(uint16_t s) { return (float)__builtin_bit_cast(_Float16, s); }
 
 // float of the signed byte N of e: one sub-dword (SDWA) conversion with
@@ -105,15 +122,17 @@ enum Planes { kHi = 0, kHiLo = 1, kLo = 2 };
 // t < nt.  The four waves' sums meet in LDS in a fixed order; with one
 // slice the workgroup writes BF16 outputs (kHi: also the FP32 carry yf
 // when given; kLo: adds the carry first), otherwise FP32 partials to
-// ws[slice][token][row] (16 token rows per slice) that gemv_reduce_kernel
-// adds in slice order.
+// ws[tile][slice][token][row] (16 token rows per slice) that the tile's
+// last workgroup adds in slice order (split_finish).
 constexpr int kWsTokens = 16;
+constexpr int kMaxSlices = 16;  // K slices of a split launch, at most
+constexpr int kLowRows = 1;     // 64-row tiles per low-pass workgroup
 
 template <int TB, int kP>
 __device__ __forceinline__ void gemv_tile(const uint16_t* __restrict__ x, int B, int K, int N,
                                           const uint8_t* __restrict__ hi, const uint8_t* __restrict__ lo,
                                           const uint16_t* __restrict__ sc, const int* tok, int nt,
-                                          uint16_t* __restrict__ y, float* __restrict__ yf, float* __restrict__ ws,
+                                          uint16_t* __restrict__ y, float* __restrict__ yf, float* ws,
                                           float (*red)[TB][64], uint4* xs, int tile, int slice, int nslice) {
   constexpr bool kFull = kP != kHi;  // an escalation pass: flagged tokens only
   const int lane = threadIdx.x & 63;
@@ -137,35 +156,30 @@ __device__ __forceinline__ void gemv_tile(const uint16_t* __restrict__ x, int B,
 
   int b = b0 + wave;
   uint4 xv = make_uint4(0, 0, 0, 0);
-  if (!kFull && b < b1) xv = xg[(size_t)b * 4];
-  // escalation (memory-bound): the next block's planes load one block ahead
+  if (!kFull && b < b1) xv = gload16(xg, (size_t)b * 4);
+  // the next block's planes and scale load one block ahead
   uint4 nh = make_uint4(0, 0, 0, 0), nl = make_uint4(0, 0, 0, 0);
   uint16_t ns = 0;
-  if (kFull && b < b1) {
-    if constexpr (kP != kLo) nh = hp[(size_t)b * 64];
-    nl = lp[(size_t)b * 64];
-    ns = sp[(size_t)b * 64];
+  if (b < b1) {
+    if constexpr (kP != kLo) nh = gload16(hp, (size_t)b * 64);
+    if constexpr (kP != kHi) nl = gload16(lp, (size_t)b * 64);
+    ns = gload2(sp, (size_t)b * 64);
   }
   for (; b < b1; b += 4) {
-    uint4 dh, dl = make_uint4(0, 0, 0, 0);
-    float s;
-    if constexpr (kFull) {
-      dh = nh, dl = nl;
-      s = f16_to_f32(ns);
+    const uint4 dh = nh, dl = nl;
+    const float s = f16_to_f32(ns);
+    {
       const int bn = b + 4 < b1 ? b + 4 : b;  // the last block reloads itself
-      if constexpr (kP != kLo) nh = hp[(size_t)bn * 64];
-      nl = lp[(size_t)bn * 64];
-      ns = sp[(size_t)bn * 64];
-    } else {
-      dh = hp[(size_t)b * 64];
-      s = f16_to_f32(sp[(size_t)b * 64]);
+      if constexpr (kP != kLo) nh = gload16(hp, (size_t)bn * 64);
+      if constexpr (kP != kHi) nl = gload16(lp, (size_t)bn * 64);
+      ns = gload2(sp, (size_t)bn * 64);
     }
     if constexpr (!kFull) {
       // a wave's LDS accesses complete in order: this write follows the
       // reads of the previous block and precedes the reads below
       xslot[lane] = xv;
       const int bn = b + 4 < b1 ? b + 4 : b;  // next block's x (the last reloads itself)
-      xv = xg[(size_t)bn * 4];
+      xv = gload16(xg, (size_t)bn * 4);
     }
     bf16x2 wp[16];
     if constexpr (kP == kHiLo)
@@ -222,7 +236,177 @@ __device__ __forceinline__ void gemv_tile(const uint16_t* __restrict__ x, int B,
         y[o] = (uint16_t)f32_to_bf16(v);
       }
     } else {
-      ws[((size_t)slice * kWsTokens + tok[t]) * ((size_t)((N + 63) / 64) * 64) + n] = v;
+      // coherent at device scope (visible to workgroups on other XCDs)
+      __hip_atomic_store(ws + (((size_t)tile * nslice + slice) * kWsTokens + tok[t]) * 64 + l, v, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Split K: after a workgroup has stored its partial sums of tile `tile`
+// (for the tokens in tmask), it bumps the tile's arrival counter; the last
+// of the nslice workgroups to arrive adds the partials in slice order
+// (kLo: onto the carry yf; kHi with yf: also storing the FP32 sums), writes
+// the BF16 outputs and resets the counter to zero for the next call.
+// Partials and counter are device-scope atomic accesses, coherent across
+// the XCDs' separate L2s without cache-wide write-back or invalidation:
+// each workgroup waits until its partial stores are complete before the
+// counter is bumped, so the last arriver's device-scope loads see every
+// slice.  Every thread of the workgroup calls it; nothing waits on another
+// workgroup.
+template <int kP, int R = 1>
+__device__ __forceinline__ void split_finish(const float* __restrict__ ws, uint32_t* __restrict__ counters, int tile,
+                                             int nslice, int N, uint32_t tmask, uint16_t* __restrict__ y,
+                                             float* __restrict__ yf) {
+  __shared__ uint32_t last;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's partial stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = old == (uint32_t)nslice - 1u ? 1u : 0u;
+  }
+  __syncthreads();
+  if (!last) return;
+  const int ntiles = (N + 63) >> 6;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int t64 = tile * R + r;  // 64-row tile of the partials
+    if (t64 >= ntiles) break;
+    // every partial this thread adds is loaded first (the loads overlap; a
+    // slot past the tile's slices reloads the last slice, always in
+    // bounds), then each output sums its slices in order
+    constexpr int kPer = kWsTokens * 64 / 256;  // outputs per thread
+    float part[kPer][kMaxSlices];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int o = threadIdx.x + 256 * j, t = o >> 6, l = o & 63;
+#pragma unroll
+      for (int sl = 0; sl < kMaxSlices; ++sl) {
+        const int sc = sl < nslice ? sl : nslice - 1;
+        part[j][sl] = __hip_atomic_load(ws + (((size_t)t64 * nslice + sc) * kWsTokens + t) * 64 + l,
+                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int o = threadIdx.x + 256 * j, t = o >> 6, l = o & 63;
+      const int n = t64 * 64 + l;
+      if (!((tmask >> t) & 1u) || n >= N) continue;
+      const size_t i = (size_t)t * N + n;
+      float v = kP == kLo ? yf[i] : 0.0f;
+#pragma unroll
+      for (int sl = 0; sl < kMaxSlices; ++sl)
+        if (sl < nslice) v += part[j][sl];
+      if (kP == kHi && yf != nullptr) yf[i] = v;
+      y[i] = (uint16_t)f32_to_bf16(v);
+    }
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Low pass over R 64-row tiles (tile R t .. R t + R - 1) at once: lane l
+// owns row l of each, so every broadcast read of x feeds R rows' dot
+// products (LDS traffic per multiply-add falls by R).  Same arithmetic and
+// order per output as gemv_tile's low pass.  Split K: partials per 64-row
+// tile, finished by split_finish<kHi, R>.
+template <int TB, int R>
+__device__ __forceinline__ void low_tile(const uint16_t* __restrict__ x, int B, int K, int N,
+                                         const uint8_t* __restrict__ hi, const uint16_t* __restrict__ sc, int nt,
+                                         uint16_t* __restrict__ y, float* __restrict__ yf, float* ws,
+                                         float (*red)[TB][64], uint4* xs, int tile, int slice, int nslice) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nb = K >> 5;
+  const int per = (nb + nslice - 1) / nslice;
+  const int b0 = slice * per, b1 = min(nb, b0 + per);
+  const int ntiles = (N + 63) >> 6;
+  const uint4* hp[R];
+  const uint16_t* sp[R];
+  bool live[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int t64 = tile * R + r;
+    live[r] = t64 < ntiles;  // workgroup-uniform
+    const size_t base = (size_t)(live[r] ? t64 : 0) * nb * 64 + lane;
+    hp[r] = reinterpret_cast<const uint4*>(hi) + base;
+    sp[r] = sc + base;
+  }
+  const int xt_l = (lane >> 2) < B ? (lane >> 2) : B - 1;
+  const uint4* xg = reinterpret_cast<const uint4*>(x + (size_t)xt_l * K) + (lane & 3);
+  uint4* const xslot = xs + wave * 64;
+  float acc[R][TB];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int t = 0; t < TB; ++t) acc[r][t] = 0.0f;
+  int b = b0 + wave;
+  uint4 xv = make_uint4(0, 0, 0, 0);
+  uint4 nh[R];
+  uint16_t ns[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) nh[r] = make_uint4(0, 0, 0, 0), ns[r] = 0;
+  if (b < b1) {
+    xv = gload16(xg, (size_t)b * 4);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (live[r]) nh[r] = gload16(hp[r], (size_t)b * 64), ns[r] = gload2(sp[r], (size_t)b * 64);
+  }
+  for (; b < b1; b += 4) {
+    uint4 dh[R];
+    float s[R];
+    const int bn = b + 4 < b1 ? b + 4 : b;  // the last block reloads itself
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      dh[r] = nh[r], s[r] = f16_to_f32(ns[r]);
+      if (live[r]) nh[r] = gload16(hp[r], (size_t)bn * 64), ns[r] = gload2(sp[r], (size_t)bn * 64);
+    }
+    // a wave's LDS accesses complete in order: this write follows the
+    // reads of the previous block and precedes the reads below
+    xslot[lane] = xv;
+    xv = gload16(xg, (size_t)bn * 4);
+    bf16x2 wp[R][16];
+#pragma unroll
+    for (int r = 0; r < R; ++r) unpack_hi16(dh[r], wp[r]);
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      uint32_t xq[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 v = xslot[4 * t + i];
+        xq[4 * i] = v.x, xq[4 * i + 1] = v.y, xq[4 * i + 2] = v.z, xq[4 * i + 3] = v.w;
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float blk = 0.0f;
+#pragma unroll
+        for (int p = 0; p < 16; ++p) blk = __builtin_amdgcn_fdot2_f32_bf16(wp[r][p], as_bf16x2(xq[p]), blk, false);
+        acc[r][t] = fmaf(blk, s[r], acc[r][t]);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r > 0) __syncthreads();  // the previous sub-tile's reads of red are done
+#pragma unroll
+    for (int t = 0; t < TB; ++t) red[wave][t][lane] = acc[r][t];
+    __syncthreads();
+    if (!live[r]) continue;
+    const int t64 = tile * R + r;
+    for (int o = threadIdx.x; o < TB * 64; o += 256) {
+      const int t = o >> 6, l = o & 63;
+      const int n = t64 * 64 + l;
+      if (t >= nt) continue;
+      const float v = ((red[0][t][l] + red[1][t][l]) + red[2][t][l]) + red[3][t][l];
+      if (nslice == 1) {
+        if (n < N) {
+          const size_t i = (size_t)t * N + n;
+          if (yf != nullptr) yf[i] = v;
+          y[i] = (uint16_t)f32_to_bf16(v);
+        }
+      } else {
+        __hip_atomic_store(ws + (((size_t)t64 * nslice + slice) * kWsTokens + t) * 64 + l, v, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
 }
@@ -231,14 +415,12 @@ template <int TB>
 __global__ __launch_bounds__(256) void gemv_low_kernel(const uint16_t* __restrict__ x, int B, int K, int N,
                                                        const uint8_t* __restrict__ hi,
                                                        const uint16_t* __restrict__ sc, uint16_t* __restrict__ y,
-                                                       float* __restrict__ yf, float* __restrict__ ws) {
+                                                       float* __restrict__ yf, float* __restrict__ ws,
+                                                       uint32_t* __restrict__ counters) {
   __shared__ float red[4][TB][64];
   __shared__ uint4 xs[4 * 64];
-  int tok[TB];
-#pragma unroll
-  for (int t = 0; t < TB; ++t) tok[t] = t;
-  gemv_tile<TB, kHi>(x, B, K, N, hi, nullptr, sc, tok, B < TB ? B : TB, y, yf, ws, red, xs, blockIdx.x, blockIdx.y,
-                     gridDim.y);
+  low_tile<TB, kLowRows>(x, B, K, N, hi, sc, B < TB ? B : TB, y, yf, ws, red, xs, blockIdx.x, blockIdx.y, gridDim.y);
+  if (gridDim.y > 1) split_finish<kHi, kLowRows>(ws, counters, blockIdx.x, gridDim.y, N, (1u << B) - 1u, y, yf);
 }
 
 // Escalation: a workgroup takes the flagged tokens in groups of four (in
@@ -276,7 +458,7 @@ __device__ __forceinline__ void stage_x(uint4* xst, const uint16_t* __restrict__
   const int kc = (b1 - b0) * 4;
   for (int i = threadIdx.x; i < nt * kc; i += 256) {
     const int t = i / kc, c = i - t * kc;
-    xst[t * kc + c] = reinterpret_cast<const uint4*>(x + (size_t)tok[t] * K + (size_t)b0 * 32)[c];
+    xst[t * kc + c] = gload16(reinterpret_cast<const uint4*>(x + (size_t)tok[t] * K + (size_t)b0 * 32), c);
   }
   __syncthreads();
 }
@@ -313,8 +495,8 @@ __device__ __forceinline__ void escalate_wave_tile(const uint16_t* __restrict__ 
   for (int f = 0; f < PF; ++f) {
     const int bb = f < nb ? f : nb - 1;
     ph[f] = make_uint4(0, 0, 0, 0);
-    if constexpr (kP != kLo) ph[f] = hp[(size_t)bb * 64];  // kLo: w_hi may be NULL
-    pl[f] = lp[(size_t)bb * 64], ps[f] = sp[(size_t)bb * 64];
+    if constexpr (kP != kLo) ph[f] = gload16(hp, (size_t)bb * 64);  // kLo: w_hi may be NULL
+    pl[f] = gload16(lp, (size_t)bb * 64), ps[f] = gload2(sp, (size_t)bb * 64);
   }
   // four blocks per turn so that the partial index is static
   for (int b4 = 0; b4 < nb; b4 += 4) {
@@ -327,8 +509,8 @@ __device__ __forceinline__ void escalate_wave_tile(const uint16_t* __restrict__ 
 #pragma unroll
       for (int f = 0; f + 1 < PF; ++f) ph[f] = ph[f + 1], pl[f] = pl[f + 1], ps[f] = ps[f + 1];
       const int bn = b + PF < nb ? b + PF : b;  // the last blocks reload themselves
-      if constexpr (kP != kLo) ph[PF - 1] = hp[(size_t)bn * 64];
-      pl[PF - 1] = lp[(size_t)bn * 64], ps[PF - 1] = sp[(size_t)bn * 64];
+      if constexpr (kP != kLo) ph[PF - 1] = gload16(hp, (size_t)bn * 64);
+      pl[PF - 1] = gload16(lp, (size_t)bn * 64), ps[PF - 1] = gload2(sp, (size_t)bn * 64);
       bf16x2 wp[16];
       if constexpr (kP == kLo)
         unpack_lo16(dl, wp);
@@ -381,10 +563,13 @@ __global__ __launch_bounds__(256) void gemv_escalate_kernel(const uint16_t* __re
                                                             const uint16_t* __restrict__ sc,
                                                             const uint8_t* __restrict__ flags,
                                                             uint16_t* __restrict__ y, float* __restrict__ yf,
-                                                            float* __restrict__ ws, int staged) {
+                                                            float* __restrict__ ws, uint32_t* __restrict__ counters,
+                                                            int staged) {
   extern __shared__ uint4 xst[];  // the flagged tokens' x of this slice, when staged
   __shared__ float red[4][kEscTokens][64];
   uint32_t fmask = flag_mask(flags, B);
+  const uint32_t all = fmask;
+  if (all == 0) return;  // nothing flagged: no weight traffic, no arrival (the counters stay zero)
   int tok[kEscTokens];
   for (int nt; (nt = next_group(fmask, tok)) > 0;) {  // nothing (more) flagged: no weight traffic
     uint4* xs = nullptr;
@@ -400,23 +585,7 @@ __global__ __launch_bounds__(256) void gemv_escalate_kernel(const uint16_t* __re
                               gridDim.y);
     __syncthreads();  // the next group reuses red and xst
   }
-}
-
-// y[t][n] = BF16(sum over slices of ws[slice][t][n]) in slice order, for
-// every token (flags == nullptr) or the flagged ones.  carry_in (a lo-only
-// escalation) is added first; carry_out (a low pass) keeps the FP32 sum.
-__global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restrict__ ws, int nslice, int B, int N,
-                                                          int Np, const uint8_t* __restrict__ flags,
-                                                          const float* __restrict__ carry_in,
-                                                          float* __restrict__ carry_out, uint16_t* __restrict__ y) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)B * N) return;
-  const int t = (int)(i / N), n = (int)(i - (int64_t)t * N);
-  if (flags && !flags[t]) return;
-  float v = carry_in ? carry_in[i] : 0.0f;
-  for (int sl = 0; sl < nslice; ++sl) v += ws[((size_t)sl * kWsTokens + t) * Np + n];
-  if (carry_out) carry_out[i] = v;
-  y[i] = (uint16_t)f32_to_bf16(v);
+  if (gridDim.y > 1) split_finish<kP>(ws, counters, blockIdx.x, gridDim.y, N, all, y, yf);
 }
 
 // Grouped launch: workgroup g of the grid takes 64-row tile
@@ -528,32 +697,32 @@ static int gemv_tb(int64_t B) { return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B 
 
 // K slices per row tile: one when the row tiles alone give 256 workgroups,
 // else enough for about 512 workgroups, each keeping at least one block
-// per wave.
+// per wave, and at most kMaxSlices (the partials the last arriver of a
+// tile loads at once).
 int gemv_slices(int64_t N, int64_t K) {
   const int64_t tiles = (N + 63) / 64, nb = K / 32;
   if (tiles == 0 || tiles >= 256) return 1;
   int64_t s = (512 + tiles - 1) / tiles;
-  const int64_t cap = nb / 4 > 1 ? nb / 4 : 1;
+  int64_t cap = nb / 4 > 1 ? nb / 4 : 1;
+  if (cap > kMaxSlices) cap = kMaxSlices;
   return (int)(s < cap ? s : cap);
 }
+
+// Workspace of a split launch: 1 KiB of per-tile arrival counters (a split
+// shape has fewer than 256 row tiles; zero between calls, at the same place
+// for every shape, so shapes can share a workspace), then the FP32
+// partials [tile][slice][16 tokens][64 rows].
+constexpr size_t kCounterBytes = 256 * sizeof(uint32_t);
 
 size_t gemv_workspace_bytes(int64_t B, int64_t N, int64_t K) {
   (void)B;
   const int s = gemv_slices(N, K);
-  return s > 1 ? (size_t)s * kWsTokens * ((N + 63) / 64 * 64) * sizeof(float) : 0;
+  return s > 1 ? kCounterBytes + (size_t)s * kWsTokens * ((N + 63) / 64 * 64) * sizeof(float) : 0;
 }
 
 static int slices_for(int64_t B, int64_t N, int64_t K, size_t ws_bytes) {
   const int s = gemv_slices(N, K);
   return (s > 1 && ws_bytes >= gemv_workspace_bytes(B, N, K)) ? s : 1;
-}
-
-static hipError_t launch_reduce(const float* ws, int nslice, int64_t B, int64_t N, const uint8_t* flags,
-                                const float* carry_in, float* carry_out, uint16_t* y, hipStream_t stream) {
-  const int64_t total = B * N;
-  gemv_reduce_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(
-      ws, nslice, (int)B, (int)N, (int)((N + 63) / 64 * 64), flags, carry_in, carry_out, y);
-  return hipGetLastError();
 }
 
 hipError_t launch_gemv_low(const uint16_t* x, int64_t B, int64_t K, int64_t N, const uint8_t* hi,
@@ -562,19 +731,18 @@ hipError_t launch_gemv_low(const uint16_t* x, int64_t B, int64_t K, int64_t N, c
   const unsigned tiles = (unsigned)((N + 63) / 64);
   if (tiles == 0) return hipSuccess;
   const int ns = slices_for(B, N, K, ws_bytes);
-  const dim3 grid(tiles, ns);
+  const dim3 grid((tiles + kLowRows - 1) / kLowRows, ns);  // kLowRows 64-row tiles per workgroup
   const int b = (int)B, k = (int)K, n = (int)N;
-  float* w = static_cast<float*>(ws);
+  uint32_t* cnt = static_cast<uint32_t*>(ws);
+  float* w = ns > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kCounterBytes) : nullptr;
   switch (gemv_tb(B)) {
-    case 1: gemv_low_kernel<1><<<grid, 256, 0, stream>>>(x, b, k, n, hi, scales, y, yf, w); break;
-    case 2: gemv_low_kernel<2><<<grid, 256, 0, stream>>>(x, b, k, n, hi, scales, y, yf, w); break;
-    case 4: gemv_low_kernel<4><<<grid, 256, 0, stream>>>(x, b, k, n, hi, scales, y, yf, w); break;
-    case 8: gemv_low_kernel<8><<<grid, 256, 0, stream>>>(x, b, k, n, hi, scales, y, yf, w); break;
-    default: gemv_low_kernel<16><<<grid, 256, 0, stream>>>(x, b, k, n, hi, scales, y, yf, w); break;
+    case 1: gemv_low_kernel<1><<<grid, 256, 0, stream>>>(x, b, k, n, hi, scales, y, yf, w, cnt); break;
+    case 2: gemv_low_kernel<2><<<grid, 256, 0, stream>>>(x, b, k, n, hi, scales, y, yf, w, cnt); break;
+    case 4: gemv_low_kernel<4><<<grid, 256, 0, stream>>>(x, b, k, n, hi, scales, y, yf, w, cnt); break;
+    case 8: gemv_low_kernel<8><<<grid, 256, 0, stream>>>(x, b, k, n, hi, scales, y, yf, w, cnt); break;
+    default: gemv_low_kernel<16><<<grid, 256, 0, stream>>>(x, b, k, n, hi, scales, y, yf, w, cnt); break;
   }
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess && ns > 1) e = launch_reduce(w, ns, B, N, nullptr, nullptr, yf, y, stream);
-  return e;
+  return hipGetLastError();
 }
 
 hipError_t launch_gemv_escalate(const uint16_t* x, int64_t B, int64_t K, int64_t N, const uint8_t* hi,
@@ -584,7 +752,6 @@ hipError_t launch_gemv_escalate(const uint16_t* x, int64_t B, int64_t K, int64_t
   if (tiles == 0) return hipSuccess;
   const int ns = slices_for(B, N, K, ws_bytes);
   const int b = (int)B, k = (int)K, n = (int)N;
-  float* w = static_cast<float*>(ws);
   if (ns == 1 && tiles >= 2048) {
     // enough tiles for one wave each: no cross-wave reduction
     if (yf)
@@ -600,14 +767,14 @@ hipError_t launch_gemv_escalate(const uint16_t* x, int64_t B, int64_t K, int64_t
   const int staged = per * 32 <= kXStageElems ? 1 : 0;
   const size_t shm = staged ? (size_t)kEscTokens * per * 32 * 2 : 0;
   const dim3 grid3(tiles, ns);
+  uint32_t* cnt = static_cast<uint32_t*>(ws);
+  float* w = ns > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kCounterBytes) : nullptr;
   if (yf)
-    gemv_escalate_kernel<kLo><<<grid3, 256, shm, stream>>>(x, b, k, n, hi, lo, scales, flags, y, yf, w, staged);
+    gemv_escalate_kernel<kLo><<<grid3, 256, shm, stream>>>(x, b, k, n, hi, lo, scales, flags, y, yf, w, cnt, staged);
   else
-    gemv_escalate_kernel<kHiLo><<<grid3, 256, shm, stream>>>(x, b, k, n, hi, lo, scales, flags, y, nullptr, w,
+    gemv_escalate_kernel<kHiLo><<<grid3, 256, shm, stream>>>(x, b, k, n, hi, lo, scales, flags, y, nullptr, w, cnt,
                                                              staged);
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess && ns > 1) e = launch_reduce(w, ns, B, N, flags, yf, nullptr, y, stream);
-  return e;
+  return hipGetLastError();
 }
 
 hipError_t launch_gemv_grouped(const rq_gemv_problem* probs, int count, int64_t total_tiles, int64_t B,

@@ -1,21 +1,20 @@
 """FP8 per-token-head-tile quantize-on-write with float32 scales.
 
 Oracle (test infrastructure).  Follows the Day-0 page (Day 0 LLM Inference
-Support, section III.3.3 "KV Cache: FP8 Per-Token-Head-Tile Quantization,
-Tile Size = 128", and the per-group listing of section V, which the page
-says the KV variant follows with a token x head x 128 grouping):
+Support, section III.3.3, "KV Cache: FP8 Per-Token-Head-Tile Quantization,
+Tile Size = 128"): within each token and head, every run of 128 consecutive
+elements shares one scaling factor, and the page says the per-group recipe
+of section V carries over with that grouping.  Written out from the
+mathematics of that recipe:
 
-1. group each (token, head) vector into tiles of 128 consecutive elements;
-2. amax per tile;
-3. scale = amax / 448, or 1 for an all-zero tile;
-4. q = x / scale, clipped to +-448;
-5. cast to E4M3FN (nearest, ties to even).
+* a tile's scaling factor is its largest magnitude divided by the largest
+  E4M3FN value, 448; a tile of zeros gets the factor 1 (nothing to divide);
+* every element is divided by its tile's factor, limited to [-448, 448] and
+  rounded to the nearest E4M3FN value (ties to the even code).
 
-Reading: unlike the power-of-two MX scale, this scale is the plain quotient
-amax / 448, kept as float32; steps 3 and 4 are float32 operations (one
-IEEE rounding each, as a float32 tensor pipeline performs them), because
-the float result decides the integer code and both sides must decide it in
-the same precision.
+Reading: the factor is the plain quotient (not a power of two) and is kept
+in float32, and the element division is a float32 operation; both decide
+the integer code, so the GPU makes them in the same precision.
 """
 
 import numpy as np
@@ -23,23 +22,34 @@ import numpy as np
 from . import formats as F
 
 TILE = 128
-FP8_MAX = np.float32(448.0)
+E4M3_LARGEST = np.float32(448.0)
+
+
+def tile_factor(tile_max):
+    """float32 largest magnitudes -> float32 scaling factors (1 where 0)."""
+    tile_max = np.asarray(tile_max, dtype=np.float32)
+    safe = np.where(tile_max > 0, tile_max, np.float32(448.0))
+    return np.where(tile_max > 0, np.divide(safe, E4M3_LARGEST, dtype=np.float32), np.float32(1.0))
+
+
+def encode_tiles(tiles, factors):
+    """tiles float32 [..., TILE], factors float32 [...] -> E4M3FN codes."""
+    ratio = np.divide(tiles, factors[..., None], dtype=np.float32)
+    limited = np.minimum(np.maximum(ratio, -E4M3_LARGEST), E4M3_LARGEST)
+    return F.e4m3_encode(limited.astype(np.float64))
 
 
 def quantize_kv(x_bits, tile=TILE):
     """x BF16 bits [T, H, D] (D % tile == 0) -> (codes uint8 [T, H, D],
     scales float32 [T, H, D/tile])."""
-    x32 = F.bf16_to_f64(x_bits).astype(np.float32)  # exact
-    T, H, D = x32.shape
+    vals = F.bf16_to_f64(x_bits).astype(np.float32)  # every BF16 value is a float32
+    T, H, D = vals.shape
     if D % tile:
         raise ValueError("head dim must be a multiple of the tile")
-    g = x32.reshape(T, H, D // tile, tile)
-    amax = np.abs(g).max(axis=-1)
-    scale = np.where(amax > 0, amax / FP8_MAX, np.float32(1.0)).astype(np.float32)
-    q = (g / scale[..., None]).astype(np.float32)
-    q = np.clip(q, -FP8_MAX, FP8_MAX)
-    codes = F.e4m3_encode(q.astype(np.float64))
-    return codes.reshape(T, H, D).astype(np.uint8), scale
+    tiles = vals.reshape(T, H, D // tile, tile)
+    factors = tile_factor(np.max(np.abs(tiles), axis=-1))
+    codes = encode_tiles(tiles, factors)
+    return codes.reshape(T, H, D).astype(np.uint8), factors.astype(np.float32)
 
 
 def dequantize_kv(codes, scales, tile=TILE):

@@ -36,7 +36,7 @@ def test_graph_replays_match_eager():
         d = W.c5_linear(i, N=n, K=k)
         planes = api.pack_nibble_planes(dev(d["w"]), dev(np.asarray(d["scales"], np.float16).view(np.int16)))
         wsb = L.rq_gemv_workspace_bytes(16, n, k)
-        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda")  # arrival counters start at zero
         carry = torch.empty((16, n), dtype=torch.float32, device="cuda") if i < 2 else None
         gemvs.append(dict(x=dev_bf16(d["x"]), planes=planes, n=n, k=k, ws=ws, wsb=wsb, carry=carry,
                           flags=dev(d["flags"]), y=torch.empty((16, n), dtype=torch.int16, device="cuda")))
