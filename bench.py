@@ -39,7 +39,7 @@ sys.path.insert(0, ROOT)
 
 PEAK = {"mxfp4": 10.1e15, "mxfp8": 5.0e15, "bf16": 2.5e15, "hbm": 8.0e12}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_mxfp8_qwen3_linear_set.json")
-GEMM_SRCS = [os.path.join(ROOT, "mixed_precision_block_amd", "csrc", f) for f in ("gemm.hip", "gemm_pipe.hip")]
+GEMM_SRCS = [os.path.join(ROOT, "mixed_precision_block_amd", "csrc", f) for f in ("gemm.hip", "gemm_pipe.hip", "rq_cvt.h")]
 
 
 def log(msg):
@@ -162,23 +162,28 @@ def write_traffic(pmc_dir):
     grids = {}
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         for (d, name, g), v in per_dispatch("main", counter).items():
-            if "gemm_pipe_kernel" not in name:
+            # the main line's exact MXFP8 GEMMs with BF16 output (template
+            # arguments <2, 0, ...>); the run also holds the FP8-instruction
+            # and FP32-output launches of the bench's other figures
+            if "gemm_pipe_kernel<2, 0," not in name:
                 continue
-            e = grids.setdefault(g, {"grid_threads": g, "dispatches": 0, "FETCH_SIZE": 0.0, "WRITE_SIZE": 0.0})
+            tmpl = name[name.index("<") + 1:name.index(">")]
+            e = grids.setdefault((tmpl, g), {"grid_threads": g, "template": tmpl, "dispatches": 0, "FETCH_SIZE": 0.0,
+                                             "WRITE_SIZE": 0.0})
             e[counter] += v * scale[counter]
             if counter == "FETCH_SIZE":
                 e["dispatches"] += 1
     per_grid = []
     for g, e in sorted(grids.items()):
         n = e["dispatches"]
-        per_grid.append({"grid_threads": g, "dispatches": n, "read_bytes": round(e["FETCH_SIZE"] / n),
-                         "write_bytes": round(e["WRITE_SIZE"] / n)})
+        per_grid.append({"template": e["template"], "grid_threads": e["grid_threads"], "dispatches": n,
+                         "read_bytes": round(e["FETCH_SIZE"] / n), "write_bytes": round(e["WRITE_SIZE"] / n)})
     total = sum((e["read_bytes"] + e["write_bytes"]) * e["dispatches"] for e in per_grid)
     nd = sum(e["dispatches"] for e in per_grid)
     M = 4096
     alg = [M * g["a"].shape[1] * 33 // 32 + g["w"].shape[0] * g["a"].shape[1] * 33 // 32 + M * g["w"].shape[0] * 2
            for g in W.c2_layer(M=M)]
-    summary = {"kernel": "gemm_pipe_kernel<MXFP8, BF16 out>",
+    summary = {"kernel": "gemm_pipe_kernel<MXFP8 exact, BF16 out>",
                "workload": "qwen3-0.6b linear set of one layer, 4096 tokens, MXFP8, four GEMMs per step",
                "gemm_source_sha256_16": source_hash(GEMM_SRCS),
                "hbm_bytes_per_launch": round(total / nd),
