@@ -99,6 +99,80 @@ __global__ __launch_bounds__(256) void quant_append_kernel(const uint16_t* __res
   if ((c & 3) == 0) scales[row * lds + (K >> 5) + (c >> 2)] = (uint8_t)sb;
 }
 
+// Primary quantization plus the appended columns in one pass over each row
+// (the gather form of the ARC activations and weights: primary blocks in
+// the original channel order, appended block j / 32 from channel idx[j]).
+// A workgroup owns a run of rows; thread t owns chunks c = t + 256 i
+// (i < CPT) of every row and encodes them from its registers, as
+// quant_rows_kernel does.  It parks in LDS what the appended columns take
+// from its chunk: RESIDUAL the residual of every element against the code
+// just made (residual8), COPY the values themselves.  Threads t < S / 8
+// then gather their appended chunk from LDS and encode it.  The next row's
+// loads go out before the current row is encoded.  idx entries outside
+// [0, K) read as 0.
+template <class Fmt, bool kResidual, int CPT>
+__global__ __launch_bounds__(256) void quant_rows_append_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                                int64_t K, const int32_t* __restrict__ idx,
+                                                                int64_t S, uint8_t* __restrict__ codes,
+                                                                uint8_t* __restrict__ scales, int rows_per_wg) {
+  extern __shared__ uint4 row_lds[];  // K / 8 chunks of BF16 (residuals or values)
+  constexpr int kElemBytesNum = Fmt::kMantBits == 1 ? 1 : 2;  // bytes per 2 elements
+  const int chunks = (int)(K >> 3), s_chunks = (int)(S >> 3);
+  const int64_t ldc = (K + S) / 2 * kElemBytesNum, lds = (K + S) >> 5;
+  const int64_t r0 = (int64_t)blockIdx.x * rows_per_wg;
+  const int64_t r1 = min(rows, r0 + rows_per_wg);
+  const uint16_t* rh = reinterpret_cast<const uint16_t*>(row_lds);
+  // this thread's appended chunk (threads below S / 8, at most 256 of them),
+  // its channels held in registers
+  const int t = (int)threadIdx.x;
+  const bool app = t < s_chunks;
+  int32_t ch[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ch[e] = app ? idx[8 * t + e] : -1;
+  uint4 q[CPT];
+  auto load_row = [&](int64_t r) {
+    const uint4* xr = reinterpret_cast<const uint4*>(x + r * K);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = t + 256 * i;
+      q[i] = c < chunks ? xr[c] : make_uint4(0, 0, 0, 0);
+    }
+  };
+  if (r0 < r1) load_row(r0);
+  for (int64_t row = r0; row < r1; ++row) {
+    __syncthreads();  // the previous row's appended reads are done with the LDS
+    uint4 cur[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) cur[i] = q[i];
+    if (row + 1 < r1) load_row(row + 1);
+    // chunks is a multiple of 4, so the four lanes of a quad (one 32-block)
+    // take the same branches
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = t + 256 * i;
+      if (c >= chunks) break;
+      const uint32_t sb = (uint32_t)(mx_block_exp<Fmt>(quad_max(amax8(cur[i]))) + 127);
+      const uint2 cv = encode8<Fmt>(cur[i], sb);
+      store8<Fmt>(cv, codes + row * ldc + (int64_t)c * 4 * kElemBytesNum);
+      if ((c & 3) == 0) scales[row * lds + (c >> 2)] = (uint8_t)sb;
+      if constexpr (kResidual)
+        row_lds[c] = residual8<Fmt>(cur[i], cv, sb);
+      else
+        row_lds[c] = cur[i];
+    }
+    __syncthreads();  // the parked row is complete
+    if (app) {  // whole quads: s_chunks is a multiple of 4
+      uint32_t v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (ch[e] >= 0 && ch[e] < K) ? (uint32_t)rh[ch[e]] : 0u;
+      const uint4 q2 = pack8(v);
+      const uint32_t sb2 = (uint32_t)(mx_block_exp<Fmt>(quad_max(amax8(q2))) + 127);
+      encode_store8<Fmt>(q2, sb2, codes + row * ldc + (K + (int64_t)t * 8) / 2 * kElemBytesNum);
+      if ((t & 3) == 0) scales[row * lds + (K >> 5) + (t >> 2)] = (uint8_t)sb2;
+    }
+  }
+}
+
 // ARCQuant fused front end (ARCQuant page, technical summary, "Kernel
 // Implementatie" with the stages of "Methodologie").  A workgroup owns
 // rows_per_wg consecutive rows and keeps its threads' perm entries in
@@ -272,15 +346,64 @@ hipError_t launch_quant_append(int fmt, int mode, const uint16_t* x, int64_t row
   return hipGetLastError();
 }
 
+// Workgroups that fit on the chip at once for a kernel of 256 threads with
+// `lds` bytes of LDS and about `vgprs` registers per thread, so that a run
+// of rows per workgroup covers the rows in one round.
+static int64_t resident_wgs(size_t lds, int vgprs) {
+  int per_cu = std::min(8, 512 / std::max(vgprs, 1));   // waves per SIMD = workgroups per CU
+  if (lds > 0) per_cu = std::min<int>(per_cu, (int)((160 * 1024) / lds));
+  return 256 * (int64_t)std::max(per_cu, 1);
+}
+
+template <class Fmt, int CPT>
+static hipError_t launch_rows_append_c(int mode, const uint16_t* x, int64_t rows, int64_t K, const int32_t* idx,
+                                       int64_t S, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  const size_t shm = (size_t)K * 2;
+  const int64_t target = resident_wgs(shm, 24 + 12 * CPT);
+  const int rpw = (int)((rows + target - 1) / target);
+  const unsigned g = (unsigned)((rows + rpw - 1) / rpw);
+  if (mode == 1)
+    quant_rows_append_kernel<Fmt, true, CPT><<<g, 256, shm, stream>>>(x, rows, K, idx, S, codes, scales, rpw);
+  else
+    quant_rows_append_kernel<Fmt, false, CPT><<<g, 256, shm, stream>>>(x, rows, K, idx, S, codes, scales, rpw);
+  return hipGetLastError();
+}
+
+template <class Fmt>
+static hipError_t launch_rows_append_f(int mode, const uint16_t* x, int64_t rows, int64_t K, const int32_t* idx,
+                                       int64_t S, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  if (K <= 2048) return launch_rows_append_c<Fmt, 1>(mode, x, rows, K, idx, S, codes, scales, stream);
+  if (K <= 4096) return launch_rows_append_c<Fmt, 2>(mode, x, rows, K, idx, S, codes, scales, stream);
+  if (K <= 8192) return launch_rows_append_c<Fmt, 4>(mode, x, rows, K, idx, S, codes, scales, stream);
+  return launch_rows_append_c<Fmt, 8>(mode, x, rows, K, idx, S, codes, scales, stream);
+}
+
+hipError_t launch_quant_rows_append(int fmt, int mode, const uint16_t* x, int64_t rows, int64_t K,
+                                    const int32_t* idx, int64_t S, uint8_t* codes, uint8_t* scales,
+                                    hipStream_t stream) {
+  const int64_t ldc = fmt == 1 ? (K + S) / 2 : K + S, lds = (K + S) / 32;
+  if (rows == 0) return hipSuccess;
+  if (S == 0) return launch_quant_rows(fmt, x, rows, K, codes, scales, ldc, lds, stream);
+  if (S > 2048 || K > 16384) {
+    // beyond one appended chunk per thread or a row in LDS: two passes
+    hipError_t e = launch_quant_rows(fmt, x, rows, K, codes, scales, ldc, lds, stream);
+    if (e == hipSuccess) e = launch_quant_append(fmt, mode, x, rows, K, idx, S, codes, scales, ldc, lds, stream);
+    return e;
+  }
+  if (fmt == 1) return launch_rows_append_f<FmtE2M1>(mode, x, rows, K, idx, S, codes, scales, stream);
+  return launch_rows_append_f<FmtE4M3>(mode, x, rows, K, idx, S, codes, scales, stream);
+}
+
 template <class Fmt, int CPT>
 static hipError_t launch_frontend_c(int mode, bool norm, const uint16_t* x, int64_t rows, int64_t K,
                                     const int32_t* perm, int64_t S, float eps, uint8_t* codes, uint8_t* scales,
                                     hipStream_t stream) {
-  // about 2048 workgroups, each over a run of rows (its perm entries stay
-  // in registers)
-  const int rpw = (int)std::max<int64_t>(1, rows / 2048);
-  const unsigned g = (unsigned)((rows + rpw - 1) / rpw);
+  // the workgroups that fit on the chip at once, each over a run of rows
+  // (its perm entries stay in registers), so the rows take one round
   const size_t shm = (size_t)K * 2;
+  const int64_t target = resident_wgs(shm, 32 + 20 * CPT);
+  const int rpw = (int)((rows + target - 1) / target);
+  const unsigned g = (unsigned)((rows + rpw - 1) / rpw);
   if (mode == 1 && norm)
     arc_frontend_kernel<Fmt, true, true, CPT><<<g, 256, shm, stream>>>(x, rows, K, perm, S, eps, codes, scales, rpw);
   else if (mode == 1)

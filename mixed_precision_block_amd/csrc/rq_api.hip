@@ -102,11 +102,13 @@ rq_status rq_quantize(const void* x_bf16, int64_t rows, int64_t K, int fmt, cons
   const int64_t Kp = K + S;
   const int64_t ldc = code_row_bytes(fmt, Kp), lds = Kp / 32;
   hipStream_t st = as_stream(stream);
-  hipError_t e = rq::launch_quant_rows(fmt, static_cast<const uint16_t*>(x_bf16), rows, K,
-                                       static_cast<uint8_t*>(codes), scales, ldc, lds, st);
-  if (e == hipSuccess && append != RQ_APPEND_NONE)
-    e = rq::launch_quant_append(fmt, append == RQ_APPEND_RESIDUAL ? 1 : 2, static_cast<const uint16_t*>(x_bf16),
-                                rows, K, idx, S, static_cast<uint8_t*>(codes), scales, ldc, lds, st);
+  hipError_t e;
+  if (append == RQ_APPEND_NONE)
+    e = rq::launch_quant_rows(fmt, static_cast<const uint16_t*>(x_bf16), rows, K, static_cast<uint8_t*>(codes),
+                              scales, ldc, lds, st);
+  else
+    e = rq::launch_quant_rows_append(fmt, append == RQ_APPEND_RESIDUAL ? 1 : 2, static_cast<const uint16_t*>(x_bf16),
+                                     rows, K, idx, S, static_cast<uint8_t*>(codes), scales, st);
   return hip_status(e, "rq_quantize launch");
 }
 
@@ -212,11 +214,8 @@ rq_status rq_gemm_arc(const void* a_bf16, int64_t M, int64_t K, const int32_t* i
   uint8_t* codes = static_cast<uint8_t*>(workspace);
   uint8_t* scales = codes + round256(static_cast<size_t>(M * (Kp / 2)));
   hipStream_t st = as_stream(stream);
-  hipError_t e = rq::launch_quant_rows(RQ_MXFP4, static_cast<const uint16_t*>(a_bf16), M, K, codes, scales, Kp / 2,
-                                       Kp / 32, st);
-  if (e == hipSuccess)
-    e = rq::launch_quant_append(RQ_MXFP4, 1, static_cast<const uint16_t*>(a_bf16), M, K, idx, S, codes, scales,
-                                Kp / 2, Kp / 32, st);
+  hipError_t e = rq::launch_quant_rows_append(RQ_MXFP4, 1, static_cast<const uint16_t*>(a_bf16), M, K, idx, S, codes,
+                                              scales, st);
   if (e == hipSuccess)
     e = rq::launch_gemm(RQ_MXFP4, out == RQ_OUT_F32 ? rq::kEpiStoreF32 : rq::kEpiStoreBf16, codes, scales, w_aug,
                         w_aug_scales, M, N, Kp, y, st);

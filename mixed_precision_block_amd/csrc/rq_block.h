@@ -77,6 +77,39 @@ __device__ __forceinline__ void store8(uint2 c, uint8_t* dst) {
     *reinterpret_cast<uint2*>(dst) = c;
 }
 
+// Residuals of 8 BF16 values against their codes c under block scale byte
+// sb: x - deq(code), as BF16 bit patterns.  The codes are dequantized by
+// the hardware scaled conversion to float (exact: a power-of-two scaling
+// of a grid value) and the difference is exact in float: both terms are
+// multiples of the smaller of x's unit in the last place and the grid step,
+// and the residual is below half a grid step, so it is a BF16 value.
+typedef float rq_v2f __attribute__((ext_vector_type(2)));
+template <class Fmt>
+__device__ __forceinline__ uint4 residual8(uint4 q, uint2 c, uint32_t sb) {
+  const float scale = e8m0_to_f32(sb);
+  rq_v2f t[4];
+  if constexpr (Fmt::kMantBits == 1) {
+    t[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, scale, 0);
+    t[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, scale, 1);
+    t[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, scale, 2);
+    t[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, scale, 3);
+  } else {
+    t[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c.x, scale, false);
+    t[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c.x, scale, true);
+    t[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c.y, scale, false);
+    t[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c.y, scale, true);
+  }
+  const float d[8] = {t[0].x, t[0].y, t[1].x, t[1].y, t[2].x, t[2].y, t[3].x, t[3].y};
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  uint32_t r[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float xv = bf16_to_f32((e & 1) ? w[e >> 1] >> 16 : w[e >> 1] & 0xFFFFu);
+    r[e] = __builtin_bit_cast(uint32_t, xv - d[e]) >> 16;
+  }
+  return pack8(r);
+}
+
 // Encode 8 BF16 values with block scale byte sb and store them: FP4 -> one
 // dword (element 2j in the low nibble of byte j), FP8 -> two dwords.
 template <class Fmt>

@@ -50,6 +50,13 @@ hipError_t launch_quant_rows(int fmt, const uint16_t* x, int64_t rows, int64_t K
 hipError_t launch_quant_append(int fmt, int mode, const uint16_t* x, int64_t rows, int64_t K,
                                const int32_t* idx, int64_t S, uint8_t* codes, uint8_t* scales,
                                int64_t ldc_bytes, int64_t lds_bytes, hipStream_t stream);
+// Primary quantization with appended columns (mode 1 residual, 2 copy) in
+// one pass over each row, codes [rows x (K+S)] (FP4 packed) and scales
+// [rows x (K+S)/32]; S == 0 is plain quantization.  Falls back to the two
+// passes above for S > 2048 or K > 16384.
+hipError_t launch_quant_rows_append(int fmt, int mode, const uint16_t* x, int64_t rows, int64_t K,
+                                    const int32_t* idx, int64_t S, uint8_t* codes, uint8_t* scales,
+                                    hipStream_t stream);
 // Fused front end: optional RMSNorm (eps, no gain), reorder by perm,
 // primary block quantization over K, and for positions 0..S-1 an appended
 // block (mode 1 residual, 2 copy; S == 0 for none).  K <= 16384 (the row

@@ -138,6 +138,27 @@ def test_append_modes(fmt, ofmt, mode):
     assert np.array_equal(gc, Q.storage_codes(oc, ofmt))
 
 
+@pytest.mark.parametrize("fmt,ofmt", FMTS)
+@pytest.mark.parametrize("K,S", [(256, 32), (4096, 128), (2080, 96), (9600, 2048), (12288, 2080)])
+def test_residual_append_extreme_exponents(fmt, ofmt, K, S):
+    """Residual appends on blocks whose scale spans BF16's range: rows of
+    subnormal BF16 values (block byte 0 or near it), rows near the largest
+    finite BF16 and ordinary rows, for the one-pass path (a row in LDS;
+    S / 8 appended chunks over the workgroup) and, at K = 12288 with
+    S = 2080 (more appended chunks than threads), the two-pass path."""
+    rng = np.random.default_rng(K + S)
+    rows = 24
+    mag = rng.standard_normal((rows, K))
+    scale = np.concatenate([np.full(8, 2.0 ** -133), np.full(8, 2.0 ** 120), np.ones(8)])
+    x = F.f64_to_bf16(mag * scale[:, None])
+    idx = rng.integers(0, K, S).astype(np.int32)
+    log(f"extreme residual append fmt={ofmt} K={K} S={S}")
+    gc, gs = gpu_quant(x, fmt, idx, L.RQ_APPEND_RESIDUAL)
+    oc, os_ = A.augment_activations(x, idx, ofmt)
+    assert np.array_equal(gs, os_)
+    assert np.array_equal(gc, Q.storage_codes(oc, ofmt))
+
+
 def test_channel_amax_and_selection():
     for d, S in ((W.c3_arc(), 128), (W.c1_gemm_mxfp4(), 32)):
         x = d["a"]
