@@ -16,10 +16,10 @@
 // Work split: a workgroup owns 64 rows; its four waves take interleaved
 // 32-blocks of K; per block each lane turns its 16 bytes into 16 exact BF16
 // pairs once and reuses them for every token (low pass: the block's x for
-// all tokens is one coalesced 1 KiB load per wave, broadcast through LDS;
-// escalation: the few flagged tokens' x are copied to LDS by the workgroup
-// where they fit, else come through the scalar cache, the address being
-// wave-uniform).  FP32 block partials are scaled by
+// all tokens is four 256-byte loads per wave that DPP row broadcasts hand
+// to the dot products, with no LDS traffic; escalation: the few flagged
+// tokens' x are copied to LDS by the workgroup where they fit, else come
+// through the scalar cache, the address being wave-uniform).  FP32 block partials are scaled by
 // the block's FP16 scale and accumulated; the four waves' sums are added in
 // a fixed order through LDS.  Shapes with few row tiles split K over
 // workgroups (grid y); each writes its FP32 partial sums to the caller's
@@ -115,18 +115,19 @@ __device__ __forceinline__ void unpack_full(const uint4 dh, const uint4 dl, bf16
 // only lo when it starts from the low pass's FP32 carry.
 enum Planes { kHi = 0, kHiLo = 1, kLo = 2 };
 
-// Every pass shares one loop: a workgroup owns 64 rows and the K-blocks
-// [b0, b1) of its slice (grid y splits K when there are too few row tiles
-// to fill the chip); wave w takes blocks b0 + w, b0 + w + 4, ...  The
-// workgroup computes TB accumulator slots; slot t is token tok[t] for
+// Both passes share one shape of loop: a workgroup owns 64 rows and the
+// K-blocks [b0, b1) of its slice (grid y splits K when there are too few
+// row tiles to fill the chip); wave w takes blocks b0 + w, b0 + w + 4, ...
+// The workgroup computes TB accumulator slots; slot t is token tok[t] for
 // t < nt.  The four waves' sums meet in LDS in a fixed order; with one
-// slice the workgroup writes BF16 outputs (kHi: also the FP32 carry yf
-// when given; kLo: adds the carry first), otherwise FP32 partials to
-// ws[tile][slice][token][row] (16 token rows per slice) that the tile's
-// last workgroup adds in slice order (split_finish).
+// slice the workgroup writes BF16 outputs (the low pass: also the FP32
+// carry yf when given; the escalation from the carry: adds it first),
+// otherwise FP32 partials to ws[tile][slice][token][row] (16 token rows
+// per slice) that the tile's last workgroup adds in slice order
+// (split_finish).  gemv_tile is the escalation's loop, low_tile the low
+// pass's.
 constexpr int kWsTokens = 16;
 constexpr int kMaxSlices = 16;  // K slices of a split launch, at most
-constexpr int kLowRows = 1;     // 64-row tiles per low-pass workgroup
 
 template <int TB, int kP>
 __device__ __forceinline__ void gemv_tile(const uint16_t* __restrict__ x, int B, int K, int N,
@@ -134,7 +135,7 @@ __device__ __forceinline__ void gemv_tile(const uint16_t* __restrict__ x, int B,
                                           const uint16_t* __restrict__ sc, const int* tok, int nt,
                                           uint16_t* __restrict__ y, float* __restrict__ yf, float* ws,
                                           float (*red)[TB][64], uint4* xs, int tile, int slice, int nslice) {
-  constexpr bool kFull = kP != kHi;  // an escalation pass: flagged tokens only
+  static_assert(kP != kHi, "the low pass runs in low_tile");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nb = K >> 5;
@@ -144,25 +145,17 @@ __device__ __forceinline__ void gemv_tile(const uint16_t* __restrict__ x, int B,
   const uint4* hp = reinterpret_cast<const uint4*>(hi) + tbase;
   const uint4* lp = reinterpret_cast<const uint4*>(lo) + tbase;
   const uint16_t* sp = sc + tbase;
-  // Low pass: x of the current block for all tokens -- lane l fetches 8
-  // values (16 bytes) of token l / 4 one block ahead, the wave parks them
-  // in its own 1 KiB LDS slot, and every lane reads them back as broadcasts.
-  const int xt_l = (lane >> 2) < B ? (lane >> 2) : B - 1;
-  const uint4* xg = reinterpret_cast<const uint4*>(x + (size_t)xt_l * K) + (lane & 3);
-  uint4* const xslot = xs + wave * 64;
   float acc[TB];
 #pragma unroll
   for (int t = 0; t < TB; ++t) acc[t] = 0.0f;
 
   int b = b0 + wave;
-  uint4 xv = make_uint4(0, 0, 0, 0);
-  if (!kFull && b < b1) xv = gload16(xg, (size_t)b * 4);
   // the next block's planes and scale load one block ahead
   uint4 nh = make_uint4(0, 0, 0, 0), nl = make_uint4(0, 0, 0, 0);
   uint16_t ns = 0;
   if (b < b1) {
-    if constexpr (kP != kLo) nh = gload16(hp, (size_t)b * 64);
-    if constexpr (kP != kHi) nl = gload16(lp, (size_t)b * 64);
+    if constexpr (kP == kHiLo) nh = gload16(hp, (size_t)b * 64);
+    nl = gload16(lp, (size_t)b * 64);
     ns = gload2(sp, (size_t)b * 64);
   }
   for (; b < b1; b += 4) {
@@ -170,49 +163,32 @@ __device__ __forceinline__ void gemv_tile(const uint16_t* __restrict__ x, int B,
     const float s = f16_to_f32(ns);
     {
       const int bn = b + 4 < b1 ? b + 4 : b;  // the last block reloads itself
-      if constexpr (kP != kLo) nh = gload16(hp, (size_t)bn * 64);
-      if constexpr (kP != kHi) nl = gload16(lp, (size_t)bn * 64);
+      if constexpr (kP == kHiLo) nh = gload16(hp, (size_t)bn * 64);
+      nl = gload16(lp, (size_t)bn * 64);
       ns = gload2(sp, (size_t)bn * 64);
-    }
-    if constexpr (!kFull) {
-      // a wave's LDS accesses complete in order: this write follows the
-      // reads of the previous block and precedes the reads below
-      xslot[lane] = xv;
-      const int bn = b + 4 < b1 ? b + 4 : b;  // next block's x (the last reloads itself)
-      xv = gload16(xg, (size_t)bn * 4);
     }
     bf16x2 wp[16];
     if constexpr (kP == kHiLo)
       unpack_full(dh, dl, wp);
-    else if constexpr (kP == kLo)
-      unpack_lo16(dl, wp);
     else
-      unpack_hi16(dh, wp);
+      unpack_lo16(dl, wp);
 #pragma unroll
     for (int t = 0; t < TB; ++t) {
-      if (kFull && t >= nt) continue;  // wave-uniform; the low pass computes every slot
+      if (t >= nt) continue;  // wave-uniform
       uint32_t xq[16];
-      if constexpr (kFull) {
-        if (xs != nullptr) {
-          // the flagged tokens' x of this slice, staged in LDS by the workgroup
-          const int kc = (b1 - b0) * 4;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint4 v = xs[t * kc + (b - b0) * 4 + i];
-            xq[4 * i] = v.x, xq[4 * i + 1] = v.y, xq[4 * i + 2] = v.z, xq[4 * i + 3] = v.w;
-          }
-        } else {
-          // the few flagged tokens: x straight through the scalar cache
-          const uint32_t* xt = reinterpret_cast<const uint32_t*>(x) + ((size_t)tok[t] * K + 32 * (size_t)b) / 2;
-#pragma unroll
-          for (int p = 0; p < 16; ++p) xq[p] = xt[p];
-        }
-      } else {
+      if (xs != nullptr) {
+        // the flagged tokens' x of this slice, staged in LDS by the workgroup
+        const int kc = (b1 - b0) * 4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint4 v = xslot[4 * t + i];
+          const uint4 v = xs[t * kc + (b - b0) * 4 + i];
           xq[4 * i] = v.x, xq[4 * i + 1] = v.y, xq[4 * i + 2] = v.z, xq[4 * i + 3] = v.w;
         }
+      } else {
+        // the few flagged tokens: x straight through the scalar cache
+        const uint32_t* xt = reinterpret_cast<const uint32_t*>(x) + ((size_t)tok[t] * K + 32 * (size_t)b) / 2;
+#pragma unroll
+        for (int p = 0; p < 16; ++p) xq[p] = xt[p];
       }
       float blk = 0.0f;
 #pragma unroll
@@ -232,7 +208,6 @@ __device__ __forceinline__ void gemv_tile(const uint16_t* __restrict__ x, int B,
       if (n < N) {
         const size_t o = (size_t)tok[t] * N + n;
         if constexpr (kP == kLo) v = yf[o] + v;
-        if (kP == kHi && yf != nullptr) yf[o] = v;
         y[o] = (uint16_t)f32_to_bf16(v);
       }
     } else {
@@ -304,109 +279,177 @@ __device__ __forceinline__ void split_finish(const float* __restrict__ ws, uint3
   if (threadIdx.x == 0) __hip_atomic_store(counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Low pass over R 64-row tiles (tile R t .. R t + R - 1) at once: lane l
-// owns row l of each, so every broadcast read of x feeds R rows' dot
-// products (LDS traffic per multiply-add falls by R).  Same arithmetic and
-// order per output as gemv_tile's low pass.  Split K: partials per 64-row
-// tile, finished by split_finish<kHi, R>.
-template <int TB, int R>
+// The low pass's x goes straight to registers, with no LDS traffic.  For a
+// K-block, lane l (n = l % 16, its place in its row of 16 lanes) holds in
+// register j of group g dword 4 (n % 4) + j of the 64-byte block of slot
+// 4 g + n / 4; the wave's four rows hold the same (each group is one
+// 256-byte read).  Dword p of slot 4 g + q is then register p % 4 of group
+// g at lane 4 q + p / 4 of every row, and a DPP row broadcast
+// (row_newbcast) hands it to all 16 lanes of the row as the dot product's
+// first operand.
+//
+// blk[q] + sum_p w[p] . (x_2p, x_2p+1) of slot 4 g + q for q < 4, each in
+// p order (the escalation's order).  A DPP instruction must not read a VGPR
+// that one of the two instructions before it wrote -- its accumulator
+// included -- so the four slots' dot products alternate (three others
+// between two writes of one sum) and an s_nop covers the instructions
+// before the block.
+__device__ __forceinline__ void dot4_block_bcast(float (&blk)[4], const uint4 xg, const uint32_t (&w)[16]) {
+  asm("s_nop 1\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %4, %8 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %4, %8 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %2, %4, %8 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %3, %4, %8 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %5, %9 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %5, %9 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %2, %5, %9 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %3, %5, %9 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %6, %10 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %6, %10 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %2, %6, %10 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %3, %6, %10 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %7, %11 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %7, %11 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %2, %7, %11 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %3, %7, %11 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %4, %12 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %4, %12 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %2, %4, %12 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %3, %4, %12 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %5, %13 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %5, %13 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %2, %5, %13 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %3, %5, %13 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %6, %14 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %6, %14 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %2, %6, %14 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %3, %6, %14 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %7, %15 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %7, %15 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %2, %7, %15 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %3, %7, %15 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %4, %16 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %4, %16 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %2, %4, %16 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %3, %4, %16 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %5, %17 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %5, %17 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %2, %5, %17 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %3, %5, %17 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %6, %18 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %6, %18 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %2, %6, %18 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %3, %6, %18 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %7, %19 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %7, %19 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %2, %7, %19 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %3, %7, %19 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %4, %20 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %4, %20 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %2, %4, %20 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %3, %4, %20 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %5, %21 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %5, %21 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %2, %5, %21 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %3, %5, %21 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %6, %22 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %6, %22 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %2, %6, %22 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %3, %6, %22 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %7, %23 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %7, %23 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %2, %7, %23 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %3, %7, %23 row_newbcast:15 row_mask:0xf bank_mask:0xf"
+      : "+v"(blk[0]), "+v"(blk[1]), "+v"(blk[2]), "+v"(blk[3])
+      : "v"(xg.x), "v"(xg.y), "v"(xg.z), "v"(xg.w), "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(w[4]),
+        "v"(w[5]), "v"(w[6]), "v"(w[7]), "v"(w[8]), "v"(w[9]), "v"(w[10]), "v"(w[11]), "v"(w[12]), "v"(w[13]),
+        "v"(w[14]), "v"(w[15]));
+}
+
+// Low pass of one 64-row tile over the K-blocks of its slice: wave w takes
+// blocks b0 + w, b0 + w + 4, ...; every block's planes, scale and x load one
+// block ahead.  With one slice the workgroup writes BF16 outputs (and the
+// FP32 carry yf when given), otherwise FP32 partials that split_finish adds.
+template <int TB>
 __device__ __forceinline__ void low_tile(const uint16_t* __restrict__ x, int B, int K, int N,
                                          const uint8_t* __restrict__ hi, const uint16_t* __restrict__ sc, int nt,
                                          uint16_t* __restrict__ y, float* __restrict__ yf, float* ws,
-                                         float (*red)[TB][64], uint4* xs, int tile, int slice, int nslice) {
+                                         float (*red)[TB][64], int tile, int slice, int nslice) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nb = K >> 5;
   const int per = (nb + nslice - 1) / nslice;
   const int b0 = slice * per, b1 = min(nb, b0 + per);
-  const int ntiles = (N + 63) >> 6;
-  const uint4* hp[R];
-  const uint16_t* sp[R];
-  bool live[R];
+  const size_t base = (size_t)tile * nb * 64 + lane;
+  const uint4* hp = reinterpret_cast<const uint4*>(hi) + base;
+  const uint16_t* sp = sc + base;
+  constexpr int G = (TB + 3) / 4;  // groups of four slots
+  const uint4* xg[G];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int t64 = tile * R + r;
-    live[r] = t64 < ntiles;  // workgroup-uniform
-    const size_t base = (size_t)(live[r] ? t64 : 0) * nb * 64 + lane;
-    hp[r] = reinterpret_cast<const uint4*>(hi) + base;
-    sp[r] = sc + base;
+  for (int g = 0; g < G; ++g) {
+    const int slot = 4 * g + ((lane & 15) >> 2);
+    xg[g] = reinterpret_cast<const uint4*>(x + (size_t)(slot < B ? slot : B - 1) * K) + (lane & 3);
   }
-  const int xt_l = (lane >> 2) < B ? (lane >> 2) : B - 1;
-  const uint4* xg = reinterpret_cast<const uint4*>(x + (size_t)xt_l * K) + (lane & 3);
-  uint4* const xslot = xs + wave * 64;
-  float acc[R][TB];
+  float acc[TB];
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+  for (int t = 0; t < TB; ++t) acc[t] = 0.0f;
+  // Two register sets alternate (block b in one while b + 4 loads into the
+  // other), so no loaded value is copied; a block past the slice's end
+  // reloads the last one, always in bounds.
+  auto load = [&](int blk_i, uint4 (&xr)[G], uint4& h, uint16_t& sv) {
+    h = gload16(hp, (size_t)blk_i * 64), sv = gload2(sp, (size_t)blk_i * 64);
 #pragma unroll
-    for (int t = 0; t < TB; ++t) acc[r][t] = 0.0f;
+    for (int g = 0; g < G; ++g) xr[g] = gload16(xg[g], (size_t)blk_i * 4);
+  };
+  auto block = [&](const uint4 (&xr)[G], const uint4 h, const uint16_t sv) {
+    const float s = f16_to_f32(sv);
+    bf16x2 wp[16];
+    unpack_hi16(h, wp);
+    uint32_t w[16];
+#pragma unroll
+    for (int p = 0; p < 16; ++p) w[p] = __builtin_bit_cast(uint32_t, wp[p]);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float blk[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      dot4_block_bcast(blk, xr[g], w);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (4 * g + q < TB) acc[4 * g + q] = fmaf(blk[q], s, acc[4 * g + q]);
+    }
+  };
   int b = b0 + wave;
-  uint4 xv = make_uint4(0, 0, 0, 0);
-  uint4 nh[R];
-  uint16_t ns[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) nh[r] = make_uint4(0, 0, 0, 0), ns[r] = 0;
   if (b < b1) {
-    xv = gload16(xg, (size_t)b * 4);
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (live[r]) nh[r] = gload16(hp[r], (size_t)b * 64), ns[r] = gload2(sp[r], (size_t)b * 64);
-  }
-  for (; b < b1; b += 4) {
-    uint4 dh[R];
-    float s[R];
-    const int bn = b + 4 < b1 ? b + 4 : b;  // the last block reloads itself
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      dh[r] = nh[r], s[r] = f16_to_f32(ns[r]);
-      if (live[r]) nh[r] = gload16(hp[r], (size_t)bn * 64), ns[r] = gload2(sp[r], (size_t)bn * 64);
-    }
-    // a wave's LDS accesses complete in order: this write follows the
-    // reads of the previous block and precedes the reads below
-    xslot[lane] = xv;
-    xv = gload16(xg, (size_t)bn * 4);
-    bf16x2 wp[R][16];
-#pragma unroll
-    for (int r = 0; r < R; ++r) unpack_hi16(dh[r], wp[r]);
-#pragma unroll
-    for (int t = 0; t < TB; ++t) {
-      uint32_t xq[16];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 v = xslot[4 * t + i];
-        xq[4 * i] = v.x, xq[4 * i + 1] = v.y, xq[4 * i + 2] = v.z, xq[4 * i + 3] = v.w;
-      }
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        float blk = 0.0f;
-#pragma unroll
-        for (int p = 0; p < 16; ++p) blk = __builtin_amdgcn_fdot2_f32_bf16(wp[r][p], as_bf16x2(xq[p]), blk, false);
-        acc[r][t] = fmaf(blk, s[r], acc[r][t]);
-      }
+    uint4 xa[G], xb[G], ha, hb;
+    uint16_t sa, sb;
+    load(b, xa, ha, sa);
+    for (;;) {
+      load(b + 4 < b1 ? b + 4 : b, xb, hb, sb);
+      block(xa, ha, sa);
+      b += 4;
+      if (b >= b1) break;
+      load(b + 4 < b1 ? b + 4 : b, xa, ha, sa);
+      block(xb, hb, sb);
+      b += 4;
+      if (b >= b1) break;
     }
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    if (r > 0) __syncthreads();  // the previous sub-tile's reads of red are done
-#pragma unroll
-    for (int t = 0; t < TB; ++t) red[wave][t][lane] = acc[r][t];
-    __syncthreads();
-    if (!live[r]) continue;
-    const int t64 = tile * R + r;
-    for (int o = threadIdx.x; o < TB * 64; o += 256) {
-      const int t = o >> 6, l = o & 63;
-      const int n = t64 * 64 + l;
-      if (t >= nt) continue;
-      const float v = ((red[0][t][l] + red[1][t][l]) + red[2][t][l]) + red[3][t][l];
-      if (nslice == 1) {
-        if (n < N) {
-          const size_t i = (size_t)t * N + n;
-          if (yf != nullptr) yf[i] = v;
-          y[i] = (uint16_t)f32_to_bf16(v);
-        }
-      } else {
-        __hip_atomic_store(ws + (((size_t)t64 * nslice + slice) * kWsTokens + t) * 64 + l, v, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+  for (int t = 0; t < TB; ++t) red[wave][t][lane] = acc[t];
+  __syncthreads();
+  for (int o = threadIdx.x; o < TB * 64; o += 256) {
+    const int t = o >> 6, l = o & 63;
+    const int n = tile * 64 + l;
+    if (t >= nt) continue;
+    const float v = ((red[0][t][l] + red[1][t][l]) + red[2][t][l]) + red[3][t][l];
+    if (nslice == 1) {
+      if (n < N) {
+        const size_t i = (size_t)t * N + n;
+        if (yf != nullptr) yf[i] = v;
+        y[i] = (uint16_t)f32_to_bf16(v);
       }
+    } else {
+      __hip_atomic_store(ws + (((size_t)tile * nslice + slice) * kWsTokens + t) * 64 + l, v, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -418,9 +461,8 @@ __global__ __launch_bounds__(256) void gemv_low_kernel(const uint16_t* __restric
                                                        float* __restrict__ yf, float* __restrict__ ws,
                                                        uint32_t* __restrict__ counters) {
   __shared__ float red[4][TB][64];
-  __shared__ uint4 xs[4 * 64];
-  low_tile<TB, kLowRows>(x, B, K, N, hi, sc, B < TB ? B : TB, y, yf, ws, red, xs, blockIdx.x, blockIdx.y, gridDim.y);
-  if (gridDim.y > 1) split_finish<kHi, kLowRows>(ws, counters, blockIdx.x, gridDim.y, N, (1u << B) - 1u, y, yf);
+  low_tile<TB>(x, B, K, N, hi, sc, B < TB ? B : TB, y, yf, ws, red, blockIdx.x, blockIdx.y, gridDim.y);
+  if (gridDim.y > 1) split_finish<kHi>(ws, counters, blockIdx.x, gridDim.y, N, (1u << B) - 1u, y, yf);
 }
 
 // Escalation: a workgroup takes the flagged tokens in groups of four (in
@@ -606,16 +648,11 @@ template <int TB>
 __global__ __launch_bounds__(256) void gemv_low_grouped_kernel(const rq_gemv_problem* __restrict__ probs, int count,
                                                                int B) {
   __shared__ float red[4][TB][64];
-  __shared__ uint4 xs[4 * 64];
   const rq_gemv_problem* p = find_problem(probs, count, blockIdx.x);
   const int64_t tile = (int64_t)blockIdx.x - p->tile_start;
   if (tile < 0 || tile >= (p->N + 63) / 64) return;  // a total beyond the plan
-  int tok[TB];
-#pragma unroll
-  for (int t = 0; t < TB; ++t) tok[t] = t;
-  gemv_tile<TB, kHi>(static_cast<const uint16_t*>(p->x_bf16), B, (int)p->K, (int)p->N, p->w_hi, nullptr,
-                     p->scales_tiled, tok, B < TB ? B : TB, static_cast<uint16_t*>(p->y_bf16), p->y_f32, nullptr,
-                     red, xs, (int)tile, 0, 1);
+  low_tile<TB>(static_cast<const uint16_t*>(p->x_bf16), B, (int)p->K, (int)p->N, p->w_hi, p->scales_tiled,
+               B < TB ? B : TB, static_cast<uint16_t*>(p->y_bf16), p->y_f32, nullptr, red, (int)tile, 0, 1);
 }
 
 // LDS for the grouped escalation's copy of the flagged tokens' x: problems
@@ -731,7 +768,7 @@ hipError_t launch_gemv_low(const uint16_t* x, int64_t B, int64_t K, int64_t N, c
   const unsigned tiles = (unsigned)((N + 63) / 64);
   if (tiles == 0) return hipSuccess;
   const int ns = slices_for(B, N, K, ws_bytes);
-  const dim3 grid((tiles + kLowRows - 1) / kLowRows, ns);  // kLowRows 64-row tiles per workgroup
+  const dim3 grid(tiles, ns);
   const int b = (int)B, k = (int)K, n = (int)N;
   uint32_t* cnt = static_cast<uint32_t*>(ws);
   float* w = ns > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kCounterBytes) : nullptr;
