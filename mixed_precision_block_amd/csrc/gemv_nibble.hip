@@ -129,12 +129,29 @@ enum Planes { kHi = 0, kHiLo = 1, kLo = 2 };
 constexpr int kWsTokens = 16;
 constexpr int kMaxSlices = 16;  // K slices of a split launch, at most
 
+// LDS budget for staging the flagged tokens' x in the escalation: up to
+// kXStageElems elements per token of a workgroup's K range.
+constexpr int kXStageElems = 4096;
+
+// Stage x[tok[t]][32 b0, 32 b1) for t < nt into xst (4 (b1 - b0) 16-byte
+// chunks per token).  Every thread of the workgroup calls it.
+__device__ __forceinline__ void stage_x(uint4* xst, const uint16_t* __restrict__ x, int K, const int* tok, int nt,
+                                        int b0, int b1) {
+  const int kc = (b1 - b0) * 4;
+  for (int i = threadIdx.x; i < nt * kc; i += 256) {
+    const int t = i / kc, c = i - t * kc;
+    xst[t * kc + c] = gload16(reinterpret_cast<const uint4*>(x + (size_t)tok[t] * K + (size_t)b0 * 32), c);
+  }
+  __syncthreads();
+}
+
 template <int TB, int kP>
 __device__ __forceinline__ void gemv_tile(const uint16_t* __restrict__ x, int B, int K, int N,
                                           const uint8_t* __restrict__ hi, const uint8_t* __restrict__ lo,
                                           const uint16_t* __restrict__ sc, const int* tok, int nt,
                                           uint16_t* __restrict__ y, float* __restrict__ yf, float* ws,
-                                          float (*red)[TB][64], uint4* xs, int tile, int slice, int nslice) {
+                                          float (*red)[TB][64], uint4* xs, bool stage, int tile, int slice,
+                                          int nslice) {
   static_assert(kP != kHi, "the low pass runs in low_tile");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -158,6 +175,8 @@ __device__ __forceinline__ void gemv_tile(const uint16_t* __restrict__ x, int B,
     nl = gload16(lp, (size_t)b * 64);
     ns = gload2(sp, (size_t)b * 64);
   }
+  // the copy of the flagged tokens' x to LDS overlaps the first planes' loads
+  if (stage) stage_x(xs, x, K, tok, nt, b0, b1);
   for (; b < b1; b += 4) {
     const uint4 dh = nh, dl = nl;
     const float s = f16_to_f32(ns);
@@ -489,22 +508,6 @@ __device__ __forceinline__ int next_group(uint32_t& fmask, int tok[kEscTokens]) 
   return nt;
 }
 
-// LDS budget for staging the flagged tokens' x in the escalation: up to
-// kXStageElems elements per token of a workgroup's K range.
-constexpr int kXStageElems = 4096;
-
-// Stage x[tok[t]][32 b0, 32 b1) for t < nt into xst (4 (b1 - b0) 16-byte
-// chunks per token).  Every thread of the workgroup calls it.
-__device__ __forceinline__ void stage_x(uint4* xst, const uint16_t* __restrict__ x, int K, const int* tok, int nt,
-                                        int b0, int b1) {
-  const int kc = (b1 - b0) * 4;
-  for (int i = threadIdx.x; i < nt * kc; i += 256) {
-    const int t = i / kc, c = i - t * kc;
-    xst[t * kc + c] = gload16(reinterpret_cast<const uint4*>(x + (size_t)tok[t] * K + (size_t)b0 * 32), c);
-  }
-  __syncthreads();
-}
-
 // Escalation of one 64-row tile by one wave (lane = row), over all of K.
 // The sum is kept as four partials over the blocks b = w mod 4, combined
 // as ((p0 + p1) + p2) + p3 -- the order of the four-wave tile (gemv_tile
@@ -614,17 +617,8 @@ __global__ __launch_bounds__(256) void gemv_escalate_kernel(const uint16_t* __re
   if (all == 0) return;  // nothing flagged: no weight traffic, no arrival (the counters stay zero)
   int tok[kEscTokens];
   for (int nt; (nt = next_group(fmask, tok)) > 0;) {  // nothing (more) flagged: no weight traffic
-    uint4* xs = nullptr;
-    if (staged) {
-      const int nb = K >> 5, per = (nb + (int)gridDim.y - 1) / (int)gridDim.y;
-      const int b0 = (int)blockIdx.y * per, b1 = min(nb, b0 + per);
-      if (b0 < b1) {
-        stage_x(xst, x, K, tok, nt, b0, b1);
-        xs = xst;
-      }
-    }
-    gemv_tile<kEscTokens, kP>(x, B, K, N, hi, lo, sc, tok, nt, y, yf, ws, red, xs, blockIdx.x, blockIdx.y,
-                              gridDim.y);
+    gemv_tile<kEscTokens, kP>(x, B, K, N, hi, lo, sc, tok, nt, y, yf, ws, red, staged ? xst : nullptr, staged != 0,
+                              blockIdx.x, blockIdx.y, gridDim.y);
     __syncthreads();  // the next group reuses red and xst
   }
   if (gridDim.y > 1) split_finish<kP>(ws, counters, blockIdx.x, gridDim.y, N, all, y, yf);
@@ -678,14 +672,15 @@ __global__ __launch_bounds__(256) void gemv_escalate_grouped_kernel(const rq_gem
   const bool staged = K <= kGroupStageElems;
   int tok[kEscTokens];
   for (int nt; (nt = next_group(fmask, tok)) > 0;) {
-    if (staged) stage_x(xst, x, K, tok, nt, 0, K >> 5);
     uint4* xs = staged ? xst : nullptr;
     if (p->y_f32 != nullptr)
       gemv_tile<kEscTokens, kLo>(x, B, K, (int)p->N, p->w_hi, p->w_lo, p->scales_tiled, tok, nt,
-                                 static_cast<uint16_t*>(p->y_bf16), p->y_f32, nullptr, red, xs, (int)tile, 0, 1);
+                                 static_cast<uint16_t*>(p->y_bf16), p->y_f32, nullptr, red, xs, staged, (int)tile, 0,
+                                 1);
     else
       gemv_tile<kEscTokens, kHiLo>(x, B, K, (int)p->N, p->w_hi, p->w_lo, p->scales_tiled, tok, nt,
-                                   static_cast<uint16_t*>(p->y_bf16), nullptr, nullptr, red, xs, (int)tile, 0, 1);
+                                   static_cast<uint16_t*>(p->y_bf16), nullptr, nullptr, red, xs, staged, (int)tile,
+                                   0, 1);
     __syncthreads();  // the next group reuses red and xst
   }
 }
