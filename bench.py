@@ -203,9 +203,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run plain 256 MiB device copies (the reference for HBM byte counters)")
-    ap.add_argument("--only", choices=["square", "gemv"],
-                    help="run only one group of rows (4096^3 GEMMs and the ARC front end, or the nibble GEMV "
-                         "kernels without the escalation gate) "
+    ap.add_argument("--only", choices=["square", "gemv", "ksweep"],
+                    help="run only one group of rows (4096^3 GEMMs and the ARC front end, the nibble GEMV "
+                         "kernels without the escalation gate, or the exact MXFP8 GEMM's K sweep) "
                          "and print them; for profiling runs")
     ap.add_argument("--traffic-from", metavar="DIR",
                     help="write the traffic summary from rocprofv3 --pmc CSV runs under DIR (pmc_main_FETCH_SIZE, "
@@ -235,6 +235,8 @@ def main():
         to_dev_only = (lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev))
         if args.only == "square":
             out = measure_square(torch, api, L, W, to_dev_only, dev)
+        elif args.only == "ksweep":
+            out = {"mxfp8_exact_gemm_k_sweep_4096x4096": measure_ksweep(torch, np, api, L, W, to_dev_only, dev)}
         else:
             out = measure_gemv(torch, np, api, L, W, dev, gate=False)
         print(json.dumps(out), flush=True)
@@ -391,6 +393,7 @@ def measure_rows(torch, np, api, L, W, to_dev, dev):
 
     # ---- 4096^3: plain MXFP4, ARC (K' = 4224), BF16; quantization bandwidth; ARC front end
     rows.update(measure_square(torch, api, L, W, to_dev, dev))
+    rows["mxfp8_exact_gemm_k_sweep_4096x4096"] = measure_ksweep(torch, np, api, L, W, to_dev, dev)
 
     # ---- recurrent prefill, 4096 x 2048, FFN 5632, 8 steps
     rows.update(measure_ramp(torch, api, L, W, to_dev, dev, time_calls))
@@ -458,6 +461,38 @@ def measure_square(torch, api, L, W, to_dev, dev):
     del a, w, pc, ps, qc, qs, y, w_aug, wsp
 
     return rows
+
+
+def measure_ksweep(torch, np, api, L, W, to_dev, dev):
+    """The exact MXFP8 GEMM at 4096 x 4096 x K for K = 1024 .. 8192 (the qkv
+    group's seeded operands repeated along K), and the least-squares line
+    t = fixed + K / rate through the four times: the per-launch cost that
+    does not grow with K (pipeline fill, the output write, launch) and the
+    steady-state rate of the K loop."""
+    g = W.c2_layer(M=4096)[0]
+    a0, w0 = g["a"], g["w"]
+    M, N = a0.shape[0], w0.shape[0]
+    ks, ts, out = [], [], {}
+    for rep in (1, 2, 4, 8):
+        K = a0.shape[1] * rep
+        a = to_dev(np.tile(a0, (1, rep)))
+        w = to_dev(np.tile(w0, (1, rep)))
+        ac, as_ = api.quantize(a, L.RQ_MXFP8)
+        wc, ws = api.quantize(w, L.RQ_MXFP8)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ms = time_calls(torch, lambda: L.rq_gemm(L.RQ_MXFP8, ac, as_, wc, ws, M, N, K, 0, y), 20)
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        out[f"k{K}"] = {"us": round(ms * 1e3, 1), "tflops": round(tf, 1),
+                        "frac_bf16_peak": round(tf * 1e12 / PEAK["bf16"], 4)}
+        ks.append(K)
+        ts.append(ms * 1e3)
+        del a, w, ac, as_, wc, ws, y
+    slope, fixed = np.polyfit(np.array(ks, float), np.array(ts, float), 1)
+    rate = 2.0 * M * N / (slope * 1e-6) / 1e12  # TFLOP/s of the K loop
+    out["fit"] = {"fixed_us": round(float(fixed), 1), "steady_tflops": round(float(rate), 1),
+                  "steady_frac_bf16_peak": round(float(rate) * 1e12 / PEAK["bf16"], 4)}
+    log(f"rows: exact MXFP8 K sweep {[round(t, 1) for t in ts]} us, fixed {fixed:.1f} us, steady {rate:.0f} TF")
+    return out
 
 
 def measure_front_end(torch, api, L, a, w, qc, qs, dev, time_calls):
