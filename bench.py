@@ -752,6 +752,10 @@ def measure_gemv(torch, np, api, L, W, dev, gate=True):
         planes.append((N, K, api.pack_nibble_planes(q, s)))
         del q, s
     ys = {N: torch.empty((B, N), dtype=torch.int16, device=dev) for _, _, N in lins}
+    out["gemv_inputs"] = ("int8 weights, FP16 scales and x drawn on the GPU by torch's generator (seed 20261208) "
+                          "with the config-5 recipe (w ~ N(0, 0.02^2), per-32 scales amax/127, x ~ N(0, 1)), "
+                          "not the seeded NumPy streams the parity tests use; flags from the seeded permutation "
+                          "(2 of 16 tokens)")
     # one split-K workspace, large enough for every shape (launches are stream-ordered)
     wsb = max(L.rq_gemv_workspace_bytes(B, N, K) for _, K, N in lins)
     wsp = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)  # arrival counters start at zero
