@@ -736,6 +736,10 @@ def gpu_int8_weights(torch, gen, N, K, dev):
     return q, s.view(torch.int16)
 
 
+GROUPED_NOTE = ("upper bound for a decode: the 197 linears in one launch treat their inputs as independent; "
+                "a model runs its layers in order (the layer-ordered rows)")
+
+
 def measure_gemv(torch, np, api, L, W, dev, gate=True):
     out = {}
     B = 16
@@ -867,10 +871,11 @@ def measure_gemv(torch, np, api, L, W, dev, gate=True):
     out["gemv_full_sweep_197_linears_low_pass_b16_grouped"] = {
         "us": round(ms_low_grp * 1e3, 1), "gb_s": round(tot_low / (ms_low_grp * 1e-3) / 1e9, 1),
         "frac_hbm": round(tot_low / (ms_low_grp * 1e-3) / PEAK["hbm"], 4), "bytes": tot_low,
-        "launches": 1, "tiles": table[2]}
+        "launches": 1, "tiles": table[2], "bound": GROUPED_NOTE}
     out["gemv_full_sweep_escalation_2_of_16_grouped"] = {
         "us": round(ms_esc_grp * 1e3, 1), "gb_s": round(tot_esc / (ms_esc_grp * 1e-3) / 1e9, 1),
-        "frac_hbm": round(tot_esc / (ms_esc_grp * 1e-3) / PEAK["hbm"], 4), "bytes": tot_esc}
+        "frac_hbm": round(tot_esc / (ms_esc_grp * 1e-3) / PEAK["hbm"], 4), "bytes": tot_esc,
+        "bound": GROUPED_NOTE}
     del table
     # grouped, through the FP32 carries: the escalation reads only the lo planes
     carries = [torch.empty((B, N), dtype=torch.float32, device=dev) for N, _, _ in planes]
@@ -881,10 +886,12 @@ def measure_gemv(torch, np, api, L, W, dev, gate=True):
     ms_esc_lo = time_calls(torch, lambda: api.gemv_nibble_escalate_grouped(table, B, flags, L.RQ_ESCALATE), 10)
     out["gemv_full_sweep_197_linears_low_pass_b16_grouped_with_carry"] = {
         "us": round(ms_low_c * 1e3, 1), "gb_s": round(tot_low_c / (ms_low_c * 1e-3) / 1e9, 1),
-        "frac_hbm": round(tot_low_c / (ms_low_c * 1e-3) / PEAK["hbm"], 4), "bytes": tot_low_c}
+        "frac_hbm": round(tot_low_c / (ms_low_c * 1e-3) / PEAK["hbm"], 4), "bytes": tot_low_c,
+        "bound": GROUPED_NOTE}
     out["gemv_full_sweep_escalation_2_of_16_grouped_lo_plane_from_carry"] = {
         "us": round(ms_esc_lo * 1e3, 1), "gb_s": round(tot_esc_lo / (ms_esc_lo * 1e-3) / 1e9, 1),
-        "frac_hbm": round(tot_esc_lo / (ms_esc_lo * 1e-3) / PEAK["hbm"], 4), "bytes": tot_esc_lo}
+        "frac_hbm": round(tot_esc_lo / (ms_esc_lo * 1e-3) / PEAK["hbm"], 4), "bytes": tot_esc_lo,
+        "bound": GROUPED_NOTE}
     del table, gys, carries
     out.update(measure_decode_layer_ordered(torch, api, L, W, dev, gen, xs, flags, planes[-1], low_bytes, esc_bytes))
     out["gemv_full_sweep_197_linears_low_pass_b16"] = {
