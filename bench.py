@@ -640,9 +640,13 @@ def measure_ramp(torch, api, L, W, to_dev, dev, time_calls):
     wsp8 = torch.empty(wsb8, dtype=torch.uint8, device=dev)
     r32 = {}
     finals = {}
-    for name, sched in (("all_bf16", 0), ("steps1_24_mxfp8", (1 << 24) - 1), ("uniform_mxfp8", (1 << 32) - 1)):
-        def run32(sched=sched):
-            L.rq_recurrent_prefill(h, S, D, F, w1, w2, w1q8[0], w1q8[1], w2q8[0], w2q8[1], L.RQ_MXFP8, sched, 32,
+    # MXFP8 steps with exact block-scaled GEMMs (BF16 MFMAs) and on the FP8 scaled instruction
+    for name, sched, gf in (("all_bf16", 0, L.RQ_MXFP8), ("steps1_24_mxfp8", (1 << 24) - 1, L.RQ_MXFP8),
+                            ("uniform_mxfp8", (1 << 32) - 1, L.RQ_MXFP8),
+                            ("steps1_24_mxfp8_fp8_instruction", (1 << 24) - 1, L.RQ_MXFP8_F8MFMA),
+                            ("uniform_mxfp8_fp8_instruction", (1 << 32) - 1, L.RQ_MXFP8_F8MFMA)):
+        def run32(sched=sched, gf=gf):
+            L.rq_recurrent_prefill(h, S, D, F, w1, w2, w1q8[0], w1q8[1], w2q8[0], w2q8[1], gf, sched, 32,
                                    1e-6, wsp8, wsb8)
         ms = time_calls(torch, run32, 3, warmup=1, before=lambda: h.copy_(h0))
         h.copy_(h0)
@@ -653,6 +657,8 @@ def measure_ramp(torch, api, L, W, to_dev, dev, time_calls):
         r32[name]["final_state_rel_err_vs_all_bf16"] = float((finals[name] - finals["all_bf16"]).norm()
                                                              / finals["all_bf16"].norm())
     r32["speedup_vs_all_bf16"] = round(r32["all_bf16"]["ms"] / r32["steps1_24_mxfp8"]["ms"], 4)
+    r32["speedup_vs_all_bf16_fp8_instruction"] = round(
+        r32["all_bf16"]["ms"] / r32["steps1_24_mxfp8_fp8_instruction"]["ms"], 4)
     out["recurrent_prefill_4096x2048_ffn5632_t32_k24_mxfp8"] = r32
     log(f"rows: RAMP T=32 K=24 MXFP8 {r32}")
     del h0, w1, w2, wsp, h, w1q8, w2q8, wsp8, finals

@@ -238,7 +238,8 @@ rq_status rq_recurrent_prefill(void* h_bf16, int64_t S, int64_t D, int64_t F, co
                                void* workspace, size_t ws_bytes, void* stream) {
   if (!have(h_bf16, S == 0) || !have(workspace, S == 0))
     return fail(RQ_EINVAL, "rq_recurrent_prefill: null h or workspace");
-  if (fmt != RQ_MXFP4 && fmt != RQ_MXFP8) return fail(RQ_EINVAL, "rq_recurrent_prefill: fmt must be MXFP4 or MXFP8");
+  if (fmt != RQ_MXFP4 && fmt != RQ_MXFP8 && fmt != RQ_MXFP8_F8MFMA)
+    return fail(RQ_EINVAL, "rq_recurrent_prefill: fmt must be RQ_MXFP4, RQ_MXFP8 or RQ_MXFP8_F8MFMA");
   if (steps < 1 || steps > 64) return fail(RQ_ESHAPE, "rq_recurrent_prefill: steps must be in [1, 64]");
   const uint64_t used = steps == 64 ? ~0ull : ((1ull << steps) - 1);
   const bool any_q = (schedule & used) != 0, any_bf16 = (~schedule & used) != 0;
@@ -264,6 +265,8 @@ rq_status rq_recurrent_prefill(void* h_bf16, int64_t S, int64_t D, int64_t F, co
   uint8_t* u_sc = u_codes + round256(sz * fz);
   uint16_t* h = static_cast<uint16_t*>(h_bf16);
   hipStream_t st = as_stream(stream);
+  // the codes n and u are quantized to (MXFP8 for both MXFP8 GEMM forms)
+  const int qfmt = fmt == RQ_MXFP8_F8MFMA ? RQ_MXFP8 : fmt;
   // shapes the pipelined GEMM takes quantize u in W1's epilogue (the same
   // codes as the separate pass); the others go through u in BF16
   const bool fused_u = rq::gemm_pipe_supported(fmt, S, F, D);
@@ -271,7 +274,7 @@ rq_status rq_recurrent_prefill(void* h_bf16, int64_t S, int64_t D, int64_t F, co
     const bool q = (schedule >> (t - 1)) & 1ull;
     hipError_t e;
     if (q) {
-      e = rq::launch_rmsnorm(fmt, h, S, D, eps, n_buf, n_sc, st);
+      e = rq::launch_rmsnorm(qfmt, h, S, D, eps, n_buf, n_sc, st);
       if (e == hipSuccess) {
         if (fused_u) {
           // SiLU and the block quantization of u in W1's epilogue
@@ -279,8 +282,8 @@ rq_status rq_recurrent_prefill(void* h_bf16, int64_t S, int64_t D, int64_t F, co
         } else {
           e = rq::launch_gemm(fmt, rq::kEpiSiluBf16, n_buf, n_sc, w1_q, w1_s, S, F, D, u_buf, st);
           if (e == hipSuccess)
-            e = rq::launch_quant_rows(fmt, reinterpret_cast<const uint16_t*>(u_buf), S, F, u_codes, u_sc,
-                                      code_row_bytes(fmt, F), F / 32, st);
+            e = rq::launch_quant_rows(qfmt, reinterpret_cast<const uint16_t*>(u_buf), S, F, u_codes, u_sc,
+                                      code_row_bytes(qfmt, F), F / 32, st);
         }
       }
       if (e == hipSuccess) e = rq::launch_gemm(fmt, rq::kEpiResAddBf16, u_codes, u_sc, w2_q, w2_s, S, D, F, h, st);

@@ -112,6 +112,10 @@ def test_recurrent_prefill_validation():
     allq[4] = allq[5] = None
     allq[11] = 0b1111  # every step quantized: BF16 weights not needed
     assert status_of(rq.rq_recurrent_prefill, *allq) in (L.RQ_OK, L.RQ_ENODEV)
+    for fmt, want in ((L.RQ_MXFP8_F8MFMA, (L.RQ_OK, L.RQ_ENODEV)), (L.RQ_BF16, (L.RQ_EINVAL,)), (7, (L.RQ_EINVAL,))):
+        f = list(args)
+        f[10] = fmt
+        assert status_of(rq.rq_recurrent_prefill, *f) in want, fmt
 
 
 def test_gemv_and_gate_validation():

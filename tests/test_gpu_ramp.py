@@ -10,9 +10,11 @@ import torch
 from mixed_precision_block_amd import api
 from mixed_precision_block_amd import _lib as L
 from oracle import formats as F
+from oracle import quant as Q
 from oracle import ramp as R
 from synthetic import workloads as W
 from tests import _golden as gold
+from tests import f8mfma_model as FM
 from tests.gpu_util import dev_bf16, host_bits, log, rel_fro
 
 pytestmark = pytest.mark.gpu
@@ -20,13 +22,15 @@ pytestmark = pytest.mark.gpu
 FMT = {F.FMT_MXFP4: L.RQ_MXFP4, F.FMT_MXFP8: L.RQ_MXFP8}
 
 
-def gpu_prefill(h0, w1, w2, schedule, steps, ofmt, eps=1e-6):
+def gpu_prefill(h0, w1, w2, schedule, steps, ofmt, eps=1e-6, gemm_fmt=None):
+    """gemm_fmt: the prefill's fmt when it differs from the code format
+    (RQ_MXFP8_F8MFMA: MXFP8 codes, GEMMs on the FP8 scaled instruction)."""
     fmt = FMT[ofmt]
     w1d, w2d = dev_bf16(w1), dev_bf16(w2)
     w1q = api.quantize(w1d, fmt)
     w2q = api.quantize(w2d, fmt)
     h = dev_bf16(h0)
-    api.recurrent_prefill(h, w1d, w2d, w1q, w2q, fmt, schedule, steps, eps)
+    api.recurrent_prefill(h, w1d, w2d, w1q, w2q, fmt if gemm_fmt is None else gemm_fmt, schedule, steps, eps)
     return host_bits(h)
 
 
@@ -56,15 +60,48 @@ def test_worked_steps():
 SCHEDULES = {"all_bf16": 0x00, "ramp_1_6": 0x3F, "uniform": 0xFF, "early_bf16": 0xFC}
 
 
-@pytest.mark.parametrize("ofmt", [F.FMT_MXFP4, F.FMT_MXFP8])
-def test_small_schedules_against_oracle(ofmt):
+def ramp_prefill_f8_instruction(h0, w1, w2, schedule, steps):
+    """The oracle's recurrence (its RMSNorm, SiLU, BF16 rounding and MXFP8
+    block quantization) with each quantized step's two GEMMs taken by the
+    model of the FP8 scaled instruction instead of the exact block-scaled
+    sum: the reference for rq_recurrent_prefill(RQ_MXFP8_F8MFMA).  A step's
+    truncated products change a few BF16 roundings and MXFP8 codes, and the
+    recurrence carries those changes on, so the trajectory is compared with
+    this model's rather than with the exact one's."""
+    w1c, w1s = Q.quantize_mx(w1, F.FMT_MXFP8)
+    w2c, w2s = Q.quantize_mx(w2, F.FMT_MXFP8)
+    h = np.asarray(h0, dtype=np.uint16)
+    for t in range(1, steps + 1):
+        if not R.step_is_quantized(schedule, t):
+            h = R.ramp_step(h, w1, w2, False)
+            continue
+        n_bits = F.f64_to_bf16(R.rmsnorm(F.bf16_to_f64(h)))
+        nc, ns = Q.quantize_mx(n_bits, F.FMT_MXFP8)
+        z_bits = F.f64_to_bf16(FM.gemm_f8mfma(nc, ns, w1c, w1s))
+        u_bits = F.f64_to_bf16(R.silu(F.bf16_to_f64(z_bits)))
+        uc, us = Q.quantize_mx(u_bits, F.FMT_MXFP8)
+        v_bits = F.f64_to_bf16(FM.gemm_f8mfma(uc, us, w2c, w2s))
+        h = F.f64_to_bf16(F.bf16_to_f64(h) + F.bf16_to_f64(v_bits))
+    return h
+
+
+@pytest.mark.parametrize("ofmt,gemm_fmt", [(F.FMT_MXFP4, None), (F.FMT_MXFP8, None),
+                                           (F.FMT_MXFP8, L.RQ_MXFP8_F8MFMA)])
+def test_small_schedules_against_oracle(ofmt, gemm_fmt):
+    """Against the oracle's trajectory at 0.1 x the schedule's own error
+    (distance from all-BF16); the FP8 instruction's schedule against the
+    oracle's recurrence with the instruction's GEMM model."""
     d = W.c4_ramp(S=96, D=256, F=704)
     ref_bf16 = R.ramp_prefill(d["h0"], d["w1"], d["w2"], 0, 8, ofmt)
+    f8 = gemm_fmt == L.RQ_MXFP8_F8MFMA
     for name, sched in SCHEDULES.items():
-        if ofmt == F.FMT_MXFP8 and name not in ("ramp_1_6", "uniform"):
+        if ofmt == F.FMT_MXFP8 and name not in (("ramp_1_6",) if f8 else ("ramp_1_6", "uniform")):
             continue
-        g = gpu_prefill(d["h0"], d["w1"], d["w2"], sched, 8, ofmt)
-        o = R.ramp_prefill(d["h0"], d["w1"], d["w2"], sched, 8, ofmt)
+        g = gpu_prefill(d["h0"], d["w1"], d["w2"], sched, 8, ofmt, gemm_fmt=gemm_fmt)
+        if f8:
+            o = ramp_prefill_f8_instruction(d["h0"], d["w1"], d["w2"], sched, 8)
+        else:
+            o = R.ramp_prefill(d["h0"], d["w1"], d["w2"], sched, 8, ofmt)
         err_sched = R.hidden_relative_error(o, ref_bf16)
         err_gpu = rel_fro(F.bf16_to_f64(g), F.bf16_to_f64(o))
         tol = max(1e-3, 0.1 * err_sched)
