@@ -728,13 +728,21 @@ hipError_t launch_pack_nibble_planes(const int8_t* w, const uint16_t* scales, in
 static int gemv_tb(int64_t B) { return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B <= 8 ? 8 : 16; }
 
 // K slices per row tile: one when the row tiles alone give 256 workgroups,
-// else enough for about 512 workgroups, each keeping at least one block
-// per wave, and at most kMaxSlices (the partials the last arriver of a
-// tile loads at once).
-int gemv_slices(int64_t N, int64_t K) {
+// else enough for about `target` workgroups, each keeping at least one
+// block per wave, and at most kMaxSlices (the partials the last arriver of
+// a tile loads at once).  Every split launch pays one cross-workgroup
+// arrival, whatever its slice count, so the count trades that against each
+// workgroup's share of the work: the low pass (16 tokens of dot products
+// per weight) aims at 1024 workgroups, the escalation (the few flagged
+// tokens) at 128 -- the fastest of 64 .. 2048 for each on a decode step of
+// the Qwen3-0.6B shapes in layer order.  The workspace is sized for the
+// low pass, the larger count.
+constexpr int64_t kLowTarget = 1024, kEscTarget = 128;
+
+static int gemv_slices(int64_t N, int64_t K, int64_t target) {
   const int64_t tiles = (N + 63) / 64, nb = K / 32;
   if (tiles == 0 || tiles >= 256) return 1;
-  int64_t s = (512 + tiles - 1) / tiles;
+  int64_t s = (target + tiles - 1) / tiles;
   int64_t cap = nb / 4 > 1 ? nb / 4 : 1;
   if (cap > kMaxSlices) cap = kMaxSlices;
   return (int)(s < cap ? s : cap);
@@ -748,12 +756,14 @@ constexpr size_t kCounterBytes = 256 * sizeof(uint32_t);
 
 size_t gemv_workspace_bytes(int64_t B, int64_t N, int64_t K) {
   (void)B;
-  const int s = gemv_slices(N, K);
+  const int s = gemv_slices(N, K, kLowTarget);
   return s > 1 ? kCounterBytes + (size_t)s * kWsTokens * ((N + 63) / 64 * 64) * sizeof(float) : 0;
 }
 
-static int slices_for(int64_t B, int64_t N, int64_t K, size_t ws_bytes) {
-  const int s = gemv_slices(N, K);
+// The slices of a pass: split only with a workspace of the full size (the
+// escalation's count never exceeds the low pass's, which sizes it).
+static int slices_for(int64_t B, int64_t N, int64_t K, size_t ws_bytes, int64_t target) {
+  const int s = gemv_slices(N, K, target);
   return (s > 1 && ws_bytes >= gemv_workspace_bytes(B, N, K)) ? s : 1;
 }
 
@@ -762,7 +772,7 @@ hipError_t launch_gemv_low(const uint16_t* x, int64_t B, int64_t K, int64_t N, c
                            hipStream_t stream) {
   const unsigned tiles = (unsigned)((N + 63) / 64);
   if (tiles == 0) return hipSuccess;
-  const int ns = slices_for(B, N, K, ws_bytes);
+  const int ns = slices_for(B, N, K, ws_bytes, kLowTarget);
   const dim3 grid(tiles, ns);
   const int b = (int)B, k = (int)K, n = (int)N;
   uint32_t* cnt = static_cast<uint32_t*>(ws);
@@ -782,7 +792,7 @@ hipError_t launch_gemv_escalate(const uint16_t* x, int64_t B, int64_t K, int64_t
                                 float* yf, void* ws, size_t ws_bytes, hipStream_t stream) {
   const unsigned tiles = (unsigned)((N + 63) / 64);
   if (tiles == 0) return hipSuccess;
-  const int ns = slices_for(B, N, K, ws_bytes);
+  const int ns = slices_for(B, N, K, ws_bytes, kEscTarget);
   const int b = (int)B, k = (int)K, n = (int)N;
   if (ns == 1 && tiles >= 2048) {
     // enough tiles for one wave each: no cross-wave reduction
