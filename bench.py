@@ -12,19 +12,25 @@ quantized once and stacked along N.  value = GEMM FLOP per step (128.85
 GFLOP, all seven linears) / wall time per step, in TFLOP/s, inputs resident
 in HBM.
 
-`roofline` covers the dominant kernel (the MXFP8 GEMM): algorithmic FLOP
-(2 M N K per launch) over its average launch time, from HIP events around
-back-to-back launches of each of the step's four GEMMs on the same inputs,
-averaged over the four; `traffic` is the HBM bytes per launch from the
-committed counter summary (write it with --traffic-from).  `rows` measures the other
-steps of the path on their own workloads: single MXFP4 GEMM (128 x 1024 x
-1024), 4096^3 MXFP4 plain / ARC (K' = 4224) / BF16, quantization bandwidth,
-the recurrent prefill (8 steps, RAMP vs all-BF16) and the nibble GEMV
-(LM head, full 28-layer sweep, escalation).  `cpu_baseline` times the CPU
-oracle on a bounded sample of the main workload.
+`roofline` covers the dominant kernel (the exact MXFP8 GEMM, which runs on
+BF16 MFMAs, so its peak is the BF16 one): algorithmic FLOP (2 M N K per
+launch) over its average launch time, from HIP events around back-to-back
+launches of each of the step's four GEMMs on the same inputs, averaged over
+the four; `traffic` is the HBM bytes per launch from the committed counter
+summary (write it with --traffic-from).  The same GEMMs on the FP8 scaled
+instruction and both paths' distance from the oracle are reported beside
+it.  `rows` measures the other steps of the path on their own workloads:
+single MXFP4 GEMM (128 x 1024 x 1024), 4096^3 MXFP4 plain / ARC (K' =
+4224) / BF16, the exact MXFP8 GEMM's K sweep, quantization bandwidth, the
+recurrent prefill (8 steps, RAMP vs all-BF16; 32 steps with 24 in MXFP8)
+and the nibble GEMV (LM head, the 28-layer sweep grouped and in layer
+order, escalation, gate).  `cpu_baseline` times the CPU oracle on a bounded
+sample of the main workload.
 
     python bench.py [--steps K] [--warmup W] [--no-rows] [--no-cpu-baseline]
+    python bench.py --only square|gemv|ksweep   # one group of rows, for profiling
     python bench.py --traffic-from gpurun_out   # after the --pmc runs
+
 """
 
 import argparse

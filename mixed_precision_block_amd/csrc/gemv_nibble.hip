@@ -248,7 +248,7 @@ __device__ __forceinline__ void gemv_tile(const uint16_t* __restrict__ x, int B,
 // counter is bumped, so the last arriver's device-scope loads see every
 // slice.  Every thread of the workgroup calls it; nothing waits on another
 // workgroup.
-template <int kP, int R = 1>
+template <int kP>
 __device__ __forceinline__ void split_finish(const float* __restrict__ ws, uint32_t* __restrict__ counters, int tile,
                                              int nslice, int N, uint32_t tmask, uint16_t* __restrict__ y,
                                              float* __restrict__ yf) {
@@ -261,39 +261,33 @@ __device__ __forceinline__ void split_finish(const float* __restrict__ ws, uint3
   }
   __syncthreads();
   if (!last) return;
-  const int ntiles = (N + 63) >> 6;
+  // every partial this thread adds is loaded first (the loads overlap; a
+  // slot past the tile's slices reloads the last slice, always in bounds),
+  // then each output sums its slices in order
+  constexpr int kPer = kWsTokens * 64 / 256;  // outputs per thread
+  float part[kPer][kMaxSlices];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int t64 = tile * R + r;  // 64-row tile of the partials
-    if (t64 >= ntiles) break;
-    // every partial this thread adds is loaded first (the loads overlap; a
-    // slot past the tile's slices reloads the last slice, always in
-    // bounds), then each output sums its slices in order
-    constexpr int kPer = kWsTokens * 64 / 256;  // outputs per thread
-    float part[kPer][kMaxSlices];
+  for (int j = 0; j < kPer; ++j) {
+    const int o = threadIdx.x + 256 * j, t = o >> 6, l = o & 63;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int o = threadIdx.x + 256 * j, t = o >> 6, l = o & 63;
-#pragma unroll
-      for (int sl = 0; sl < kMaxSlices; ++sl) {
-        const int sc = sl < nslice ? sl : nslice - 1;
-        part[j][sl] = __hip_atomic_load(ws + (((size_t)t64 * nslice + sc) * kWsTokens + t) * 64 + l,
-                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+    for (int sl = 0; sl < kMaxSlices; ++sl) {
+      const int sc = sl < nslice ? sl : nslice - 1;
+      part[j][sl] = __hip_atomic_load(ws + (((size_t)tile * nslice + sc) * kWsTokens + t) * 64 + l,
+                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+  }
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int o = threadIdx.x + 256 * j, t = o >> 6, l = o & 63;
-      const int n = t64 * 64 + l;
-      if (!((tmask >> t) & 1u) || n >= N) continue;
-      const size_t i = (size_t)t * N + n;
-      float v = kP == kLo ? yf[i] : 0.0f;
+  for (int j = 0; j < kPer; ++j) {
+    const int o = threadIdx.x + 256 * j, t = o >> 6, l = o & 63;
+    const int n = tile * 64 + l;
+    if (!((tmask >> t) & 1u) || n >= N) continue;
+    const size_t i = (size_t)t * N + n;
+    float v = kP == kLo ? yf[i] : 0.0f;
 #pragma unroll
-      for (int sl = 0; sl < kMaxSlices; ++sl)
-        if (sl < nslice) v += part[j][sl];
-      if (kP == kHi && yf != nullptr) yf[i] = v;
-      y[i] = (uint16_t)f32_to_bf16(v);
-    }
+    for (int sl = 0; sl < kMaxSlices; ++sl)
+      if (sl < nslice) v += part[j][sl];
+    if (kP == kHi && yf != nullptr) yf[i] = v;
+    y[i] = (uint16_t)f32_to_bf16(v);
   }
   if (threadIdx.x == 0) __hip_atomic_store(counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
