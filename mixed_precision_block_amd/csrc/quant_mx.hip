@@ -313,18 +313,28 @@ __global__ __launch_bounds__(256) void channel_amax_kernel(const uint16_t* __res
 
 static inline unsigned grid_for(int64_t threads) { return (unsigned)((threads + 255) / 256); }
 
-hipError_t launch_quant_rows(int fmt, const uint16_t* x, int64_t rows, int64_t K, uint8_t* codes,
-                             uint8_t* scales, int64_t ldc, int64_t lds, hipStream_t stream) {
-  if (rows == 0 || K == 0) return hipSuccess;
-  const int64_t segs = (K / 8 + 63) / 64, units = rows * segs;
-  if (units > 0x7FFFFFFFll || rows > 0xFFFFFFFFll) return hipErrorInvalidValue;
-  constexpr int U = 2;  // segments per wave (1, 2, 4 and 8 measured; 2 is best from 4096 x 1024 to x 3072)
+template <int U>
+static hipError_t launch_quant_rows_u(int fmt, const uint16_t* x, int64_t rows, int64_t K, int64_t segs,
+                                      int64_t units, uint8_t* codes, uint8_t* scales, int64_t ldc, int64_t lds,
+                                      hipStream_t stream) {
   const unsigned g = (unsigned)((units + 4 * U - 1) / (4 * U));
   if (fmt == 1)
     quant_rows_kernel<FmtE2M1, U><<<g, 256, 0, stream>>>(x, (uint32_t)rows, K, (uint32_t)segs, codes, scales, ldc, lds);
   else
     quant_rows_kernel<FmtE4M3, U><<<g, 256, 0, stream>>>(x, (uint32_t)rows, K, (uint32_t)segs, codes, scales, ldc, lds);
   return hipGetLastError();
+}
+
+hipError_t launch_quant_rows(int fmt, const uint16_t* x, int64_t rows, int64_t K, uint8_t* codes,
+                             uint8_t* scales, int64_t ldc, int64_t lds, hipStream_t stream) {
+  if (rows == 0 || K == 0) return hipSuccess;
+  const int64_t segs = (K / 8 + 63) / 64, units = rows * segs;
+  if (units > 0x7FFFFFFFll || rows > 0xFFFFFFFFll) return hipErrorInvalidValue;
+  // segments per wave: 2 up to 4096 x 3072 (1, 2, 4 and 8 measured on
+  // 4096 x 1024 .. 3072), 4 from 32768 segments on (4096 x 4096 MXFP4:
+  // 8.0 -> 7.1 us; 8 gave 7.9 us)
+  if (units >= 32768) return launch_quant_rows_u<4>(fmt, x, rows, K, segs, units, codes, scales, ldc, lds, stream);
+  return launch_quant_rows_u<2>(fmt, x, rows, K, segs, units, codes, scales, ldc, lds, stream);
 }
 
 hipError_t launch_quant_append(int fmt, int mode, const uint16_t* x, int64_t rows, int64_t K,
