@@ -102,108 +102,139 @@ __global__ __launch_bounds__(256) void quant_append_kernel(const uint16_t* __res
 // Primary quantization plus the appended columns in one pass over each row
 // (the gather form of the ARC activations and weights: primary blocks in
 // the original channel order, appended block j / 32 from channel idx[j]).
-// A workgroup owns a run of rows; thread t owns chunks c = t + 256 i
-// (i < CPT) of every row and encodes them from its registers, as
-// quant_rows_kernel does.  It parks in LDS what the appended columns take
-// from its chunk: RESIDUAL the residual of every element against the code
-// just made (residual8), COPY the values themselves.  Threads t < S / 8
-// then gather their appended chunk from LDS and encode it.  The next row's
-// loads go out before the current row is encoded.  idx entries outside
-// [0, K) read as 0.
-template <class Fmt, bool kResidual, int CPT>
+// A workgroup owns R consecutive rows and loads all of them before it
+// encodes any (thread t holds chunks c = t + 256 i, i < CPT, of each row),
+// together with the channel numbers of its appended tasks.  It encodes
+// every primary block from registers, as quant_rows_kernel does, and parks
+// the row's values in LDS, one buffer per row, with (RESIDUAL) the row's
+// block scale bytes.  After the one barrier, task k < R S / 8 (appended
+// chunk k mod S / 8 of row k div S / 8, taken by thread k mod 256) gathers
+// its eight channels from LDS and encodes them: COPY the values, RESIDUAL
+// each value's residual against its primary code (residual1 under its
+// block's scale byte), so residuals are formed for the S selected channels
+// only.  idx entries outside [0, K) read as 0.
+template <class Fmt, bool kResidual, int CPT, int R>
 __global__ __launch_bounds__(256) void quant_rows_append_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                                 int64_t K, const int32_t* __restrict__ idx,
                                                                 int64_t S, uint8_t* __restrict__ codes,
-                                                                uint8_t* __restrict__ scales, int rows_per_wg) {
-  extern __shared__ uint4 row_lds[];  // K / 8 chunks of BF16 (residuals or values)
+                                                                uint8_t* __restrict__ scales) {
+  // R rows of K / 8 chunks of BF16 values, then (RESIDUAL) R rows of K / 32
+  // block scale bytes
+  extern __shared__ uint4 row_lds[];
   constexpr int kElemBytesNum = Fmt::kMantBits == 1 ? 1 : 2;  // bytes per 2 elements
-  const int chunks = (int)(K >> 3), s_chunks = (int)(S >> 3);
+  constexpr int kTasks = R;  // appended tasks per thread: R S / 8 <= 256 R
+  const int chunks = (int)(K >> 3), s_chunks = (int)(S >> 3), blocks = (int)(K >> 5);
+  uint8_t* sb_lds = reinterpret_cast<uint8_t*>(row_lds + R * chunks);
   const int64_t ldc = (K + S) / 2 * kElemBytesNum, lds = (K + S) >> 5;
-  const int64_t r0 = (int64_t)blockIdx.x * rows_per_wg;
-  const int64_t r1 = min(rows, r0 + rows_per_wg);
+  const int64_t r0 = (int64_t)blockIdx.x * R;
   const uint16_t* rh = reinterpret_cast<const uint16_t*>(row_lds);
-  // this thread's appended chunk (threads below S / 8, at most 256 of them),
-  // its channels held in registers
   const int t = (int)threadIdx.x;
-  const bool app = t < s_chunks;
-  int32_t ch[8];
+  uint4 q[R][CPT];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) ch[e] = app ? idx[8 * t + e] : -1;
-  uint4 q[CPT];
-  auto load_row = [&](int64_t r) {
-    const uint4* xr = reinterpret_cast<const uint4*>(x + r * K);
+  for (int r = 0; r < R; ++r) {
+    const bool live = r0 + r < rows;
+    const uint4* xr = reinterpret_cast<const uint4*>(x + (r0 + r) * K);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = t + 256 * i;
-      q[i] = c < chunks ? xr[c] : make_uint4(0, 0, 0, 0);
+      q[r][i] = live && c < chunks ? xr[c] : make_uint4(0, 0, 0, 0);
     }
-  };
-  if (r0 < r1) load_row(r0);
-  for (int64_t row = r0; row < r1; ++row) {
-    __syncthreads();  // the previous row's appended reads are done with the LDS
-    uint4 cur[CPT];
+  }
+  int32_t ch[kTasks][8];
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) cur[i] = q[i];
-    if (row + 1 < r1) load_row(row + 1);
-    // chunks is a multiple of 4, so the four lanes of a quad (one 32-block)
-    // take the same branches
+  for (int k = 0; k < kTasks; ++k) {
+    const int task = t + 256 * k, c = task % max(s_chunks, 1);
+    const bool on = task < R * s_chunks;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ch[k][e] = on ? idx[8 * c + e] : -1;
+  }
+  // chunks is a multiple of 4, so the four lanes of a quad (one 32-block)
+  // take the same branches
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = r0 + r;
+    if (row >= rows) break;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = t + 256 * i;
       if (c >= chunks) break;
-      const uint32_t sb = (uint32_t)(mx_block_exp<Fmt>(quad_max(amax8(cur[i]))) + 127);
-      const uint2 cv = encode8<Fmt>(cur[i], sb);
+      const uint32_t sb = (uint32_t)(mx_block_exp<Fmt>(quad_max(amax8(q[r][i]))) + 127);
+      const uint2 cv = encode8<Fmt>(q[r][i], sb);
       store8<Fmt>(cv, codes + row * ldc + (int64_t)c * 4 * kElemBytesNum);
-      if ((c & 3) == 0) scales[row * lds + (c >> 2)] = (uint8_t)sb;
-      if constexpr (kResidual)
-        row_lds[c] = residual8<Fmt>(cur[i], cv, sb);
-      else
-        row_lds[c] = cur[i];
+      if ((c & 3) == 0) {
+        scales[row * lds + (c >> 2)] = (uint8_t)sb;
+        if constexpr (kResidual) sb_lds[r * blocks + (c >> 2)] = (uint8_t)sb;
+      }
+      row_lds[r * chunks + c] = q[r][i];
     }
-    __syncthreads();  // the parked row is complete
-    if (app) {  // whole quads: s_chunks is a multiple of 4
+  }
+  __syncthreads();  // every parked row is complete
+#pragma unroll
+  for (int k = 0; k < kTasks; ++k) {
+    const int task = t + 256 * k;
+    if (task >= R * s_chunks) break;
+    const int r = task / s_chunks, c = task - r * s_chunks;
+    const int64_t row = r0 + r;
+    // whole quads: s_chunks is a multiple of 4, so a quad's four tasks
+    // share the row
+    if (row < rows) {
+      const uint16_t* src = rh + (int64_t)r * K;
+      const uint8_t* sbr = sb_lds + r * blocks;
       uint32_t v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (ch[e] >= 0 && ch[e] < K) ? (uint32_t)rh[ch[e]] : 0u;
+      for (int e = 0; e < 8; ++e) {
+        const bool in = ch[k][e] >= 0 && ch[k][e] < K;
+        v[e] = in ? (uint32_t)src[ch[k][e]] : 0u;
+        if constexpr (kResidual) v[e] = in ? residual1<Fmt>(v[e], sbr[ch[k][e] >> 5]) : 0u;
+      }
       const uint4 q2 = pack8(v);
       const uint32_t sb2 = (uint32_t)(mx_block_exp<Fmt>(quad_max(amax8(q2))) + 127);
-      encode_store8<Fmt>(q2, sb2, codes + row * ldc + (K + (int64_t)t * 8) / 2 * kElemBytesNum);
-      if ((t & 3) == 0) scales[row * lds + (K >> 5) + (t >> 2)] = (uint8_t)sb2;
+      encode_store8<Fmt>(q2, sb2, codes + row * ldc + (K + (int64_t)c * 8) / 2 * kElemBytesNum);
+      if ((c & 3) == 0) scales[row * lds + (K >> 5) + (c >> 2)] = (uint8_t)sb2;
     }
   }
 }
 
 // ARCQuant fused front end (ARCQuant page, technical summary, "Kernel
-// Implementatie" with the stages of "Methodologie").  A workgroup owns
-// rows_per_wg consecutive rows and keeps its threads' perm entries in
-// registers across them; thread t owns chunks c = t + 256 i (i < CPT) of
-// every row.  Each row is staged in LDS; with kNorm its mean square is
-// summed in fp32 in the order of rmsnorm_kernel, and every element is
-// scaled by 1 / sqrt(ms + eps) and rounded to BF16 as it is gathered, so
-// the normalized values equal rmsnorm_kernel's.  The next row's loads are
-// issued before the current row is gathered.  Output position j takes
-// channel perm[j] (out-of-range entries read as 0).  Primary blocks cover
-// positions 0..K-1; the first S positions (the outlier channels after an
-// amax reorder) also fill appended block j / 32 + K / 32: the residual
-// against the primary stage (kResidual; exact, see quant_append_kernel) or
-// the value itself.
-template <class Fmt, bool kResidual, bool kNorm, int CPT>
+// Implementatie" with the stages of "Methodologie").  A workgroup owns R
+// consecutive rows and loads all of them, and its threads' perm entries,
+// before it computes anything; thread t owns chunks c = t + 256 i
+// (i < CPT) of every row.  The rows are staged in LDS, one buffer per row;
+// with kNorm each row's mean square is summed in fp32 in the order of
+// rmsnorm_kernel (lanes by butterfly, then waves 0..3), and every element
+// is scaled by 1 / sqrt(ms + eps) and rounded to BF16 as it is gathered, so
+// the normalized values equal rmsnorm_kernel's.  One barrier separates the
+// staging from the gathers.  Output position j takes channel perm[j]
+// (out-of-range entries read as 0).  Primary blocks cover positions
+// 0..K-1; the first S positions (the outlier channels after an amax
+// reorder) also fill appended block j / 32 + K / 32: the residual against
+// the primary stage (kResidual, residual8) or the value itself.
+template <class Fmt, bool kResidual, bool kNorm, int CPT, int R>
 __global__ __launch_bounds__(256) void arc_frontend_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t K,
                                                            const int32_t* __restrict__ perm, int64_t S, float eps,
-                                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                                           int rows_per_wg) {
-  extern __shared__ uint4 row_lds[];  // one row, K / 8 chunks of BF16
-  __shared__ float sh[4];
+                                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  extern __shared__ uint4 row_lds[];  // R rows of K / 8 chunks of BF16
+  __shared__ float sh[R][4];
   constexpr int kElemBytesNum = Fmt::kMantBits == 1 ? 1 : 2;  // bytes per 2 elements
   const int chunks = (int)(K >> 3), s_chunks = (int)(S >> 3);
   const int64_t ldc = (K + S) / 2 * kElemBytesNum, lds = (K + S) >> 5;
-  const int64_t r0 = (int64_t)blockIdx.x * rows_per_wg;
-  const int64_t r1 = min(rows, r0 + rows_per_wg);
+  const int64_t r0 = (int64_t)blockIdx.x * R;
+  const int t = (int)threadIdx.x;
+  uint4 q[R][CPT];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const bool live = r0 + r < rows;
+    const uint4* xr = reinterpret_cast<const uint4*>(x + (r0 + r) * K);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = t + 256 * i;
+      q[r][i] = live && c < chunks ? xr[c] : make_uint4(0, 0, 0, 0);
+    }
+  }
   int32_t p[CPT][8];
-  uint4 q[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const int c = (int)threadIdx.x + 256 * i;
+    const int c = t + 256 * i;
     int4 p0 = make_int4(-1, -1, -1, -1), p1 = p0;
     if (c < chunks) {
       p0 = reinterpret_cast<const int4*>(perm)[2 * c];
@@ -212,26 +243,16 @@ __global__ __launch_bounds__(256) void arc_frontend_kernel(const uint16_t* __res
     p[i][0] = p0.x, p[i][1] = p0.y, p[i][2] = p0.z, p[i][3] = p0.w;
     p[i][4] = p1.x, p[i][5] = p1.y, p[i][6] = p1.z, p[i][7] = p1.w;
   }
-  auto load_row = [&](int64_t r) {
-    const uint4* xr = reinterpret_cast<const uint4*>(x + r * K);
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = (int)threadIdx.x + 256 * i;
-      q[i] = c < chunks ? xr[c] : make_uint4(0, 0, 0, 0);
-    }
-  };
-  if (r0 < r1) load_row(r0);
-  const uint16_t* rh = reinterpret_cast<const uint16_t*>(row_lds);
-  for (int64_t row = r0; row < r1; ++row) {
-    __syncthreads();  // the previous row's gathers are done with row_lds
+  for (int r = 0; r < R; ++r) {
     float ss = 0.0f;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = (int)threadIdx.x + 256 * i;
+      const int c = t + 256 * i;
       if (c >= chunks) break;
-      row_lds[c] = q[i];
+      row_lds[r * chunks + c] = q[r][i];
       if constexpr (kNorm) {
-        const uint32_t w[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
+        const uint32_t w[4] = {q[r][i].x, q[r][i].y, q[r][i].z, q[r][i].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float a = bf16_to_f32(w[e] & 0xFFFFu), b = bf16_to_f32(w[e] >> 16);
@@ -240,53 +261,42 @@ __global__ __launch_bounds__(256) void arc_frontend_kernel(const uint16_t* __res
         }
       }
     }
+    if constexpr (kNorm) {
+      ss = wave_sum(ss);
+      if ((t & 63) == 0) sh[r][t >> 6] = ss;
+    }
+  }
+  __syncthreads();  // the staged rows and their partial sums are published
+  // chunks and s_chunks are multiples of 4, so the four lanes of a quad
+  // (one 32-block) take the same branches
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = r0 + r;
+    if (row >= rows) break;
+    const uint16_t* rh = reinterpret_cast<const uint16_t*>(row_lds) + (int64_t)r * K;
     float inv = 1.0f;
-    if constexpr (kNorm)
-      inv = 1.0f / sqrtf(block_sum(ss, sh) / (float)K + eps);  // block_sum's barriers publish row_lds
-    else
-      __syncthreads();
-    if (row + 1 < r1) load_row(row + 1);
-    // chunks and s_chunks are multiples of 4, so the four lanes of a quad
-    // (one 32-block) take the same branches
+    if constexpr (kNorm) inv = 1.0f / sqrtf((((sh[r][0] + sh[r][1]) + sh[r][2]) + sh[r][3]) / (float)K + eps);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = (int)threadIdx.x + 256 * i;
+      const int c = t + 256 * i;
       if (c >= chunks) break;
       uint32_t v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = (p[i][e] >= 0 && p[i][e] < K) ? (uint32_t)rh[p[i][e]] : 0u;
       uint4 qv;
-      if constexpr (kNorm) {
+      if constexpr (kNorm)
         qv = make_uint4(pack_bf16(bf16_to_f32(v[0]) * inv, bf16_to_f32(v[1]) * inv),
                         pack_bf16(bf16_to_f32(v[2]) * inv, bf16_to_f32(v[3]) * inv),
                         pack_bf16(bf16_to_f32(v[4]) * inv, bf16_to_f32(v[5]) * inv),
                         pack_bf16(bf16_to_f32(v[6]) * inv, bf16_to_f32(v[7]) * inv));
-        const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (qw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-      } else {
+      else
         qv = pack8(v);
-      }
       const uint32_t sb = (uint32_t)(mx_block_exp<Fmt>(quad_max(amax8(qv))) + 127);
       const uint2 cv = encode8<Fmt>(qv, sb);
       store8<Fmt>(cv, codes + row * ldc + (int64_t)c * 4 * kElemBytesNum);
       if ((c & 3) == 0) scales[row * lds + (c >> 2)] = (uint8_t)sb;
       if (c < s_chunks) {
-        uint32_t r[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if constexpr (kResidual) {
-            // the primary stage's value from its own code (the hardware
-            // conversion's codes are the integer encoder's)
-            const uint32_t code = code_at<Fmt>(cv, e);
-            float dq = __builtin_ldexpf(mx_mag_value<Fmt>(code & ((1u << Fmt::kSignShift) - 1u)), (int)sb - 127);
-            if (code >> Fmt::kSignShift) dq = -dq;
-            r[e] = __builtin_bit_cast(uint32_t, bf16_to_f32(v[e]) - dq) >> 16;  // exact: a BF16 value
-          } else {
-            r[e] = v[e];
-          }
-        }
-        const uint4 q2 = pack8(r);
+        const uint4 q2 = kResidual ? residual8<Fmt>(qv, cv, sb) : qv;
         const uint32_t sb2 = (uint32_t)(mx_block_exp<Fmt>(quad_max(amax8(q2))) + 127);
         encode_store8<Fmt>(q2, sb2, codes + row * ldc + (K + (int64_t)c * 8) / 2 * kElemBytesNum);
         if ((c & 3) == 0) scales[row * lds + (K >> 5) + (c >> 2)] = (uint8_t)sb2;
@@ -356,36 +366,27 @@ hipError_t launch_quant_append(int fmt, int mode, const uint16_t* x, int64_t row
   return hipGetLastError();
 }
 
-// Workgroups that fit on the chip at once for a kernel of 256 threads with
-// `lds` bytes of LDS and about `vgprs` registers per thread, so that a run
-// of rows per workgroup covers the rows in one round.
-static int64_t resident_wgs(size_t lds, int vgprs) {
-  int per_cu = std::min(8, 512 / std::max(vgprs, 1));   // waves per SIMD = workgroups per CU
-  if (lds > 0) per_cu = std::min<int>(per_cu, (int)((160 * 1024) / lds));
-  return 256 * (int64_t)std::max(per_cu, 1);
-}
-
-template <class Fmt, int CPT>
+template <class Fmt, int CPT, int R>
 static hipError_t launch_rows_append_c(int mode, const uint16_t* x, int64_t rows, int64_t K, const int32_t* idx,
                                        int64_t S, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
-  const size_t shm = (size_t)K * 2;
-  const int64_t target = resident_wgs(shm, 24 + 12 * CPT);
-  const int rpw = (int)((rows + target - 1) / target);
-  const unsigned g = (unsigned)((rows + rpw - 1) / rpw);
+  const size_t shm = (size_t)R * K * 2 + (mode == 1 ? (size_t)R * (K / 32) : 0);
+  const unsigned g = (unsigned)((rows + R - 1) / R);
   if (mode == 1)
-    quant_rows_append_kernel<Fmt, true, CPT><<<g, 256, shm, stream>>>(x, rows, K, idx, S, codes, scales, rpw);
+    quant_rows_append_kernel<Fmt, true, CPT, R><<<g, 256, shm, stream>>>(x, rows, K, idx, S, codes, scales);
   else
-    quant_rows_append_kernel<Fmt, false, CPT><<<g, 256, shm, stream>>>(x, rows, K, idx, S, codes, scales, rpw);
+    quant_rows_append_kernel<Fmt, false, CPT, R><<<g, 256, shm, stream>>>(x, rows, K, idx, S, codes, scales);
   return hipGetLastError();
 }
 
+// Two rows per workgroup up to K = 8192 (16 KiB of LDS at K = 4096: eight
+// workgroups per CU), one beyond.
 template <class Fmt>
 static hipError_t launch_rows_append_f(int mode, const uint16_t* x, int64_t rows, int64_t K, const int32_t* idx,
                                        int64_t S, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
-  if (K <= 2048) return launch_rows_append_c<Fmt, 1>(mode, x, rows, K, idx, S, codes, scales, stream);
-  if (K <= 4096) return launch_rows_append_c<Fmt, 2>(mode, x, rows, K, idx, S, codes, scales, stream);
-  if (K <= 8192) return launch_rows_append_c<Fmt, 4>(mode, x, rows, K, idx, S, codes, scales, stream);
-  return launch_rows_append_c<Fmt, 8>(mode, x, rows, K, idx, S, codes, scales, stream);
+  if (K <= 2048) return launch_rows_append_c<Fmt, 1, 2>(mode, x, rows, K, idx, S, codes, scales, stream);
+  if (K <= 4096) return launch_rows_append_c<Fmt, 2, 2>(mode, x, rows, K, idx, S, codes, scales, stream);
+  if (K <= 8192) return launch_rows_append_c<Fmt, 4, 2>(mode, x, rows, K, idx, S, codes, scales, stream);
+  return launch_rows_append_c<Fmt, 8, 1>(mode, x, rows, K, idx, S, codes, scales, stream);
 }
 
 hipError_t launch_quant_rows_append(int fmt, int mode, const uint16_t* x, int64_t rows, int64_t K,
@@ -404,24 +405,20 @@ hipError_t launch_quant_rows_append(int fmt, int mode, const uint16_t* x, int64_
   return launch_rows_append_f<FmtE4M3>(mode, x, rows, K, idx, S, codes, scales, stream);
 }
 
-template <class Fmt, int CPT>
+template <class Fmt, int CPT, int R>
 static hipError_t launch_frontend_c(int mode, bool norm, const uint16_t* x, int64_t rows, int64_t K,
                                     const int32_t* perm, int64_t S, float eps, uint8_t* codes, uint8_t* scales,
                                     hipStream_t stream) {
-  // the workgroups that fit on the chip at once, each over a run of rows
-  // (its perm entries stay in registers), so the rows take one round
-  const size_t shm = (size_t)K * 2;
-  const int64_t target = resident_wgs(shm, 32 + 20 * CPT);
-  const int rpw = (int)((rows + target - 1) / target);
-  const unsigned g = (unsigned)((rows + rpw - 1) / rpw);
+  const size_t shm = (size_t)R * K * 2;
+  const unsigned g = (unsigned)((rows + R - 1) / R);
   if (mode == 1 && norm)
-    arc_frontend_kernel<Fmt, true, true, CPT><<<g, 256, shm, stream>>>(x, rows, K, perm, S, eps, codes, scales, rpw);
+    arc_frontend_kernel<Fmt, true, true, CPT, R><<<g, 256, shm, stream>>>(x, rows, K, perm, S, eps, codes, scales);
   else if (mode == 1)
-    arc_frontend_kernel<Fmt, true, false, CPT><<<g, 256, shm, stream>>>(x, rows, K, perm, S, eps, codes, scales, rpw);
+    arc_frontend_kernel<Fmt, true, false, CPT, R><<<g, 256, shm, stream>>>(x, rows, K, perm, S, eps, codes, scales);
   else if (norm)
-    arc_frontend_kernel<Fmt, false, true, CPT><<<g, 256, shm, stream>>>(x, rows, K, perm, S, eps, codes, scales, rpw);
+    arc_frontend_kernel<Fmt, false, true, CPT, R><<<g, 256, shm, stream>>>(x, rows, K, perm, S, eps, codes, scales);
   else
-    arc_frontend_kernel<Fmt, false, false, CPT><<<g, 256, shm, stream>>>(x, rows, K, perm, S, eps, codes, scales, rpw);
+    arc_frontend_kernel<Fmt, false, false, CPT, R><<<g, 256, shm, stream>>>(x, rows, K, perm, S, eps, codes, scales);
   return hipGetLastError();
 }
 
@@ -429,11 +426,12 @@ template <class Fmt>
 static hipError_t launch_frontend_f(int mode, bool norm, const uint16_t* x, int64_t rows, int64_t K,
                                     const int32_t* perm, int64_t S, float eps, uint8_t* codes, uint8_t* scales,
                                     hipStream_t stream) {
-  // chunks per thread: K / 8 chunks over 256 threads
-  if (K <= 2048) return launch_frontend_c<Fmt, 1>(mode, norm, x, rows, K, perm, S, eps, codes, scales, stream);
-  if (K <= 4096) return launch_frontend_c<Fmt, 2>(mode, norm, x, rows, K, perm, S, eps, codes, scales, stream);
-  if (K <= 8192) return launch_frontend_c<Fmt, 4>(mode, norm, x, rows, K, perm, S, eps, codes, scales, stream);
-  return launch_frontend_c<Fmt, 8>(mode, norm, x, rows, K, perm, S, eps, codes, scales, stream);
+  // chunks per thread: K / 8 chunks over 256 threads; two rows per
+  // workgroup up to K = 8192, one beyond
+  if (K <= 2048) return launch_frontend_c<Fmt, 1, 2>(mode, norm, x, rows, K, perm, S, eps, codes, scales, stream);
+  if (K <= 4096) return launch_frontend_c<Fmt, 2, 2>(mode, norm, x, rows, K, perm, S, eps, codes, scales, stream);
+  if (K <= 8192) return launch_frontend_c<Fmt, 4, 2>(mode, norm, x, rows, K, perm, S, eps, codes, scales, stream);
+  return launch_frontend_c<Fmt, 8, 1>(mode, norm, x, rows, K, perm, S, eps, codes, scales, stream);
 }
 
 hipError_t launch_arc_frontend(int fmt, int mode, bool norm, const uint16_t* x, int64_t rows, int64_t K,

@@ -110,6 +110,28 @@ __device__ __forceinline__ uint4 residual8(uint4 q, uint2 c, uint32_t sb) {
   return pack8(r);
 }
 
+// Residual of one BF16 value (low half of v) against its own code under
+// block scale byte sb, as a BF16 bit pattern: the element alone through the
+// same scaled conversions as encode8 and residual8 (the conversion treats
+// the two inputs of a pair independently, so the code is the one its block
+// gave it), exact for the reason given at residual8.
+template <class Fmt>
+__device__ __forceinline__ uint32_t residual1(uint32_t v, uint32_t sb) {
+  const float scale = e8m0_to_f32(sb);
+  float d;
+  if constexpr (Fmt::kMantBits == 1) {
+    const uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, __builtin_bit_cast(rq_v2bf, v), scale, 0);
+    const rq_v2f t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, scale, 0);
+    d = t.x;
+  } else {
+    const rq_v2s c = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16((rq_v2s){0, 0}, __builtin_bit_cast(rq_v2bf, v), scale,
+                                                               false);
+    const rq_v2f t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(__builtin_bit_cast(uint32_t, c), scale, false);
+    d = t.x;
+  }
+  return __builtin_bit_cast(uint32_t, bf16_to_f32(v) - d) >> 16;
+}
+
 // Encode 8 BF16 values with block scale byte sb and store them: FP4 -> one
 // dword (element 2j in the low nibble of byte j), FP8 -> two dwords.
 template <class Fmt>

@@ -125,7 +125,7 @@ def test_adversarial_blocks():
 @pytest.mark.parametrize("fmt,ofmt", FMTS)
 @pytest.mark.parametrize("mode", [L.RQ_APPEND_RESIDUAL, L.RQ_APPEND_COPY])
 def test_append_modes(fmt, ofmt, mode):
-    d = W.c3_arc(M=300, K=512, N=8, n_outliers=16)
+    d = W.c3_arc(M=301, K=512, N=8, n_outliers=16)  # odd: a workgroup with one live row
     rng = np.random.default_rng(mode)
     idx = np.concatenate([A.select_outlier_channels(d["a"], 32), rng.integers(0, 512, 32)]).astype(np.int32)
     idx[40] = idx[3]  # a duplicate channel
@@ -139,17 +139,19 @@ def test_append_modes(fmt, ofmt, mode):
 
 
 @pytest.mark.parametrize("fmt,ofmt", FMTS)
-@pytest.mark.parametrize("K,S", [(256, 32), (4096, 128), (2080, 96), (9600, 2048), (12288, 2080)])
+@pytest.mark.parametrize("K,S", [(256, 32), (4096, 128), (4096, 2048), (2080, 96), (9600, 2048), (12288, 2080)])
 def test_residual_append_extreme_exponents(fmt, ofmt, K, S):
     """Residual appends on blocks whose scale spans BF16's range: rows of
     subnormal BF16 values (block byte 0 or near it), rows near the largest
-    finite BF16 and ordinary rows, for the one-pass path (a row in LDS;
-    S / 8 appended chunks over the workgroup) and, at K = 12288 with
-    S = 2080 (more appended chunks than threads), the two-pass path."""
+    finite BF16 and ordinary rows (25 of them: the last workgroup of two
+    rows has one live), for the one-pass path (the workgroup's rows in LDS;
+    S / 8 appended chunks per row, two rounds of tasks at K = 4096 with
+    S = 2048) and, at K = 12288 with S = 2080 (more appended chunks than
+    threads), the two-pass path."""
     rng = np.random.default_rng(K + S)
-    rows = 24
+    rows = 25
     mag = rng.standard_normal((rows, K))
-    scale = np.concatenate([np.full(8, 2.0 ** -133), np.full(8, 2.0 ** 120), np.ones(8)])
+    scale = np.concatenate([np.full(8, 2.0 ** -133), np.full(8, 2.0 ** 120), np.ones(9)])
     x = F.f64_to_bf16(mag * scale[:, None])
     idx = rng.integers(0, K, S).astype(np.int32)
     log(f"extreme residual append fmt={ofmt} K={K} S={S}")
