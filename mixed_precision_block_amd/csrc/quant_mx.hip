@@ -118,16 +118,18 @@ __global__ __launch_bounds__(256) void quant_rows_append_kernel(const uint16_t* 
                                                                 int64_t K, const int32_t* __restrict__ idx,
                                                                 int64_t S, uint8_t* __restrict__ codes,
                                                                 uint8_t* __restrict__ scales) {
-  // R rows of K / 8 chunks of BF16 values, then (RESIDUAL) R rows of K / 32
-  // block scale bytes
+  // R row buffers of kRowChunks chunks (the row's K / 8 chunks of BF16
+  // values, then a chunk of zeros at kZero that out-of-range idx entries
+  // read), then (RESIDUAL) R rows of K / 32 block scale bytes
   extern __shared__ uint4 row_lds[];
+  constexpr int kRowChunks = 256 * CPT + 1;
+  constexpr uint32_t kZero = 256u * CPT * 16u;
   constexpr int kElemBytesNum = Fmt::kMantBits == 1 ? 1 : 2;  // bytes per 2 elements
   constexpr int kTasks = R;  // appended tasks per thread: R S / 8 <= 256 R
   const int chunks = (int)(K >> 3), s_chunks = (int)(S >> 3), blocks = (int)(K >> 5);
-  uint8_t* sb_lds = reinterpret_cast<uint8_t*>(row_lds + R * chunks);
+  uint8_t* sb_lds = reinterpret_cast<uint8_t*>(row_lds + R * kRowChunks);
   const int64_t ldc = (K + S) / 2 * kElemBytesNum, lds = (K + S) >> 5;
   const int64_t r0 = (int64_t)blockIdx.x * R;
-  const uint16_t* rh = reinterpret_cast<const uint16_t*>(row_lds);
   const int t = (int)threadIdx.x;
   uint4 q[R][CPT];
 #pragma unroll
@@ -140,14 +142,22 @@ __global__ __launch_bounds__(256) void quant_rows_append_kernel(const uint16_t* 
       q[r][i] = live && c < chunks ? xr[c] : make_uint4(0, 0, 0, 0);
     }
   }
-  int32_t ch[kTasks][8];
+  // per appended element: LDS byte offset in a row buffer (kZero out of
+  // range) and the index of its primary block
+  uint32_t off[kTasks][8], blk[kTasks][8];
 #pragma unroll
   for (int k = 0; k < kTasks; ++k) {
     const int task = t + 256 * k, c = task % max(s_chunks, 1);
     const bool on = task < R * s_chunks;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ch[k][e] = on ? idx[8 * c + e] : -1;
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t chn = on ? (uint32_t)idx[8 * c + e] : 0xFFFFFFFFu;
+      const bool in = chn < (uint32_t)K;
+      off[k][e] = in ? 2u * chn : kZero;
+      blk[k][e] = in ? chn >> 5 : 0u;
+    }
   }
+  if (t < R) row_lds[t * kRowChunks + 256 * CPT] = make_uint4(0, 0, 0, 0);
   // chunks is a multiple of 4, so the four lanes of a quad (one 32-block)
   // take the same branches
 #pragma unroll
@@ -165,10 +175,10 @@ __global__ __launch_bounds__(256) void quant_rows_append_kernel(const uint16_t* 
         scales[row * lds + (c >> 2)] = (uint8_t)sb;
         if constexpr (kResidual) sb_lds[r * blocks + (c >> 2)] = (uint8_t)sb;
       }
-      row_lds[r * chunks + c] = q[r][i];
+      row_lds[r * kRowChunks + c] = q[r][i];
     }
   }
-  __syncthreads();  // every parked row is complete
+  __syncthreads();  // every parked row and its zero chunk is complete
 #pragma unroll
   for (int k = 0; k < kTasks; ++k) {
     const int task = t + 256 * k;
@@ -178,14 +188,13 @@ __global__ __launch_bounds__(256) void quant_rows_append_kernel(const uint16_t* 
     // whole quads: s_chunks is a multiple of 4, so a quad's four tasks
     // share the row
     if (row < rows) {
-      const uint16_t* src = rh + (int64_t)r * K;
+      const char* rb = reinterpret_cast<const char*>(row_lds + r * kRowChunks);
       const uint8_t* sbr = sb_lds + r * blocks;
       uint32_t v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const bool in = ch[k][e] >= 0 && ch[k][e] < K;
-        v[e] = in ? (uint32_t)src[ch[k][e]] : 0u;
-        if constexpr (kResidual) v[e] = in ? residual1<Fmt>(v[e], sbr[ch[k][e] >> 5]) : 0u;
+        v[e] = *reinterpret_cast<const uint16_t*>(rb + off[k][e]);
+        if constexpr (kResidual) v[e] = residual1<Fmt>(v[e], sbr[blk[k][e]]);  // 0 stays 0
       }
       const uint4 q2 = pack8(v);
       const uint32_t sb2 = (uint32_t)(mx_block_exp<Fmt>(quad_max(amax8(q2))) + 127);
@@ -196,112 +205,177 @@ __global__ __launch_bounds__(256) void quant_rows_append_kernel(const uint16_t* 
 }
 
 // ARCQuant fused front end (ARCQuant page, technical summary, "Kernel
-// Implementatie" with the stages of "Methodologie").  A workgroup owns R
-// consecutive rows and loads all of them, and its threads' perm entries,
-// before it computes anything; thread t owns chunks c = t + 256 i
-// (i < CPT) of every row.  The rows are staged in LDS, one buffer per row;
-// with kNorm each row's mean square is summed in fp32 in the order of
-// rmsnorm_kernel (lanes by butterfly, then waves 0..3), and every element
-// is scaled by 1 / sqrt(ms + eps) and rounded to BF16 as it is gathered, so
-// the normalized values equal rmsnorm_kernel's.  One barrier separates the
-// staging from the gathers.  Output position j takes channel perm[j]
-// (out-of-range entries read as 0).  Primary blocks cover positions
-// 0..K-1; the first S positions (the outlier channels after an amax
-// reorder) also fill appended block j / 32 + K / 32: the residual against
-// the primary stage (kResidual, residual8) or the value itself.
-template <class Fmt, bool kResidual, bool kNorm, int CPT, int R>
-__global__ __launch_bounds__(256) void arc_frontend_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t K,
-                                                           const int32_t* __restrict__ perm, int64_t S, float eps,
-                                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
-  extern __shared__ uint4 row_lds[];  // R rows of K / 8 chunks of BF16
-  __shared__ float sh[R][4];
-  constexpr int kElemBytesNum = Fmt::kMantBits == 1 ? 1 : 2;  // bytes per 2 elements
-  const int chunks = (int)(K >> 3), s_chunks = (int)(S >> 3);
-  const int64_t ldc = (K + S) / 2 * kElemBytesNum, lds = (K + S) >> 5;
-  const int64_t r0 = (int64_t)blockIdx.x * R;
-  const int t = (int)threadIdx.x;
-  uint4 q[R][CPT];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const bool live = r0 + r < rows;
-    const uint4* xr = reinterpret_cast<const uint4*>(x + (r0 + r) * K);
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = t + 256 * i;
-      q[r][i] = live && c < chunks ? xr[c] : make_uint4(0, 0, 0, 0);
-    }
-  }
-  int32_t p[CPT][8];
+// Implementatie" with the stages of "Methodologie").  Thread t owns chunks
+// c = t + 256 i (i < CPT) of every row.  A row is staged in an LDS row
+// buffer of kRowChunks chunks: its K / 8 chunks of BF16, then a chunk of
+// zeros at kZero that out-of-range order entries point at (the order is
+// turned into LDS byte offsets once per workgroup, so every gather is an
+// unconditional LDS read).  With kNorm the row's mean square is summed in
+// fp32 while it is staged, in the order of rmsnorm_kernel (lanes by
+// butterfly, then waves 0..3), and every element is scaled by
+// 1 / sqrt(ms + eps) and rounded to BF16 as it is gathered, so the
+// normalized values equal rmsnorm_kernel's.  Output position j takes
+// channel perm[j] (out-of-range entries read as 0).  Primary blocks cover
+// positions 0..K-1; the first S positions (the outlier channels after an
+// amax reorder) also fill appended block j / 32 + K / 32: the residual
+// against the primary stage (kResidual, residual8) or the value itself.
+template <int CPT>
+struct FeRow {
+  static constexpr int kRowChunks = 256 * CPT + 1;
+  static constexpr uint32_t kZero = 256u * CPT * 16u;
+};
+
+template <int CPT>
+__device__ __forceinline__ void fe_load(const uint16_t* __restrict__ x, int64_t row, int64_t K, bool live,
+                                        uint4 (&q)[CPT]) {
+  const uint4* xr = reinterpret_cast<const uint4*>(x + row * K);
+  const int chunks = (int)(K >> 3);
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const int c = t + 256 * i;
+    const int c = (int)threadIdx.x + 256 * i;
+    q[i] = live && c < chunks ? xr[c] : make_uint4(0, 0, 0, 0);
+  }
+}
+
+typedef __attribute__((address_space(3))) uint4 lds_uint4;
+typedef __attribute__((address_space(3))) const uint16_t lds_cu16;
+
+// LDS address of a shared-memory pointer
+__device__ __forceinline__ uint32_t lds_addr(const uint4* p) {
+  return (uint32_t)(uintptr_t)(const lds_uint4*)p;
+}
+
+// LDS addresses, in the row buffer at LDS address base, of the channels
+// this thread's chunks gather
+template <int CPT>
+__device__ __forceinline__ void fe_offsets(const int32_t* __restrict__ perm, int64_t K, uint32_t base,
+                                           uint32_t (&po)[CPT][8]) {
+  const int chunks = (int)(K >> 3);
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = (int)threadIdx.x + 256 * i;
     int4 p0 = make_int4(-1, -1, -1, -1), p1 = p0;
     if (c < chunks) {
       p0 = reinterpret_cast<const int4*>(perm)[2 * c];
       p1 = reinterpret_cast<const int4*>(perm)[2 * c + 1];
     }
-    p[i][0] = p0.x, p[i][1] = p0.y, p[i][2] = p0.z, p[i][3] = p0.w;
-    p[i][4] = p1.x, p[i][5] = p1.y, p[i][6] = p1.z, p[i][7] = p1.w;
+    const int32_t pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      po[i][e] = base + ((uint32_t)pv[e] < (uint32_t)K ? 2u * (uint32_t)pv[e] : FeRow<CPT>::kZero);
   }
+}
+
+// Stage one row in buf; with kNorm, sh_row[w] = wave w's sum of squares.
+template <bool kNorm, int CPT>
+__device__ __forceinline__ void fe_stage(const uint4 (&q)[CPT], int64_t K, uint4* buf, float* sh_row) {
+  const int chunks = (int)(K >> 3), t = (int)threadIdx.x;
+  float ss = 0.0f;
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    float ss = 0.0f;
+  for (int i = 0; i < CPT; ++i) {
+    const int c = t + 256 * i;
+    if (c >= chunks) break;
+    buf[c] = q[i];
+    if constexpr (kNorm) {
+      const uint32_t w[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = t + 256 * i;
-      if (c >= chunks) break;
-      row_lds[r * chunks + c] = q[r][i];
-      if constexpr (kNorm) {
-        const uint32_t w[4] = {q[r][i].x, q[r][i].y, q[r][i].z, q[r][i].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float a = bf16_to_f32(w[e] & 0xFFFFu), b = bf16_to_f32(w[e] >> 16);
-          ss = fmaf(a, a, ss);
-          ss = fmaf(b, b, ss);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const float a = bf16_to_f32(w[e] & 0xFFFFu), b = bf16_to_f32(w[e] >> 16);
+        ss = fmaf(a, a, ss);
+        ss = fmaf(b, b, ss);
       }
     }
-    if constexpr (kNorm) {
-      ss = wave_sum(ss);
-      if ((t & 63) == 0) sh[r][t >> 6] = ss;
-    }
   }
-  __syncthreads();  // the staged rows and their partial sums are published
+  if constexpr (kNorm) {
+    ss = wave_sum(ss);
+    if ((t & 63) == 0) sh_row[t >> 6] = ss;
+  }
+}
+
+// Gather, normalize, quantize and store one staged row.
+// (po holds LDS addresses in the first row buffer; this row's buffer lies
+// buf_off bytes further)
+// The normalization factor of a row from its four wave sums, as
+// rmsnorm_kernel forms it.
+__device__ __forceinline__ float fe_inv(const float* sh_row, int64_t K, float eps) {
+  return 1.0f / sqrtf((((sh_row[0] + sh_row[1]) + sh_row[2]) + sh_row[3]) / (float)K + eps);
+}
+
+// (inv: the row's normalization factor, used with kNorm)
+template <class Fmt, bool kResidual, bool kNorm, int CPT>
+__device__ __forceinline__ void fe_emit(uint32_t buf_off, float inv, const uint32_t (&po)[CPT][8], int64_t row,
+                                        int64_t K, int64_t S, uint8_t* __restrict__ codes,
+                                        uint8_t* __restrict__ scales) {
+  constexpr int kElemBytesNum = Fmt::kMantBits == 1 ? 1 : 2;  // bytes per 2 elements
+  const int chunks = (int)(K >> 3), s_chunks = (int)(S >> 3);
+  const int64_t ldc = (K + S) / 2 * kElemBytesNum, lds = (K + S) >> 5;
   // chunks and s_chunks are multiples of 4, so the four lanes of a quad
   // (one 32-block) take the same branches
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int64_t row = r0 + r;
-    if (row >= rows) break;
-    const uint16_t* rh = reinterpret_cast<const uint16_t*>(row_lds) + (int64_t)r * K;
-    float inv = 1.0f;
-    if constexpr (kNorm) inv = 1.0f / sqrtf((((sh[r][0] + sh[r][1]) + sh[r][2]) + sh[r][3]) / (float)K + eps);
+  for (int i = 0; i < CPT; ++i) {
+    const int c = (int)threadIdx.x + 256 * i;
+    if (c >= chunks) break;
+    uint32_t v[8];
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = t + 256 * i;
-      if (c >= chunks) break;
-      uint32_t v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (p[i][e] >= 0 && p[i][e] < K) ? (uint32_t)rh[p[i][e]] : 0u;
-      uint4 qv;
-      if constexpr (kNorm)
-        qv = make_uint4(pack_bf16(bf16_to_f32(v[0]) * inv, bf16_to_f32(v[1]) * inv),
-                        pack_bf16(bf16_to_f32(v[2]) * inv, bf16_to_f32(v[3]) * inv),
-                        pack_bf16(bf16_to_f32(v[4]) * inv, bf16_to_f32(v[5]) * inv),
-                        pack_bf16(bf16_to_f32(v[6]) * inv, bf16_to_f32(v[7]) * inv));
-      else
-        qv = pack8(v);
-      const uint32_t sb = (uint32_t)(mx_block_exp<Fmt>(quad_max(amax8(qv))) + 127);
-      const uint2 cv = encode8<Fmt>(qv, sb);
-      store8<Fmt>(cv, codes + row * ldc + (int64_t)c * 4 * kElemBytesNum);
-      if ((c & 3) == 0) scales[row * lds + (c >> 2)] = (uint8_t)sb;
-      if (c < s_chunks) {
-        const uint4 q2 = kResidual ? residual8<Fmt>(qv, cv, sb) : qv;
-        const uint32_t sb2 = (uint32_t)(mx_block_exp<Fmt>(quad_max(amax8(q2))) + 127);
-        encode_store8<Fmt>(q2, sb2, codes + row * ldc + (K + (int64_t)c * 8) / 2 * kElemBytesNum);
-        if ((c & 3) == 0) scales[row * lds + (K >> 5) + (c >> 2)] = (uint8_t)sb2;
-      }
+    for (int e = 0; e < 8; ++e) v[e] = *(lds_cu16*)(uintptr_t)(po[i][e] + buf_off);
+    uint4 qv;
+    if constexpr (kNorm)
+      qv = make_uint4(pack_bf16(bf16_to_f32(v[0]) * inv, bf16_to_f32(v[1]) * inv),
+                      pack_bf16(bf16_to_f32(v[2]) * inv, bf16_to_f32(v[3]) * inv),
+                      pack_bf16(bf16_to_f32(v[4]) * inv, bf16_to_f32(v[5]) * inv),
+                      pack_bf16(bf16_to_f32(v[6]) * inv, bf16_to_f32(v[7]) * inv));
+    else
+      qv = pack8(v);
+    const uint32_t sb = (uint32_t)(mx_block_exp<Fmt>(quad_max(amax8(qv))) + 127);
+    const uint2 cv = encode8<Fmt>(qv, sb);
+    store8<Fmt>(cv, codes + row * ldc + (int64_t)c * 4 * kElemBytesNum);
+    if ((c & 3) == 0) scales[row * lds + (c >> 2)] = (uint8_t)sb;
+    if (c < s_chunks) {
+      const uint4 q2 = kResidual ? residual8<Fmt>(qv, cv, sb) : qv;
+      const uint32_t sb2 = (uint32_t)(mx_block_exp<Fmt>(quad_max(amax8(q2))) + 127);
+      encode_store8<Fmt>(q2, sb2, codes + row * ldc + (K + (int64_t)c * 8) / 2 * kElemBytesNum);
+      if ((c & 3) == 0) scales[row * lds + (K >> 5) + (c >> 2)] = (uint8_t)sb2;
     }
+  }
+}
+
+// A workgroup owns R consecutive rows and loads all of them, and its
+// order offsets, before it computes anything; one barrier separates the
+// staging of the R rows (a buffer each) from their gathers (with kNorm a
+// second one publishes each row's factor, formed once by wave r).
+template <class Fmt, bool kResidual, bool kNorm, int CPT, int R>
+__global__ __launch_bounds__(256) void arc_frontend_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t K,
+                                                           const int32_t* __restrict__ perm, int64_t S, float eps,
+                                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  // R row buffers (static, so their LDS address is known when the kernel
+  // is compiled and the gathers' addresses need no add), the R rows' four
+  // wave sums
+  constexpr int kRowChunks = FeRow<CPT>::kRowChunks;
+  __shared__ uint4 row_lds[R * kRowChunks];
+  __shared__ float sh[R][4];
+  __shared__ float sh_inv[R];
+  const int64_t r0 = (int64_t)blockIdx.x * R;
+  const int t = (int)threadIdx.x;
+  uint4 q[R][CPT];
+#pragma unroll
+  for (int r = 0; r < R; ++r) fe_load<CPT>(x, r0 + r, K, r0 + r < rows, q[r]);
+  uint32_t po[CPT][8];
+  fe_offsets<CPT>(perm, K, lds_addr(row_lds), po);
+  if (t < R) row_lds[t * kRowChunks + 256 * CPT] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < R; ++r) fe_stage<kNorm, CPT>(q[r], K, row_lds + r * kRowChunks, sh[r]);
+  __syncthreads();  // the staged rows, their zero chunks and partial sums are published
+  if constexpr (kNorm) {
+    // wave r forms row r's factor once for the workgroup (R <= 4 waves)
+    const int w = t >> 6;
+    if (w < R && (t & 63) == 0) sh_inv[w] = fe_inv(sh[w], K, eps);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r0 + r >= rows) break;
+    fe_emit<Fmt, kResidual, kNorm, CPT>(16u * r * kRowChunks, kNorm ? sh_inv[r] : 1.0f, po, r0 + r, K, S, codes,
+                                        scales);
   }
 }
 
@@ -369,7 +443,7 @@ hipError_t launch_quant_append(int fmt, int mode, const uint16_t* x, int64_t row
 template <class Fmt, int CPT, int R>
 static hipError_t launch_rows_append_c(int mode, const uint16_t* x, int64_t rows, int64_t K, const int32_t* idx,
                                        int64_t S, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
-  const size_t shm = (size_t)R * K * 2 + (mode == 1 ? (size_t)R * (K / 32) : 0);
+  const size_t shm = (size_t)R * (256 * CPT + 1) * 16 + (mode == 1 ? (size_t)R * (K / 32) : 0);
   const unsigned g = (unsigned)((rows + R - 1) / R);
   if (mode == 1)
     quant_rows_append_kernel<Fmt, true, CPT, R><<<g, 256, shm, stream>>>(x, rows, K, idx, S, codes, scales);
@@ -409,16 +483,15 @@ template <class Fmt, int CPT, int R>
 static hipError_t launch_frontend_c(int mode, bool norm, const uint16_t* x, int64_t rows, int64_t K,
                                     const int32_t* perm, int64_t S, float eps, uint8_t* codes, uint8_t* scales,
                                     hipStream_t stream) {
-  const size_t shm = (size_t)R * K * 2;
   const unsigned g = (unsigned)((rows + R - 1) / R);
   if (mode == 1 && norm)
-    arc_frontend_kernel<Fmt, true, true, CPT, R><<<g, 256, shm, stream>>>(x, rows, K, perm, S, eps, codes, scales);
+    arc_frontend_kernel<Fmt, true, true, CPT, R><<<g, 256, 0, stream>>>(x, rows, K, perm, S, eps, codes, scales);
   else if (mode == 1)
-    arc_frontend_kernel<Fmt, true, false, CPT, R><<<g, 256, shm, stream>>>(x, rows, K, perm, S, eps, codes, scales);
+    arc_frontend_kernel<Fmt, true, false, CPT, R><<<g, 256, 0, stream>>>(x, rows, K, perm, S, eps, codes, scales);
   else if (norm)
-    arc_frontend_kernel<Fmt, false, true, CPT, R><<<g, 256, shm, stream>>>(x, rows, K, perm, S, eps, codes, scales);
+    arc_frontend_kernel<Fmt, false, true, CPT, R><<<g, 256, 0, stream>>>(x, rows, K, perm, S, eps, codes, scales);
   else
-    arc_frontend_kernel<Fmt, false, false, CPT, R><<<g, 256, shm, stream>>>(x, rows, K, perm, S, eps, codes, scales);
+    arc_frontend_kernel<Fmt, false, false, CPT, R><<<g, 256, 0, stream>>>(x, rows, K, perm, S, eps, codes, scales);
   return hipGetLastError();
 }
 
