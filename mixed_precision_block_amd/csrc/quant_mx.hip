@@ -207,10 +207,10 @@ __global__ __launch_bounds__(256) void quant_rows_append_kernel(const uint16_t* 
 // ARCQuant fused front end (ARCQuant page, technical summary, "Kernel
 // Implementatie" with the stages of "Methodologie").  Thread t owns chunks
 // c = t + 256 i (i < CPT) of every row.  A row is staged in an LDS row
-// buffer of kRowChunks chunks: its K / 8 chunks of BF16, then a chunk of
-// zeros at kZero that out-of-range order entries point at (the order is
-// turned into LDS byte offsets once per workgroup, so every gather is an
-// unconditional LDS read).  With kNorm the row's mean square is summed in
+// buffer of kRowChunks chunks: its K / 8 chunks of BF16, zeros up to chunk
+// 256 CPT, then a chunk of zeros at kZero; out-of-range order entries
+// point at zeros (the order is turned into LDS addresses once per
+// workgroup, so every gather is an unconditional LDS read).  With kNorm the row's mean square is summed in
 // fp32 while it is staged, in the order of rmsnorm_kernel (lanes by
 // butterfly, then waves 0..3), and every element is scaled by
 // 1 / sqrt(ms + eps) and rounded to BF16 as it is gathered, so the
@@ -260,21 +260,23 @@ __device__ __forceinline__ void fe_offsets(const int32_t* __restrict__ perm, int
       p1 = reinterpret_cast<const int4*>(perm)[2 * c + 1];
     }
     const int32_t pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    // entries in [K, 2048 CPT) read the buffer's zero tail, larger and
+    // negative ones (as unsigned) the zero chunk
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      po[i][e] = base + ((uint32_t)pv[e] < (uint32_t)K ? 2u * (uint32_t)pv[e] : FeRow<CPT>::kZero);
+    for (int e = 0; e < 8; ++e) po[i][e] = base + 2u * min((uint32_t)pv[e], FeRow<CPT>::kZero / 2u);
   }
 }
 
-// Stage one row in buf; with kNorm, sh_row[w] = wave w's sum of squares.
+// Stage one row in buf, its chunks past K / 8 as zeros (fe_load leaves
+// them zero); with kNorm, sh_row[w] = wave w's sum of squares (the zeros
+// add nothing).
 template <bool kNorm, int CPT>
-__device__ __forceinline__ void fe_stage(const uint4 (&q)[CPT], int64_t K, uint4* buf, float* sh_row) {
-  const int chunks = (int)(K >> 3), t = (int)threadIdx.x;
+__device__ __forceinline__ void fe_stage(const uint4 (&q)[CPT], uint4* buf, float* sh_row) {
+  const int t = (int)threadIdx.x;
   float ss = 0.0f;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int c = t + 256 * i;
-    if (c >= chunks) break;
     buf[c] = q[i];
     if constexpr (kNorm) {
       const uint32_t w[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
@@ -363,7 +365,7 @@ __global__ __launch_bounds__(256) void arc_frontend_kernel(const uint16_t* __res
   fe_offsets<CPT>(perm, K, lds_addr(row_lds), po);
   if (t < R) row_lds[t * kRowChunks + 256 * CPT] = make_uint4(0, 0, 0, 0);
 #pragma unroll
-  for (int r = 0; r < R; ++r) fe_stage<kNorm, CPT>(q[r], K, row_lds + r * kRowChunks, sh[r]);
+  for (int r = 0; r < R; ++r) fe_stage<kNorm, CPT>(q[r], row_lds + r * kRowChunks, sh[r]);
   __syncthreads();  // the staged rows, their zero chunks and partial sums are published
   if constexpr (kNorm) {
     // wave r forms row r's factor once for the workgroup (R <= 4 waves)

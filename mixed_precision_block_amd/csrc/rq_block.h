@@ -36,13 +36,16 @@ __device__ __forceinline__ float block_sum(float v, float* sh) {
 }
 
 // Largest BF16 magnitude field of eight values (element 2i in the low half
-// of dword i).
+// of dword i): the fields masked in place, a packed 16-bit unsigned max
+// over the dwords, then the larger half.
+typedef unsigned short rq_u16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t amax8(uint4 q) {
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) m = max(m, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
-  return m;
+  const rq_u16x2 a = __builtin_bit_cast(rq_u16x2, q.x & 0x7FFF7FFFu);
+  const rq_u16x2 b = __builtin_bit_cast(rq_u16x2, q.y & 0x7FFF7FFFu);
+  const rq_u16x2 c = __builtin_bit_cast(rq_u16x2, q.z & 0x7FFF7FFFu);
+  const rq_u16x2 d = __builtin_bit_cast(rq_u16x2, q.w & 0x7FFF7FFFu);
+  const rq_u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+  return max((uint32_t)m.x, (uint32_t)m.y);
 }
 
 __device__ __forceinline__ uint4 pack8(const uint32_t v[8]) {
