@@ -209,9 +209,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run plain 256 MiB device copies (the reference for HBM byte counters)")
-    ap.add_argument("--only", choices=["square", "gemv", "ksweep"],
+    ap.add_argument("--only", choices=["square", "gemv", "ksweep", "probes"],
                     help="run only one group of rows (4096^3 GEMMs and the ARC front end, the nibble GEMV "
-                         "kernels without the escalation gate, or the exact MXFP8 GEMM's K sweep) "
+                         "kernels without the escalation gate, the exact MXFP8 GEMM's K sweep, or the "
+                         "hardware probes of libprobe.so: matrix-instruction rate and shader clock on "
+                         "constant and random operands, dequantization against BF16 MFMAs) "
                          "and print them; for profiling runs")
     ap.add_argument("--traffic-from", metavar="DIR",
                     help="write the traffic summary from rocprofv3 --pmc CSV runs under DIR (pmc_main_FETCH_SIZE, "
@@ -241,6 +243,8 @@ def main():
         to_dev_only = (lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev))
         if args.only == "square":
             out = measure_square(torch, api, L, W, to_dev_only, dev)
+        elif args.only == "probes":
+            out = {"hardware_probes": measure_probes(torch, np, dev)}
         elif args.only == "ksweep":
             out = {"mxfp8_exact_gemm_k_sweep_4096x4096": measure_ksweep(torch, np, api, L, W, to_dev_only, dev)}
         else:
@@ -370,6 +374,87 @@ def main():
         line["cpu_baseline"] = cpu_baseline(np, W, gpu_f32, acc_rows)
         line["accuracy_rel_frobenius"] = line["cpu_baseline"].pop("accuracy")
     print(json.dumps(line), flush=True)
+
+
+def measure_probes(torch, np, dev, blocks=512, seed=20261204):
+    """Matrix-instruction and conversion probes (probes/probes.hip, built as
+    libprobe.so): eight independent instructions per loop iteration per
+    wave, two waves per SIMD, on operands loaded once.  For each kind the
+    sustained rate, its fraction of the datasheet peak, the shader clock
+    (shader cycle counter over the 100 MHz real-time counter, median over
+    workgroups) and the SIMD's shader cycles per matrix instruction (event
+    time x that clock / instructions per SIMD; for the conversions alone,
+    per conversion)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "mixed_precision_block_amd", "libprobe.so"))
+    lib.rqp_probe.restype = ctypes.c_int
+    lib.rqp_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    rng = np.random.default_rng(seed)
+    n = blocks * 256
+
+    def fp8_codes(size):  # random E4M3FN codes, NaN (0x7F / 0xFF) excluded
+        c = rng.integers(0, 256, size, dtype=np.uint32)
+        return np.where((c & 0x7F) == 0x7F, c ^ 1, c)
+
+    def pack8(b):  # uint32 bytes [n, 12, 4] -> dwords [n, 12]
+        b = b.astype(np.uint32)
+        return b[..., 0] | (b[..., 1] << 8) | (b[..., 2] << 16) | (b[..., 3] << 24)
+
+    ops = {
+        "fp4_constant": np.full((n, 12), 0x22222222, np.uint32),           # every E2M1 code 1.0
+        "fp4_random": rng.integers(0, 2 ** 32, (n, 12), dtype=np.uint64).astype(np.uint32),
+        "fp8_constant": np.full((n, 12), 0x38383838, np.uint32),           # every E4M3 code 1.0
+        "fp8_random": pack8(fp8_codes((n, 12, 4))),
+        "bf16_constant": np.full((n, 12), 0x3F803F80, np.uint32),          # every BF16 value 1.0
+    }
+    g = rng.standard_normal((n, 12, 2)).astype(np.float32).view(np.uint32) >> 16  # N(0, 1) in BF16
+    ops["bf16_random"] = (g[..., 0] | (g[..., 1] << 16)).astype(np.uint32)
+    ops["fp8_random_dequant"] = ops["fp8_random"]
+    # kind, operands, FLOP per instruction, peak, iterations
+    runs = [("fp4_constant", 0, 131072, PEAK["mxfp4"], 40000), ("fp4_random", 0, 131072, PEAK["mxfp4"], 40000),
+            ("fp8_constant", 1, 131072, PEAK["mxfp8"], 20000), ("fp8_random", 1, 131072, PEAK["mxfp8"], 20000),
+            ("bf16_constant", 2, 32768, PEAK["bf16"], 40000), ("bf16_random", 2, 32768, PEAK["bf16"], 40000),
+            ("bf16_random_fed_by_24_fp8_dequant_per_8", 3, 32768, PEAK["bf16"], 40000),
+            ("fp8_dequant_24_per_iteration_alone", 4, 0, None, 40000)]
+    scales = torch.from_numpy(np.full(n, 0x7F7F, np.uint32).view(np.int32)).to(dev)  # both scales 1.0
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    stamps = torch.zeros(blocks * 4, dtype=torch.int64, device=dev)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for name, kind, flop, peak, iters in runs:
+        key = "fp8_random" if kind in (3, 4) else name
+        o = torch.from_numpy(ops[key].view(np.int32).copy()).to(dev)
+
+        def call():
+            rc = lib.rqp_probe(kind, o.data_ptr(), scales.data_ptr(), blocks, iters, out.data_ptr(),
+                               stamps.data_ptr(), st)
+            if rc:
+                raise RuntimeError(f"rqp_probe({kind}) returned {rc}")
+        call()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        t = stamps.cpu().numpy().view(np.uint64).reshape(blocks, 4).astype(np.float64)
+        clk = (t[:, 2] - t[:, 0]) / np.maximum(t[:, 3] - t[:, 1], 1.0) * 100e6
+        ghz = float(np.median(clk)) / 1e9
+        per_simd = iters * (8 if flop else 24) * blocks * 4 / 1024  # instructions of one SIMD
+        r = {"ms": round(ms, 3), "shader_clock_ghz": round(ghz, 3),
+             ("shader_cycles_per_instruction" if flop else "shader_cycles_per_conversion"):
+                 round(ms * 1e-3 * ghz * 1e9 / per_simd, 1)}
+        if flop:
+            rate = blocks * 4 * iters * 8 * flop / (ms * 1e-3)
+            r.update({"tflops": round(rate / 1e12, 1), "frac_peak": round(rate / peak, 4)})
+        res[name] = r
+        del o
+    res["setup"] = (f"{blocks} workgroups of 4 waves (2 waves per SIMD), eight independent matrix instructions "
+                    "per iteration (FP4 / FP8: v_mfma_scale_f32_32x32x64_f8f6f4 with both scales 1.0; BF16: "
+                    "v_mfma_f32_32x32x16_bf16); the dequant kinds add 24 v_cvt_scalef32_pk_bf16_fp8 per iteration "
+                    "(the ratio of the exact MXFP8 GEMM's 128 x 64 wave tiles)")
+    return res
 
 
 def measure_rows(torch, np, api, L, W, to_dev, dev):
