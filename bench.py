@@ -473,10 +473,108 @@ def measure_probes(torch, np, dev, blocks=512, seed=20261204):
             r.update({"tflops": round(rate / 1e12, 1), "frac_peak": round(rate / peak, 4)})
         res[name] = r
         del o
+    res.update(measure_stream_and_launch_probes(torch, lib, dev))
     res["setup"] = (f"{blocks} workgroups of 4 waves (2 waves per SIMD), eight independent matrix instructions "
                     "per iteration (FP4 / FP8: v_mfma_scale_f32_32x32x64_f8f6f4 with both scales 1.0; BF16: "
                     "v_mfma_f32_32x32x16_bf16); the dequant kinds add 24 v_cvt_scalef32_pk_bf16_fp8 per iteration "
                     "(the ratio of the exact MXFP8 GEMM's 128 x 64 wave tiles)")
+    return res
+
+
+def measure_stream_and_launch_probes(torch, lib, dev):
+    """L2 -> LDS streaming the way the pipelined GEMM loads (rqp_stream: one
+    512-thread workgroup per CU, buffer-to-LDS loads into a ring of stages,
+    one wait and barrier per stage, no compute), from data resident in each
+    XCD's L2 (shared windows read in step by an XCD's 32 CUs, or a private
+    64 KiB window per CU; the dispatcher deals workgroups round-robin over
+    the 8 XCDs) and from HBM (each workgroup its own 4 MiB window of
+    1 GiB); and the per-launch cost of back-to-back
+    launches in a captured HIP graph (rqp_launch: an empty kernel, one that
+    reads and writes 2 MiB, arrival launches of 1 and 64 tiles whose 16
+    workgroups each meet at a device-scope counter, as the split-K GEMV's
+    do)."""
+    import ctypes
+    import numpy as np
+    lib.rqp_stream.restype = ctypes.c_int
+    lib.rqp_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                               ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.rqp_launch.restype = ctypes.c_int
+    lib.rqp_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    res = {}
+    blocks = 256
+    src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    out = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+    stamps = torch.zeros(blocks * 4, dtype=torch.int64, device=dev)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    kinds = {0: ("two_64k_stages", 2, 65536), 1: ("three_32k_stages", 3, 32768), 2: ("four_32k_stages", 4, 32768)}
+    # l2_shared: the 32 workgroups of an XCD read one 2 MiB window in step
+    # (each line read by all of them); l2_private: each workgroup streams its
+    # own 64 KiB window (2 MiB per XCD, each line read by one CU); hbm: each
+    # workgroup its own 4 MiB window of 1 GiB
+    for where, win, nwin, stages in (("l2_shared", 2 << 20, 8, 4000), ("l2_private", 64 << 10, 256, 4000),
+                                     ("hbm", 4 << 20, 256, 1000)):
+        for kind, (name, nstg, sb) in kinds.items():
+            n_st = stages * 65536 // sb
+
+            def call():
+                rc = lib.rqp_stream(kind, src.data_ptr(), src.numel(), win, nwin, blocks, n_st, out.data_ptr(),
+                                    stamps.data_ptr(), st)
+                if rc:
+                    raise RuntimeError(f"rqp_stream({kind}) returned {rc}")
+            call()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            call()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            t = stamps.cpu().numpy().view(np.uint64).reshape(blocks, 4).astype(np.float64)
+            ghz = float(np.median((t[:, 2] - t[:, 0]) / np.maximum(t[:, 3] - t[:, 1], 1.0))) * 0.1
+            nbytes = blocks * (n_st + nstg - 1) * sb
+            res[f"stream_{where}_{name}"] = {
+                "ms": round(ms, 3), "tb_s": round(nbytes / (ms * 1e-3) / 1e12, 2), "shader_clock_ghz": round(ghz, 3),
+                "bytes_per_clk_per_cu": round(nbytes / (ms * 1e-3) / (ghz * 1e9) / 256, 1)}
+    del src
+    x = torch.ones(1 << 19, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    tiles = 64
+    part = torch.empty(tiles * 16 * 256, dtype=torch.float32, device=dev)
+    counter = torch.zeros(tiles * 32, dtype=torch.int32, device=dev)
+    ysum = torch.empty(tiles * 256, dtype=torch.float32, device=dev)
+    p3 = (part.data_ptr(), counter.data_ptr(), ysum.data_ptr())
+    # counters 4 bytes apart (64 tiles' counters in two 128-byte lines) or
+    # one per 128-byte line
+    launches = {"empty_kernel": (0, 1, 1, 1, 0, 0, 0), "touch_2mib": (1, 2048, 1, 1, x.data_ptr(), y.data_ptr(), 0),
+                "arrival_counter_1_tile_16_slices": (2, 1, 16, 1, *p3),
+                "arrival_counter_64_tiles_16_slices_packed_counters": (2, tiles, 16, 1, *p3),
+                "arrival_counter_64_tiles_16_slices_one_counter_per_128b": (2, tiles, 16, 32, *p3)}
+    n = 200
+    for name, (kind, nb, sl, cs, a, b, c) in launches.items():
+        def one():
+            rc = lib.rqp_launch(kind, nb, sl, cs, a, b, c, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if rc:
+                raise RuntimeError(f"rqp_launch({kind}) returned {rc}")
+        one()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                one()
+        g.replay()
+        torch.cuda.synchronize()
+        per = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) * 1e3 / n)
+        res[f"launch_{name}"] = {"us_per_launch": round(sorted(per)[2], 2), "launches_per_graph": n}
+        del g
+    if float(ysum[1].item()) != 16.0 or float(ysum[(tiles - 1) * 256 + 3].item()) != 48.0:
+        raise RuntimeError("arrival probe: the last workgroup's sum is wrong")
     return res
 
 

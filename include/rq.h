@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define RQ_ABI_VERSION 4
+#define RQ_ABI_VERSION 5
 
 typedef enum {
   RQ_OK = 0,
@@ -274,10 +274,11 @@ rq_status rq_pack_nibble_planes(const int8_t *w, const uint16_t *scales_f16,
  * K) bytes (caller-owned, 16-byte aligned) lets shapes with few 64-row
  * tiles split K over more workgroups within the one launch: each writes
  * FP32 partial sums and bumps a per-tile arrival counter kept in the
- * workspace's first 1 KiB, and the last to arrive adds the partials in a
- * fixed order and resets the counter.  Those 1 KiB must be ZERO before
- * the first call (zero the workspace once after allocating it); every call
- * leaves them zero again, so the workspace can be reused by later calls of
+ * workspace's first 32 KiB (one counter per 128-byte line), and the last to
+ * arrive adds the partials in a fixed order and resets the counter.  Those
+ * 32 KiB must be ZERO before the first call (zero the workspace once after
+ * allocating it); every call leaves them zero again, so the workspace can
+ * be reused by later calls of
  * any shape and by graph replays.  Calls sharing a workspace must not
  * overlap.
  * NULL / smaller runs the shape unsplit.  The result is the same bits

@@ -75,7 +75,7 @@ _SIGNATURES = {
 _lib = None
 
 # The RQ_ABI_VERSION these signatures and RqGemvProblem follow (include/rq.h).
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 def lib():

@@ -128,6 +128,10 @@ enum Planes { kHi = 0, kHiLo = 1, kLo = 2 };
 // pass's.
 constexpr int kWsTokens = 16;
 constexpr int kMaxSlices = 16;  // K slices of a split launch, at most
+// Arrival counters sit one per 128-byte line (32 uint32 apart): atomics of
+// many tiles on one line serialize at the memory side, which made a
+// 64-tile, 16-slice launch 2.5 times as long as with a line per counter.
+constexpr int kCounterStride = 32;
 
 // LDS budget for staging the flagged tokens' x in the escalation: up to
 // kXStageElems elements per token of a workgroup's K range.
@@ -256,7 +260,8 @@ __device__ __forceinline__ void split_finish(const float* __restrict__ ws, uint3
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's partial stores are complete
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t old = __hip_atomic_fetch_add(counters + (size_t)tile * kCounterStride, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
     last = old == (uint32_t)nslice - 1u ? 1u : 0u;
   }
   __syncthreads();
@@ -289,7 +294,8 @@ __device__ __forceinline__ void split_finish(const float* __restrict__ ws, uint3
     if (kP == kHi && yf != nullptr) yf[i] = v;
     y[i] = (uint16_t)f32_to_bf16(v);
   }
-  if (threadIdx.x == 0) __hip_atomic_store(counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0)
+    __hip_atomic_store(counters + (size_t)tile * kCounterStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The low pass's x goes straight to registers, with no LDS traffic.  For a
@@ -726,12 +732,12 @@ static int gemv_tb(int64_t B) { return B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B 
 // block per wave, and at most kMaxSlices (the partials the last arriver of
 // a tile loads at once).  Every split launch pays one cross-workgroup
 // arrival, whatever its slice count, so the count trades that against each
-// workgroup's share of the work: the low pass (16 tokens of dot products
-// per weight) aims at 1024 workgroups, the escalation (the few flagged
-// tokens) at 128 -- the fastest of 64 .. 2048 for each on a decode step of
-// the Qwen3-0.6B shapes in layer order.  The workspace is sized for the
-// low pass, the larger count.
-constexpr int64_t kLowTarget = 1024, kEscTarget = 128;
+// workgroup's share of the work: both passes aim at 1024 workgroups, the
+// fastest of 128 .. 2048 for each on a decode step of the Qwen3-0.6B shapes
+// in layer order once the arrival counters sit on lines of their own (with
+// packed counters the escalation's best was 128).  The workspace is sized
+// for the low pass's count, which the escalation's never exceeds.
+constexpr int64_t kLowTarget = 1024, kEscTarget = 1024;
 
 static int gemv_slices(int64_t N, int64_t K, int64_t target) {
   const int64_t tiles = (N + 63) / 64, nb = K / 32;
@@ -742,11 +748,11 @@ static int gemv_slices(int64_t N, int64_t K, int64_t target) {
   return (int)(s < cap ? s : cap);
 }
 
-// Workspace of a split launch: 1 KiB of per-tile arrival counters (a split
-// shape has fewer than 256 row tiles; zero between calls, at the same place
-// for every shape, so shapes can share a workspace), then the FP32
-// partials [tile][slice][16 tokens][64 rows].
-constexpr size_t kCounterBytes = 256 * sizeof(uint32_t);
+// Workspace of a split launch: 32 KiB of per-tile arrival counters, one per
+// 128-byte line (a split shape has fewer than 256 row tiles; zero between
+// calls, at the same place for every shape, so shapes can share a
+// workspace), then the FP32 partials [tile][slice][16 tokens][64 rows].
+constexpr size_t kCounterBytes = 256 * kCounterStride * sizeof(uint32_t);
 
 size_t gemv_workspace_bytes(int64_t B, int64_t N, int64_t K) {
   (void)B;

@@ -126,3 +126,133 @@ extern "C" int rqp_probe(int kind, const void* ops, const void* scales, int bloc
   }
   return (int)hipGetLastError();
 }
+
+namespace rqp {
+
+// L2 -> LDS streaming as the pipelined GEMM does it: eight waves per
+// workgroup (one workgroup per CU) fill a ring of NSTG LDS stages of SB
+// bytes with 16-byte buffer-to-LDS loads (lane l of a load at byte 16 l of
+// a 1 KiB slot), wait for the stage in flight with the GEMM's count of
+// outstanding loads and meet one barrier per stage; nothing is computed.
+// Workgroup g reads the window [win * (g % nwin), + win) of src (win a
+// power of two), wrapping inside it; the buffer resource spans exactly
+// src_bytes, so any offset beyond it reads zeros without touching memory.
+template <int NSTG, int SB>
+__global__ __launch_bounds__(512, 1) void stream_kernel(const uint8_t* __restrict__ src, uint32_t src_bytes,
+                                                       uint32_t win, uint32_t nwin, int stages,
+                                                       float* __restrict__ out, uint64_t* __restrict__ t) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTG * SB];
+  constexpr int kLoads = SB / 1024 / 8;  // 1 KiB loads per wave per stage
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, (int)src_bytes, 0x00020000);
+  const uint32_t base = win * (blockIdx.x % nwin);
+  auto issue = [&](int s) {
+    uint8_t* st = smem + (s % NSTG) * SB;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const uint32_t slot = (uint32_t)(wave * kLoads + i);
+      const uint32_t off = base + (((uint32_t)s * (uint32_t)SB + slot * 1024u + 16u * (uint32_t)lane) & (win - 1u));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(st + slot * 1024), 16,
+                                               off, 0, 0, 0);
+    }
+  };
+  stamp(t, 0);
+  for (int s = 0; s < NSTG - 1; ++s) issue(s);
+  for (int s = 0; s < stages; ++s) {
+    issue(s + NSTG - 1);
+    // the oldest stage in flight has landed: NSTG - 1 stages' loads may still be outstanding
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NSTG - 1) * kLoads) : "memory");
+  }
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  stamp(t, 1);
+  out[(size_t)blockIdx.x * 512 + threadIdx.x] = (float)smem[(threadIdx.x * 16) % (NSTG * SB)];
+}
+
+// Launch latency: an empty kernel; one that reads one dword per thread; and
+// one whose workgroups meet at a device-scope arrival counter the way the
+// split-K GEMV finishes (each stores a partial with a device-scope store,
+// waits for it, bumps the counter; the last to arrive loads every partial,
+// writes the sum and resets the counter).  No workgroup waits for another.
+__global__ __launch_bounds__(256) void empty_kernel() {}
+
+__global__ __launch_bounds__(256) void touch_kernel(const float* __restrict__ x, float* __restrict__ y) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  y[i] = x[i] + 1.0f;
+}
+
+constexpr unsigned kMaxArrivals = 16;  // slices of one tile, at most
+
+// grid (tiles, slices): workgroup (t, s) stores its partial, waits for the
+// store, bumps tile t's counter; the tile's last workgroup loads the
+// tile's partials (all loads issued before any is added), writes their sum
+// and resets the counter.
+__global__ __launch_bounds__(256) void arrival_kernel(float* __restrict__ part, unsigned* __restrict__ counter,
+                                                      unsigned cstride, float* __restrict__ y) {
+  const unsigned tile = blockIdx.x, slices = gridDim.y;
+  const size_t i = ((size_t)tile * slices + blockIdx.y) * 256 + threadIdx.x;
+  __hip_atomic_store(part + i, (float)threadIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's partial store is complete
+  __syncthreads();
+  __shared__ unsigned last;
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(counter + (size_t)tile * cstride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           slices - 1;
+  __syncthreads();
+  if (last) {
+    float v[kMaxArrivals];
+#pragma unroll
+    for (unsigned b = 0; b < kMaxArrivals; ++b)
+      v[b] = __hip_atomic_load(part + ((size_t)tile * slices + min(b, slices - 1)) * 256 + threadIdx.x,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    float s = 0.0f;
+#pragma unroll
+    for (unsigned b = 0; b < kMaxArrivals; ++b) s += b < slices ? v[b] : 0.0f;
+    y[(size_t)tile * 256 + threadIdx.x] = s;
+    if (threadIdx.x == 0)
+      __hip_atomic_store(counter + (size_t)tile * cstride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+}  // namespace rqp
+
+// L2 -> LDS streaming: kind 0 two 64 KiB stages, 1 three 32 KiB stages,
+// 2 four 32 KiB stages; 512-thread workgroups, one per CU.  src of
+// src_bytes (< 2^31); workgroup g reads window g % nwin of win bytes
+// (win a power of two of at least 1 KiB, nwin * win <= src_bytes).  out: blocks * 512
+// floats; stamps: blocks * 4 u64.  Returns a hipError_t value, or 1 for a
+// bad argument.
+extern "C" int rqp_stream(int kind, const void* src, uint32_t src_bytes, uint32_t win, uint32_t nwin, int blocks,
+                          int stages, void* out, void* stamps, hipStream_t stream) {
+  if (win < 1024 || (win & (win - 1)) || nwin == 0 || (uint64_t)win * nwin > src_bytes || src_bytes >= 0x80000000u)
+    return 1;
+  const uint8_t* s = (const uint8_t*)src;
+  float* y = (float*)out;
+  uint64_t* t = (uint64_t*)stamps;
+  switch (kind) {
+    case 0: rqp::stream_kernel<2, 65536><<<blocks, 512, 0, stream>>>(s, src_bytes, win, nwin, stages, y, t); break;
+    case 1: rqp::stream_kernel<3, 32768><<<blocks, 512, 0, stream>>>(s, src_bytes, win, nwin, stages, y, t); break;
+    case 2: rqp::stream_kernel<4, 32768><<<blocks, 512, 0, stream>>>(s, src_bytes, win, nwin, stages, y, t); break;
+    default: return 1;
+  }
+  return (int)hipGetLastError();
+}
+
+// Launch-latency kernels: kind 0 empty, 1 touch (x, y: blocks * 256
+// floats), 2 arrival with blocks tiles of `slices` workgroups (slices <= 16;
+// part: blocks * slices * 256 floats, counter: tile t's counter at element
+// t * cstride of blocks * cstride zeroed unsigned, y: blocks * 256 floats).
+// Returns a hipError_t value, or 1 for a bad kind or size.
+extern "C" int rqp_launch(int kind, int blocks, int slices, int cstride, void* a, void* b, void* c,
+                          hipStream_t stream) {
+  if (blocks <= 0 || (kind == 2 && (slices <= 0 || slices > (int)rqp::kMaxArrivals || cstride <= 0))) return 1;
+  switch (kind) {
+    case 0: rqp::empty_kernel<<<blocks, 256, 0, stream>>>(); break;
+    case 1: rqp::touch_kernel<<<blocks, 256, 0, stream>>>((const float*)a, (float*)b); break;
+    case 2:
+      rqp::arrival_kernel<<<dim3(blocks, slices), 256, 0, stream>>>((float*)a, (unsigned*)b, (unsigned)cstride,
+                                                                   (float*)c);
+      break;
+    default: return 1;
+  }
+  return (int)hipGetLastError();
+}

@@ -13,6 +13,9 @@ from oracle import formats as F
 DEV = "cuda"
 REL_FRO = 1e-5
 PER_ELEM = 1e-3
+# the split-K GEMV workspace starts with its arrival counters, one per
+# 128-byte line for up to 256 row tiles (include/rq.h, rq_gemv_nibble_escalate)
+COUNTER_BYTES = 32768
 
 
 def log(msg):

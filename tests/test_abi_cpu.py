@@ -32,7 +32,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert rq.rq_abi_version() == L.ABI_VERSION == 4
+    assert rq.rq_abi_version() == L.ABI_VERSION == 5
     lib = L.lib()
     assert lib.rq_status_str(L.RQ_ESHAPE) == b"RQ_ESHAPE"
     assert lib.rq_status_str(99) == b"RQ_UNKNOWN"
@@ -162,8 +162,8 @@ def test_gemv_and_gate_validation():
     assert rq.rq_escalation_gate_workspace_bytes(0, 100) == 0
     assert status_of(rq.rq_kv_quantize, A16, 4, 2, 100, A16, A16) == L.RQ_ESHAPE
     # split-K workspace: few row tiles -> slices x 16 token rows x padded rows x FP32; many tiles or bad shapes -> 0
-    assert rq.rq_gemv_workspace_bytes(16, 1024, 1024) == 1024 + 8 * 16 * 1024 * 4
-    assert rq.rq_gemv_workspace_bytes(1, 100, 1024) == 1024 + 8 * 16 * 128 * 4
+    assert rq.rq_gemv_workspace_bytes(16, 1024, 1024) == 32768 + 8 * 16 * 1024 * 4
+    assert rq.rq_gemv_workspace_bytes(1, 100, 1024) == 32768 + 8 * 16 * 128 * 4
     assert rq.rq_gemv_workspace_bytes(16, 151936, 1024) == 0
     assert rq.rq_gemv_workspace_bytes(16, 1024, 100) == 0
     assert rq.rq_gemv_workspace_bytes(17, 1024, 1024) == 0

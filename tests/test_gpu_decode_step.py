@@ -16,7 +16,7 @@ from mixed_precision_block_amd import api
 from mixed_precision_block_amd import _lib as L
 from oracle import gemv as V
 from synthetic import workloads as W
-from tests.gpu_util import check_bf16, dev, dev_bf16, host_bits, log
+from tests.gpu_util import COUNTER_BYTES, check_bf16, dev, dev_bf16, host_bits, log
 
 pytestmark = pytest.mark.gpu
 
@@ -76,7 +76,7 @@ def test_decode_step_layer_ordered():
         x_bits, y_bits = eager[i], eager[len(stages) + i]
         ref, bound = expected(x_bits, s, flags_h)
         off += check_bf16(y_bits, ref, bound, f"decode step {s['name']} {s['N']}x{s['K']}", k=s["K"])
-    assert torch.count_nonzero(ws[:1024]).item() == 0, "arrival counters not reset"
+    assert torch.count_nonzero(ws[:COUNTER_BYTES]).item() == 0, "arrival counters not reset"
 
     # the whole step as one captured graph, replayed with eager work between
     g = torch.cuda.CUDAGraph()

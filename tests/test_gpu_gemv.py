@@ -10,7 +10,7 @@ from oracle import formats as F
 from oracle import gemv as V
 from synthetic import workloads as W
 from tests import _golden as gold
-from tests.gpu_util import check_bf16, dev, dev_bf16, host, host_bits, log
+from tests.gpu_util import COUNTER_BYTES, check_bf16, dev, dev_bf16, host, host_bits, log
 
 pytestmark = pytest.mark.gpu
 
@@ -143,11 +143,11 @@ def test_deterministic():
 def test_split_workspace_reused_across_calls():
     """One workspace serves consecutive split calls of different shapes and
     phases; every output equals a fresh-workspace run and the oracle.  Only
-    its first 1 KiB (the arrival counters) is zeroed, once: stale partial
+    its first 32 KiB (the arrival counters) is zeroed, once: stale partial
     sums must not matter, and every call leaves the counters zero."""
     wsb = max(L.rq_gemv_workspace_bytes(16, n, k) for n, k in ((1000, 1024), (130, 3072), (64, 256)))
     ws = torch.full((wsb,), 0x7F, dtype=torch.uint8, device="cuda")
-    ws[:1024].zero_()
+    ws[:COUNTER_BYTES].zero_()
     for rep in range(2):
         for i, (n, k) in enumerate(((1000, 1024), (130, 3072), (64, 256))):
             d = W.c5_linear(i + 2, B=16, N=n, K=k)
@@ -167,7 +167,7 @@ def test_split_workspace_reused_across_calls():
             bound = V.abs_bound(d["x"], d["w"], d["scales"]) + V.abs_bound(d["x"], 16 * hi8.astype(np.int64),
                                                                             d["scales"])
             check_bf16(host_bits(y), ref, bound, f"reuse {n}x{k}", k=k)
-            assert torch.count_nonzero(ws[:1024]).item() == 0, "arrival counters not reset"
+            assert torch.count_nonzero(ws[:COUNTER_BYTES]).item() == 0, "arrival counters not reset"
 
 
 @pytest.mark.parametrize("B", [1, 5, 16])
