@@ -939,7 +939,7 @@ def measure_ramp_study(torch, np, api, L, W, to_dev, dev, time_calls):
         h0 = to_dev(d["h0"][:s_tok])
         h = torch.empty_like(h0)
         wsb = L.rq_recurrent_prefill_workspace_bytes(s_tok, D, F, L.RQ_MXFP4)
-        wsp = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)  # arrival counters start at zero
+        wsp = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
         t = {}
         for name, sched in (("all_bf16", 0x00), ("ramp", 0x3F)):
             t[name] = time_calls(torch, lambda sched=sched: L.rq_recurrent_prefill(
