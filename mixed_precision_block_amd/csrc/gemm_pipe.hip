@@ -22,7 +22,9 @@
 //   the fragment reads of consecutive rows hit distinct banks (checked for
 //   both 32- and 64-bank LDS models).
 // * WMW x WNW waves, each owning a (BM/WMW) x (BN/WNW) quadrant of MFMA
-//   tiles of 32 x 32; accumulators live in AGPRs.  256 x 256 tiles use
+//   tiles of 32 x 32; accumulators live in AGPRs.  With KS = 2 there are
+//   two such grids, each summing every other slice of each stage, and the
+//   second grid's sums are added to the first's through LDS at the end.  256 x 256 tiles use
 //   eight waves (two per SIMD, so one wave's waits overlap the other's
 //   MFMAs), 128 x 128 tiles four.
 // * Workgroups are ordered so that consecutive tiles land on the same XCD
@@ -91,10 +93,10 @@ __device__ __forceinline__ void load_lds4(__amdgpu_buffer_rsrc_t r, void* lds, u
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
 }
 
-template <int FMT, int BM, int BN, int RB, int WMW, int WNW, int NSTG>
+template <int FMT, int BM, int BN, int RB, int WMW, int WNW, int NSTG, int KS = 1>
 struct DmaCfg {
   using T = PipeTraits<FMT, RB>;
-  static constexpr int NW = WMW * WNW, NT = 64 * NW;
+  static constexpr int NW = WMW * WNW * KS, NT = 64 * NW;  // KS groups of WMW x WNW waves
   static constexpr int TM = BM / 32 / WMW, TN = BN / 32 / WNW;
   static constexpr int WM = BM / WMW, WN = BN / WNW;
   static constexpr int CPR = RB / 16;                 // 16-byte chunks per row
@@ -120,22 +122,25 @@ struct DmaCfg {
   static_assert(NSTG * STAGE <= 160 * 1024, "stages fit the LDS");
 };
 
-template <int FMT, int EPI, int BM, int BN, int RB, int WMW, int WNW, int NSTG>
-__global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint8_t* __restrict__ A,
+template <int FMT, int EPI, int BM, int BN, int RB, int WMW, int WNW, int NSTG, int KS>
+__global__ __launch_bounds__(64 * WMW * WNW * KS, 1) void gemm_pipe_kernel(const uint8_t* __restrict__ A,
                                                                       const uint8_t* __restrict__ As,
                                                                       const uint8_t* __restrict__ W,
                                                                       const uint8_t* __restrict__ Ws, int M, int N,
                                                                       int K, void* __restrict__ Y,
                                                                       uint8_t* __restrict__ Ys, int tiles_m,
                                                                       int tiles_n) {
-  using C = DmaCfg<FMT, BM, BN, RB, WMW, WNW, NSTG>;
+  using C = DmaCfg<FMT, BM, BN, RB, WMW, WNW, NSTG, KS>;
   using T = PipeTraits<FMT, RB>;
   constexpr int TM = C::TM, TN = C::TN;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTG * C::STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WNW, wn = wave % WNW;
+  // K group kg of the workgroup's KS groups takes the stage slices kk with
+  // kk % KS == kg; inside a group, waves form the WMW x WNW grid
+  const int kg = wave / (WMW * WNW), wg = wave % (WMW * WNW);
+  const int wm = wg / WNW, wn = wg % WNW;
   const int half = lane >> 5, lrow = lane & 31;
 
   // XCD-aware tile order
@@ -237,6 +242,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       if (kk >= nkk) break;  // nkk == KK (folded) except in a partial last stage
+      if (KS > 1 && kk % KS != kg) continue;
       v4i fa[TM][NQ], fb[TN][NQ];
       // 16-byte chunk(s) of this slice for the lane's half
       const int c0 = kF8 ? kk * 4 + half : kk * 2 + half;
@@ -258,7 +264,7 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
       if constexpr (FMT == 2) {
         // exact MXFP8: both block scales of the slice, as floats; each lane
         // dequantizes its codes to BF16 and the BF16 MFMA accumulates in FP32
-        if (kk % 2 == 0) {
+        if (KS > 1 || kk % 2 == 0) {
 #pragma unroll
           for (int i = 0; i < TM; ++i)
             sa[i] = *reinterpret_cast<const uint32_t*>(sc + (wm * C::WM + i * 32 + lrow) * C::SBPR + 4 * (kk / 2));
@@ -366,6 +372,40 @@ __global__ __launch_bounds__(64 * WMW * WNW, 1) void gemm_pipe_kernel(const uint
   if (tail_kk > 0) compute(smem + (nfull % NSTG) * C::STAGE, tail_kk);
   // past-end loads may still be landing in LDS that the epilogue reuses
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  if constexpr (KS == 2) {
+    // the second K group's sums go through LDS to the first group's wave of
+    // the same quadrant, which adds them to its own (first group + second,
+    // a fixed order); the first group then runs the epilogue alone
+    static_assert(WMW * WNW * TM * TN * 16 * 256 <= NSTG * C::STAGE, "exchange fits the stage buffers");
+    float4* xch = reinterpret_cast<float4*>(smem) + (size_t)wg * TM * TN * 4 * 64;
+    if (kg == 1) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            xch[((i * TN + j) * 4 + g) * 64 + lane] =
+                float4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+    }
+    __syncthreads();
+    if (kg == 0) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float4 o = xch[((i * TN + j) * 4 + g) * 64 + lane];
+            acc[i][j][4 * g] += o.x;
+            acc[i][j][4 * g + 1] += o.y;
+            acc[i][j][4 * g + 2] += o.z;
+            acc[i][j][4 * g + 3] += o.w;
+          }
+    }
+    __syncthreads();  // every read of the exchange is done before the strips reuse the LDS
+    if (kg == 1) return;
+  }
 
   // Epilogue.  The W tile is the MFMA's first operand, so the accumulator
   // is the transposed tile: lane l, element r holds row m = l % 32 of the A
@@ -499,11 +539,11 @@ bool gemm_pipe_supported(int fmt, int64_t M, int64_t N, int64_t K) {
   return 256 * ld < (int64_t)0x7FFFFFFF && M > 0 && N > 0;
 }
 
-template <int FMT, int EPI, int BM, int BN, int RB, int WMW, int WNW, int NSTG>
+template <int FMT, int EPI, int BM, int BN, int RB, int WMW, int WNW, int NSTG, int KS = 1>
 static hipError_t launch_pipe_t(const void* a, const uint8_t* as, const void* w, const uint8_t* ws, int64_t M,
                                 int64_t N, int64_t K, void* y, uint8_t* ys, hipStream_t stream) {
   const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
-  gemm_pipe_kernel<FMT, EPI, BM, BN, RB, WMW, WNW, NSTG><<<tm * tn, 64 * WMW * WNW, 0, stream>>>(
+  gemm_pipe_kernel<FMT, EPI, BM, BN, RB, WMW, WNW, NSTG, KS><<<tm * tn, 64 * WMW * WNW * KS, 0, stream>>>(
       static_cast<const uint8_t*>(a), as, static_cast<const uint8_t*>(w), ws, (int)M, (int)N, (int)K, y, ys, tm,
       tn);
   return hipGetLastError();
@@ -537,6 +577,17 @@ static hipError_t launch_pipe_r(const void* a, const uint8_t* as, const void* w,
   // 128 x 128 tile per CU they move twice the operand bytes per FLOP and
   // lose (4096 x 1024 x 2048 MXFP8 14.0 -> 18.7 us).
   if (small <= 128) return launch_pipe_t<FMT, EPI, 64, 64, RB, 2, 2, 3>(a, as, w, ws, M, N, K, y, ys, stream);
+  if constexpr (FMT == 2) {
+    // exact MXFP8 with K of at least 24 stages: two K groups of 2 x 2 waves
+    // of 64 x 64, each group taking every other slice, their sums added
+    // through LDS before the epilogue.  Each wave's operand conversions then
+    // feed two MFMAs where a 64 x 32 wave's feed one (4 instead of 6
+    // conversions per MFMA, still two waves per SIMD).  4096 x 1024 x 3072:
+    // 30.1 -> 28.2 us; at 16 stages (K = 2048) the exchange costs what the
+    // conversions save.
+    if (small <= 256 && K / 128 >= 24)
+      return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 2, 3, 2>(a, as, w, ws, M, N, K, y, ys, stream);
+  }
   if constexpr (FMT != 4) {
     if (small <= 256) return launch_pipe_t<FMT, EPI, 128, 128, RB, 2, 4, 3>(a, as, w, ws, M, N, K, y, ys, stream);
   }

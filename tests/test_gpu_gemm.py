@@ -128,6 +128,24 @@ def test_small_tile_boundary_sampled(fmt, ofmt, M, N, K):
     sampled_shape_check(fmt, ofmt, M, N, K, "tile-boundary")
 
 
+@pytest.mark.parametrize("M,N,K", [(2049, 1000, 3072), (1100, 2100, 3200)])
+def test_mxfp8_two_k_groups_sampled(M, N, K):
+    """Exact MXFP8 shapes with 128 x 128 tiles for at most one per CU and K
+    of at least 24 stages, whose workgroups sum even and odd slices in two
+    groups of waves and add the second group's sums to the first's: ragged
+    M and N (136 and 153 tiles), K of 24 and 25 stages; sampled rows against
+    the oracle, and two runs bit for bit alike."""
+    sampled_shape_check(L.RQ_MXFP8, F.FMT_MXFP8, M, N, K, "two-k-group")
+    rng = np.random.default_rng(M + N + K)
+    ac = dev(random_codes(rng, M, K, F.FMT_MXFP8))
+    wc = dev(random_codes(rng, N, K, F.FMT_MXFP8))
+    as_ = dev(rng.integers(118, 136, (M, K // 32)).astype(np.uint8))
+    ws = dev(rng.integers(118, 136, (N, K // 32)).astype(np.uint8))
+    y1 = host(api.gemm(L.RQ_MXFP8, ac, as_, wc, ws, K, L.RQ_OUT_F32))
+    y2 = host(api.gemm(L.RQ_MXFP8, ac, as_, wc, ws, K, L.RQ_OUT_F32))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
 @pytest.mark.parametrize("fmt,ofmt", MX + [(L.RQ_BF16, None)])
 @pytest.mark.parametrize("M,N,K", [(4000, 2000, 4160), (4096, 2048, 5632), (3000, 1900, 2048)])
 def test_tall_tiles_long_k_sampled(fmt, ofmt, M, N, K):
