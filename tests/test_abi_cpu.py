@@ -271,3 +271,28 @@ def test_empty_tensors_may_be_null_and_nothing_else():
                      None, None) == L.RQ_EINVAL  # x [B, K] is not empty
     assert status_of(rq.rq_kv_quantize, None, 0, 2, 128, None, None) in passed
     assert status_of(rq.rq_kv_quantize, None, 3, 2, 128, None, None) == L.RQ_EINVAL
+
+
+def test_probe_library_loads_and_rejects_bad_arguments():
+    """libprobe.so (the hardware probes behind bench.py --only probes) loads
+    beside librq.so, exports its three entry points, and refuses bad
+    arguments before any launch."""
+    path = os.path.join(os.path.dirname(L.LIB_PATH), "libprobe.so")
+    p = ctypes.CDLL(path)
+    for name in ("rqp_probe", "rqp_stream", "rqp_launch"):
+        assert hasattr(p, name), name
+    p.rqp_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    p.rqp_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                             ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    p.rqp_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert p.rqp_probe(9, None, None, 1, 1, None, None, None) == 1  # unknown kind
+    assert p.rqp_stream(0, None, 1 << 20, 3000, 1, 1, 1, None, None, None) == 1  # window not a power of two
+    assert p.rqp_stream(0, None, 1 << 20, 1 << 20, 2, 1, 1, None, None, None) == 1  # windows past the buffer
+    assert p.rqp_stream(0, None, 1 << 31, 1 << 20, 1, 1, 1, None, None, None) == 1  # buffer beyond 2 GiB
+    assert p.rqp_stream(7, None, 1 << 20, 1 << 20, 1, 1, 1, None, None, None) == 1  # unknown kind
+    assert p.rqp_launch(2, 1, 17, 1, None, None, None, None) == 1  # more than 16 slices
+    assert p.rqp_launch(2, 1, 16, 0, None, None, None, None) == 1  # counter stride 0
+    assert p.rqp_launch(0, 0, 1, 1, None, None, None, None) == 1  # no workgroups
+    assert p.rqp_launch(5, 1, 1, 1, None, None, None, None) == 1  # unknown kind
