@@ -132,6 +132,9 @@ __global__ __launch_bounds__(64 * WMW * WNW * KS, 1) void gemm_pipe_kernel(const
                                                                       int tiles_n) {
   using C = DmaCfg<FMT, BM, BN, RB, WMW, WNW, NSTG, KS>;
   using T = PipeTraits<FMT, RB>;
+  // two K groups only for the exact MXFP8 path, whose slices reload their
+  // scale dwords each time (the other formats load them every other slice)
+  static_assert(KS == 1 || (KS == 2 && FMT == 2), "K groups: one, or two on the exact MXFP8 path");
   constexpr int TM = C::TM, TN = C::TN;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTG * C::STAGE];
 
