@@ -393,6 +393,7 @@ def main():
         del g["ac"], g["as_"], g["y"], g["a"]
     if not args.no_rows:
         line["rows"] = measure_rows(torch, np, api, L, W, to_dev, dev)
+        line["hardware_ceilings"] = hardware_ceilings(measure_probes(torch, np, dev))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(np, W, gpu_f32, acc_rows)
         line["accuracy_rel_frobenius"] = line["cpu_baseline"].pop("accuracy")
@@ -479,6 +480,23 @@ def measure_probes(torch, np, dev, blocks=512, seed=20261204):
                     "v_mfma_f32_32x32x16_bf16); the dequant kinds add 24 v_cvt_scalef32_pk_bf16_fp8 per iteration "
                     "(the ratio of the exact MXFP8 GEMM's 128 x 64 wave tiles)")
     return res
+
+
+def hardware_ceilings(p):
+    """The probes' figures that bound this line's fractions: the matrix
+    instructions' sustained rate on random operands (the clock drops on
+    random bits), the BF16 instruction fed by the exact MXFP8 path's
+    dequantization, streaming rates and launch costs."""
+    return {
+        "mfma_random_operands_frac_of_peak": {k: p[f"{k}_random"]["frac_peak"] for k in ("fp4", "fp8", "bf16")},
+        "mfma_random_shader_clock_ghz": {k: p[f"{k}_random"]["shader_clock_ghz"] for k in ("fp4", "fp8", "bf16")},
+        "bf16_mfma_fed_by_fp8_dequant_frac_of_bf16_peak": p["bf16_random_fed_by_24_fp8_dequant_per_8"]["frac_peak"],
+        "l2_to_lds_tb_s": p["stream_l2_private_two_64k_stages"]["tb_s"],
+        "hbm_to_lds_tb_s": p["stream_hbm_two_64k_stages"]["tb_s"],
+        "launch_us": {"empty": p["launch_empty_kernel"]["us_per_launch"],
+                      "arrival_64_tiles_16_slices": p["launch_arrival_counter_64_tiles_16_slices_one_counter_per_128b"]
+                      ["us_per_launch"]},
+        "source": "bench.py --only probes (mixed_precision_block_amd/probes/probes.hip)"}
 
 
 def measure_stream_and_launch_probes(torch, lib, dev):
