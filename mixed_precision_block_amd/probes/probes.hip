@@ -1,10 +1,13 @@
-// Hardware probes behind the ceilings quoted for the GEMM kernels: the
-// sustained matrix-instruction rate and shader clock on constant versus
-// random operand bits, and how far VALU dequantization overlaps BF16
-// matrix instructions.  Measurement only: nothing in librq calls these,
-// and their results are never used as GEMM outputs.
+// Hardware probes behind the ceilings quoted for the library's kernels:
+// the sustained matrix-instruction rate and shader clock on constant versus
+// random operand bits, how far VALU dequantization overlaps BF16 matrix
+// instructions (rqp_probe), L2 and HBM streaming into LDS the way the
+// pipelined GEMM loads (rqp_stream), and the cost of back-to-back launches,
+// with and without the split-K GEMV's cross-workgroup arrival (rqp_launch).
+// Measurement only: nothing in librq calls these, and their results are
+// never used as outputs of the library.
 //
-// Each probe wave keeps eight independent accumulators and issues eight
+// Each matrix-instruction probe wave keeps eight independent accumulators and issues eight
 // matrix instructions per loop iteration on operands it loaded once.  Lane 0
 // of every workgroup's first wave reads the shader cycle counter
 // (s_memtime) and the 100 MHz real-time counter (s_memrealtime) before and
