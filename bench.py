@@ -591,6 +591,34 @@ def measure_stream_and_launch_probes(torch, lib, dev):
             per.append(e0.elapsed_time(e1) * 1e3 / n)
         res[f"launch_{name}"] = {"us_per_launch": round(sorted(per)[2], 2), "launches_per_graph": n}
         del g
+    # LDS reads: 1, 2 and 4 waves per SIMD (one, two and four 256-thread
+    # workgroups per CU)
+    lib.rqp_lds.restype = ctypes.c_int
+    lib.rqp_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    for per_cu in (1, 2, 4):
+        nb = 256 * per_cu
+        lo = torch.empty(nb * 256, dtype=torch.float32, device=dev)
+        st_l = torch.zeros(nb * 4, dtype=torch.int64, device=dev)
+        iters = 20000
+
+        def lds_call():
+            rc = lib.rqp_lds(nb, iters, lo.data_ptr(), st_l.data_ptr(),
+                             ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if rc:
+                raise RuntimeError(f"rqp_lds returned {rc}")
+        lds_call()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        lds_call()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        t = st_l.cpu().numpy().view(np.uint64).reshape(nb, 4).astype(np.float64)
+        ghz = float(np.median((t[:, 2] - t[:, 0]) / np.maximum(t[:, 3] - t[:, 1], 1.0))) * 0.1
+        nbytes = nb * 256 * iters * 8 * 16
+        res[f"lds_read_{per_cu}_waves_per_simd"] = {
+            "ms": round(ms, 3), "shader_clock_ghz": round(ghz, 3),
+            "bytes_per_clk_per_cu": round(nbytes / (ms * 1e-3) / (ghz * 1e9) / 256, 1)}
     if float(ysum[1].item()) != 16.0 or float(ysum[(tiles - 1) * 256 + 3].item()) != 48.0:
         raise RuntimeError("arrival probe: the last workgroup's sum is wrong")
     return res

@@ -2,8 +2,9 @@
 // the sustained matrix-instruction rate and shader clock on constant versus
 // random operand bits, how far VALU dequantization overlaps BF16 matrix
 // instructions (rqp_probe), L2 and HBM streaming into LDS the way the
-// pipelined GEMM loads (rqp_stream), and the cost of back-to-back launches,
-// with and without the split-K GEMV's cross-workgroup arrival (rqp_launch).
+// pipelined GEMM loads (rqp_stream), LDS reads (rqp_lds), and the cost of
+// back-to-back launches, with and without the split-K GEMV's cross-workgroup
+// arrival (rqp_launch).
 // Measurement only: nothing in librq calls these, and their results are
 // never used as outputs of the library.
 //
@@ -257,5 +258,41 @@ extern "C" int rqp_launch(int kind, int blocks, int slices, int cstride, void* a
       break;
     default: return 1;
   }
+  return (int)hipGetLastError();
+}
+
+namespace rqp {
+
+// LDS read rate: each wave of a 256-thread workgroup reads 16 bytes per lane
+// (ds_read_b128, lane l at byte 16 l of its wave's 1 KiB, no bank
+// conflict) eight times per iteration from a 32 KiB buffer it filled once,
+// xor-folding the values so that every read is kept.
+__global__ __launch_bounds__(256) void lds_read_kernel(int iters, float* __restrict__ out, uint64_t* __restrict__ t) {
+  __shared__ uint4 buf[2048];  // 32 KiB
+  for (int i = threadIdx.x; i < 2048; i += 256) buf[i] = make_uint4(i, i + 1, i + 2, i + 3);
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint4 acc = make_uint4(0, 0, 0, 0);
+  stamp(t, 0);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const uint4 v = buf[((wave * 8 + r + it) & 31) * 64 + lane];
+      acc.x ^= v.x, acc.y ^= v.y, acc.z ^= v.z, acc.w ^= v.w;
+    }
+  }
+  stamp(t, 1);
+  out[(size_t)blockIdx.x * 256 + threadIdx.x] = (float)(acc.x ^ acc.y ^ acc.z ^ acc.w);
+}
+
+}  // namespace rqp
+
+// LDS read rate: blocks workgroups of 256 threads (blocks / 256 per CU; a
+// CU holds at most 8 of them by waves per SIMD), iters iterations of eight
+// 16-byte reads per lane.  out: blocks * 256 floats; stamps: blocks * 4 u64.
+// Returns a hipError_t value, or 1 for a bad size.
+extern "C" int rqp_lds(int blocks, int iters, void* out, void* stamps, hipStream_t stream) {
+  if (blocks <= 0 || iters <= 0) return 1;
+  rqp::lds_read_kernel<<<blocks, 256, 0, stream>>>(iters, (float*)out, (uint64_t*)stamps);
   return (int)hipGetLastError();
 }
