@@ -95,6 +95,30 @@ class Timer:
         return sum(s.elapsed_time(e) for s, e in self.pairs)
 
 
+WARM_MS = 50.0  # sustained work before a timing: the clocks settle within about 30 ms
+
+
+def warm_clocks(torch, fns, before=None, ms=WARM_MS):
+    """Calls fns round-robin (each after `before` when given) until `ms` of
+    wall time has passed, in batches that double up to about 2 ms, so the
+    GPU has left the lower clocks it drops to while idle (about 10% slower
+    over the first 25-30 ms of work) before anything is timed."""
+    n, spent = 1, 0.0
+    while spent < ms:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            for fn in fns:
+                if before:
+                    before()
+                fn()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) * 1e3
+        spent += dt
+        if dt < 2.0:
+            n *= 2
+
+
 def time_calls(torch, fn, iters, warmup=10, before=None, batches=5, graph=False):
     """Per-call milliseconds of fn().  Without `before`: the median over
     `batches` batches of iters back-to-back calls, each batch bracketed by
@@ -104,6 +128,7 @@ def time_calls(torch, fn, iters, warmup=10, before=None, batches=5, graph=False)
     once in a HIP graph and times its replays.  With `before`: events
     bracket each call, the untimed `before` work runs in between, and the
     mean is returned."""
+    warm_clocks(torch, [fn], before)
     for _ in range(warmup):
         if before:
             before()
@@ -146,6 +171,7 @@ def time_interleaved(torch, fns, iters, warmup=10, batches=9):
     pair of events per batch) alternate between the functions, so drifts of
     the clock (which follows power on random operands) reach them alike;
     the median over each function's batches."""
+    warm_clocks(torch, fns)
     for fn in fns:
         for _ in range(warmup):
             fn()
@@ -227,7 +253,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-rows", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -304,16 +330,7 @@ def main():
             L.rq_quantize(g["a"], M, g["K"], L.RQ_MXFP8, None, 0, L.RQ_APPEND_NONE, g["ac"], g["as_"])
             L.rq_gemm(L.RQ_MXFP8, g["ac"], g["as_"], g["wc"], g["ws"], M, g["N"], g["K"], L.RQ_OUT_BF16, g["y"])
 
-    for _ in range(args.warmup):
-        step()
-    # timed region: the steps alone, wall clock between synchronizations
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
+    step()  # the quantized inputs that the per-launch figures run on
     # the GEMM's average launch duration: each of the step's GEMMs launched
     # back to back between one pair of events (events around every launch
     # would add their own packets to the measured time), averaged over them
@@ -344,6 +361,20 @@ def main():
         per_gemm_f8[f"{g['name']} {M}x{g['N']}x{g['K']}"] = {
             "us": round(ms_g * 1e3, 2), "tflops": round(f_g / (ms_g * 1e-3) / 1e12, 1),
             "frac_mxfp8_peak": round(f_g / (ms_g * 1e-3) / PEAK["mxfp8"], 4)}
+    # The step's own timing follows the per-launch figures above, whose
+    # ~100 ms of sustained work has brought the clocks up from where they
+    # sit while the GPU is idle (otherwise the first ~30 ms run about 10%
+    # slower, and a short warm-up would leave the timed steps inside that).
+    for _ in range(args.warmup):
+        step()
+    # timed region: the steps alone, wall clock between synchronizations
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
     # FP32 outputs of the first rows, for the accuracy check in the oracle leg
     acc_rows = 256
     gpu_f32 = {}
