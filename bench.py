@@ -27,6 +27,11 @@ and the nibble GEMV (LM head, the 28-layer sweep grouped and in layer
 order, escalation, gate).  `cpu_baseline` times the CPU oracle on a bounded
 sample of the main workload.
 
+Every figure is timed after at least 50 ms of sustained calls of the same
+work: after an idle spell the GPU runs about 10% slower for its first
+25-30 ms.  The main line's timed steps come right after its per-launch
+figures and the W warm-up steps.
+
     python bench.py [--steps K] [--warmup W] [--no-rows] [--no-cpu-baseline]
     python bench.py --only square|gemv|ksweep   # one group of rows, for profiling
     python bench.py --traffic-from gpurun_out   # after the --pmc runs
